@@ -1,0 +1,199 @@
+"""Python binding of the fp8blk C ABI (include/fp8blk.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``_build/libfp8blk.so``.  PyTorch supplies device memory and the
+current HIP stream.  If the library is missing, loading raises at once; there
+is no fallback of any kind.
+
+Two layers:
+  * ``lib()`` returns the ctypes handle with typed signatures of the C
+    functions (raw device pointers, sizes, stream handle);
+  * ``fp8_quant_act_1x128``, ``fp8_quant_weight_128x128``,
+    ``fp8_block_gemm`` and ``fp8_block_grouped_gemm`` take torch tensors on
+    the GPU, allocate outputs when not given, call the C function on
+    ``torch.cuda.current_stream()`` and raise ``Fp8Error`` on a nonzero
+    status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_build", "libfp8blk.so")
+
+FP8_OK = 0
+FP8_ERR_NULL = 1
+FP8_ERR_SHAPE = 2
+FP8_ERR_ALIGN = 3
+FP8_ERR_DTYPE = 4
+FP8_ERR_WORKSPACE = 5
+FP8_ERR_HIP = 6
+FP8_OUT_F32 = 0
+FP8_OUT_BF16 = 1
+
+# Every symbol the header declares, with (argtypes, restype).
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SIGNATURES = {
+    "fp8_quant_act_1x128": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "fp8_quant_weight_128x128": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "fp8_block_gemm": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P,
+                        ctypes.c_size_t, _P], ctypes.c_int),
+    "fp8_block_grouped_gemm": ([_P, _P, _P, _P, _P, _I64, _I64, _P, ctypes.c_int,
+                                _I64, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "fp8_gemm_workspace_bytes": ([_I64, _I64, _I64, ctypes.c_int], ctypes.c_size_t),
+    "fp8_status_string": ([ctypes.c_int], ctypes.c_char_p),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class Fp8Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().fp8_status_string(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+def lib():
+    """Load libfp8blk.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(
+                    f"fp8blk HIP library not found at {LIB_PATH}; build it with "
+                    "`python -m fp8_fine_grained_token_amd.build`")
+            h = ctypes.CDLL(LIB_PATH)
+            for name, (args, res) in _SIGNATURES.items():
+                fn = getattr(h, name)
+                fn.argtypes = args
+                fn.restype = res
+            _lib = h
+        return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fp8_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != FP8_OK:
+        raise Fp8Error(status, where)
+
+
+# ---- torch-tensor layer -----------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _out_code(out_dtype):
+    torch = _torch()
+    if out_dtype in (torch.float32, "f32", FP8_OUT_F32):
+        return FP8_OUT_F32, torch.float32
+    if out_dtype in (torch.bfloat16, "bf16", FP8_OUT_BF16):
+        return FP8_OUT_BF16, torch.bfloat16
+    raise ValueError(f"unsupported out_dtype {out_dtype}")
+
+
+def fp8_quant_act_1x128(x, q=None, scales=None, stream=None):
+    """x: bf16 [M][K] -> (q uint8 [M][K] E4M3, scales fp32 [M][ceil(K/128)])."""
+    torch = _torch()
+    M, K = x.shape
+    G = (K + 127) // 128
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, G), dtype=torch.float32, device=x.device)
+    _check(lib().fp8_quant_act_1x128(_dev(x, "x", torch.bfloat16), M, K, _dev(q, "q", torch.uint8),
+                                     _dev(scales, "scales", torch.float32),
+                                     _stream_handle(stream)), "fp8_quant_act_1x128")
+    return q, scales
+
+
+def fp8_quant_weight_128x128(w, q=None, scales=None, stream=None):
+    """w: bf16 [N][K] -> (q uint8 [N][K], scales fp32 [ceil(N/128)][ceil(K/128)])."""
+    torch = _torch()
+    N, K = w.shape
+    if q is None:
+        q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty(((N + 127) // 128, (K + 127) // 128), dtype=torch.float32,
+                             device=w.device)
+    _check(lib().fp8_quant_weight_128x128(_dev(w, "w", torch.bfloat16), N, K,
+                                          _dev(q, "q", torch.uint8),
+                                          _dev(scales, "scales", torch.float32),
+                                          _stream_handle(stream)), "fp8_quant_weight_128x128")
+    return q, scales
+
+
+def fp8_gemm_workspace_bytes(M: int, N: int, K: int, out_dtype="bf16") -> int:
+    code, _ = _out_code(out_dtype)
+    return int(lib().fp8_gemm_workspace_bytes(M, N, K, code))
+
+
+def _workspace_args(workspace):
+    if workspace is None:
+        return ctypes.c_void_p(0), 0
+    torch = _torch()
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
+def fp8_block_gemm(a, sa, w, sw, out_dtype="bf16", c=None, workspace=None, stream=None):
+    """C[M][N] = block-scaled product of a [M][K] E4M3 (scales [M][K/128]) and
+    w [N][K] E4M3 (scales [N/128][K/128]); bf16 or fp32 output."""
+    torch = _torch()
+    M, K = a.shape
+    N = w.shape[0]
+    code, tdt = _out_code(out_dtype)
+    if c is None:
+        c = torch.empty((M, N), dtype=tdt, device=a.device)
+    wp, wb = _workspace_args(workspace)
+    _check(lib().fp8_block_gemm(_dev(a, "a", torch.uint8), _dev(sa, "sa", torch.float32),
+                                _dev(w, "w", torch.uint8), _dev(sw, "sw", torch.float32),
+                                _dev(c, "c", tdt), code, M, N, K, wp, wb,
+                                _stream_handle(stream)), "fp8_block_gemm")
+    return c
+
+
+def fp8_block_grouped_gemm(a, sa, w, sw, group_offsets, out_dtype="bf16", c=None,
+                           workspace=None, stream=None):
+    """Grouped GEMM over expert-sorted rows: a [T][K], w [E][N][K],
+    sw [E][N/128][K/128], group_offsets int32 [E+1] on the GPU."""
+    torch = _torch()
+    T, K = a.shape
+    E, N, _ = w.shape
+    code, tdt = _out_code(out_dtype)
+    if c is None:
+        c = torch.empty((T, N), dtype=tdt, device=a.device)
+    wp, wb = _workspace_args(workspace)
+    _check(lib().fp8_block_grouped_gemm(_dev(a, "a", torch.uint8), _dev(sa, "sa", torch.float32),
+                                        _dev(w, "w", torch.uint8), _dev(sw, "sw", torch.float32),
+                                        _dev(group_offsets, "group_offsets", torch.int32), E, T,
+                                        _dev(c, "c", tdt), code, N, K, wp, wb,
+                                        _stream_handle(stream)), "fp8_block_grouped_gemm")
+    return c

@@ -1,0 +1,205 @@
+// 1x128 activation and 128x128 weight quantization to OCP E4M3 (gfx950).
+//
+// Method: page "dssusan.co.kr qna 93378", Figure 7 (a): one scale per token
+// per 128 channels for activations and per 128x128 block for weights, with
+// the scale following each small group's own maximum.  Page "why-be.co.kr
+// as_center 36949", passage on the quantization round trip: the activation
+// quantizer reads 128 BF16 values per group and writes FP8 back, so it is a
+// pure HBM stream (about 3 bytes moved per element) and is built as one.
+//
+// Activation kernel layout: a 16-lane DPP row owns one group; each lane
+// loads 8 bf16 (16 bytes), so a wave64 streams four groups = 1 KiB per load
+// instruction and stores 512 contiguous E4M3 bytes.  The group maximum is a
+// 4-step DPP reduction inside the row; the scale is stored by the row's
+// first lane.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace fp8blk {
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kQuantThreads = 256;
+constexpr int kQuantUnroll = 4;  // chunks of 8 elements per thread per block
+
+// Fast path: K % 128 == 0, x 16-byte and q 8-byte aligned.  The tensor is a
+// flat sequence of 128-element groups; chunk c (8 elements) belongs to group
+// c / 16 and its scale index is that group index (scales are [M][K/128]).
+__global__ __launch_bounds__(kQuantThreads) void quant_act_flat_kernel(
+    const u32x4 *__restrict__ x, u32x2 *__restrict__ q, float *__restrict__ scales,
+    int64_t n_chunks) {
+    const int64_t base = (int64_t)blockIdx.x * (kQuantThreads * kQuantUnroll) + threadIdx.x;
+    uint4 v[kQuantUnroll];
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+        const int64_t c = base + (int64_t)u * kQuantThreads;
+        if (c < n_chunks) {
+            const u32x4 t = __builtin_nontemporal_load(x + c);
+            v[u] = make_uint4(t.x, t.y, t.z, t.w);
+        } else {
+            v[u] = make_uint4(0, 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+        const int64_t c = base + (int64_t)u * kQuantThreads;
+        float f[8];
+        unpack8(v[u], f);
+        // n_chunks is a multiple of 16 and rows start at multiples of 16, so
+        // a DPP row is entirely in or out of range; all lanes join the DPP.
+        const float amax = row16_max(absmax8(f));
+        const QuotientCtx qc(amax);
+        const uint2 out = quant8(f, qc);
+        if (c < n_chunks) {
+            u32x2 o;
+            o.x = out.x;
+            o.y = out.y;
+            __builtin_nontemporal_store(o, q + c);
+            if ((threadIdx.x & 15) == 0) scales[c >> 4] = qc.s;
+        }
+    }
+}
+
+// General path: any K and alignment.  One DPP row per group (m, g); lane j
+// covers channels [128 g + 8 j, +8) clipped to K.  kVec: K % 8 == 0 with x
+// 16-byte and q 8-byte aligned, so every in-range chunk is a full vector.
+template <bool kVec>
+__global__ __launch_bounds__(kQuantThreads) void quant_act_general_kernel(
+    const uint16_t *__restrict__ x, uint8_t *__restrict__ q, float *__restrict__ scales,
+    int64_t M, int64_t K, int64_t G) {
+    const int64_t grp = (int64_t)blockIdx.x * (kQuantThreads / 16) + (threadIdx.x >> 4);
+    const int j = threadIdx.x & 15;
+    const bool grp_ok = grp < M * G;
+    const int64_t m = grp_ok ? grp / G : 0;
+    const int64_t g = grp_ok ? grp - m * G : 0;
+    const int64_t k0 = g * kGroup + 8 * j;
+    const int64_t off = m * K + k0;
+    int n = 0;
+    if (grp_ok && k0 < K) n = (K - k0) < 8 ? (int)(K - k0) : 8;
+    float f[8];
+    if (kVec && n == 8) {
+        unpack8(*reinterpret_cast<const uint4 *>(x + off), f);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            f[i] = i < n ? __uint_as_float((uint32_t)x[off + i] << 16) : 0.0f;
+    }
+    const float amax = row16_max(absmax8(f));
+    const QuotientCtx qc(amax);
+    const uint2 out = quant8(f, qc);
+    if (kVec && n == 8) {
+        *reinterpret_cast<uint2 *>(q + off) = out;
+    } else {
+        const uint8_t *b = reinterpret_cast<const uint8_t *>(&out);
+        for (int i = 0; i < n; ++i) q[off + i] = b[i];
+    }
+    if (grp_ok && j == 0) scales[grp] = qc.s;
+}
+
+// 128x128 weight blocks: one workgroup (4 waves) per block (nb, g), with the
+// flat block index nb * G + g in blockIdx.x.  Thread t
+// covers chunk c = t + 256 i (i < 8): block row c / 16, channels 8 (c % 16)
+// .. +8.  Block maximum: per-thread, per-wave DPP/shuffle, then across the
+// four waves through LDS.  Offline work (weights are quantized once).
+template <bool kVec>
+__global__ __launch_bounds__(kQuantThreads) void quant_weight_kernel(
+    const uint16_t *__restrict__ w, uint8_t *__restrict__ q, float *__restrict__ scales,
+    int64_t N, int64_t K, int64_t G) {
+    __shared__ float wave_amax[kQuantThreads / 64];
+    const int64_t nb = blockIdx.x / G, g = blockIdx.x - (blockIdx.x / G) * G;
+    const int64_t n0 = nb * kGroup, k0 = g * kGroup;
+    float f[8][8];
+    int cnt[8];
+    int64_t off[8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int c = threadIdx.x + kQuantThreads * i;
+        const int64_t n = n0 + (c >> 4);
+        const int64_t k = k0 + 8 * (c & 15);
+        int cn = 0;
+        if (n < N && k < K) cn = (K - k) < 8 ? (int)(K - k) : 8;
+        cnt[i] = cn;
+        off[i] = n * K + k;
+        if (kVec && cn == 8) {
+            unpack8(*reinterpret_cast<const uint4 *>(w + off[i]), f[i]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                f[i][e] = e < cn ? __uint_as_float((uint32_t)w[off[i] + e] << 16) : 0.0f;
+        }
+        amax = fmaxf(amax, absmax8(f[i]));
+    }
+    amax = wave_max(amax);
+    if ((threadIdx.x & 63) == 0) wave_amax[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wave_amax[0], wave_amax[1]), fmaxf(wave_amax[2], wave_amax[3]));
+    const QuotientCtx qc(amax);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint2 out = quant8(f[i], qc);
+        if (kVec && cnt[i] == 8) {
+            *reinterpret_cast<uint2 *>(q + off[i]) = out;
+        } else {
+            const uint8_t *b = reinterpret_cast<const uint8_t *>(&out);
+            for (int e = 0; e < cnt[i]; ++e) q[off[i] + e] = b[e];
+        }
+    }
+    if (threadIdx.x == 0) scales[nb * G + g] = qc.s;
+}
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+hipError_t launch_quant_act_1x128(const void *x, int64_t M, int64_t K, void *q, float *scales,
+                                  hipStream_t stream) {
+    const int64_t G = (K + kGroup - 1) / kGroup;
+    const bool vec = (K % 8 == 0) && aligned(x, 16) && aligned(q, 8);
+    if (K % kGroup == 0 && vec) {
+        const int64_t n_chunks = M * K / 8;
+        const int64_t per_block = (int64_t)kQuantThreads * kQuantUnroll;
+        const int64_t blocks = (n_chunks + per_block - 1) / per_block;
+        hipLaunchKernelGGL(quant_act_flat_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0,
+                           stream, static_cast<const u32x4 *>(x), static_cast<u32x2 *>(q), scales,
+                           n_chunks);
+    } else {
+        const int64_t groups = M * G;
+        const int64_t per_block = kQuantThreads / 16;
+        const int64_t blocks = (groups + per_block - 1) / per_block;
+        if (vec)
+            hipLaunchKernelGGL(quant_act_general_kernel<true>, dim3((unsigned)blocks),
+                               dim3(kQuantThreads), 0, stream, static_cast<const uint16_t *>(x),
+                               static_cast<uint8_t *>(q), scales, M, K, G);
+        else
+            hipLaunchKernelGGL(quant_act_general_kernel<false>, dim3((unsigned)blocks),
+                               dim3(kQuantThreads), 0, stream, static_cast<const uint16_t *>(x),
+                               static_cast<uint8_t *>(q), scales, M, K, G);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weight_128x128(const void *w, int64_t N, int64_t K, void *q,
+                                       float *scales, hipStream_t stream) {
+    const int64_t G = (K + kGroup - 1) / kGroup;
+    const int64_t NB = (N + kGroup - 1) / kGroup;
+    const bool vec = (K % 8 == 0) && aligned(w, 16) && aligned(q, 8);
+    const dim3 grid((unsigned)(NB * G));
+    if (vec)
+        hipLaunchKernelGGL(quant_weight_kernel<true>, grid, dim3(kQuantThreads), 0, stream,
+                           static_cast<const uint16_t *>(w), static_cast<uint8_t *>(q), scales, N,
+                           K, G);
+    else
+        hipLaunchKernelGGL(quant_weight_kernel<false>, grid, dim3(kQuantThreads), 0, stream,
+                           static_cast<const uint16_t *>(w), static_cast<uint8_t *>(q), scales, N,
+                           K, G);
+    return hipGetLastError();
+}
+
+}  // namespace fp8blk

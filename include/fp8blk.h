@@ -1,0 +1,149 @@
+/*
+ * fp8blk — fine-grained FP8 quantization and block-scaled FP8 GEMM for
+ * MI355X (gfx950).  C ABI.
+ *
+ * The method (page "dssusan.co.kr qna 93378", passage on Figure 7 (a) and the
+ * passages that follow it):
+ *   - activations are grouped and scaled per token per 128 channels (1x128
+ *     tiles); weights per 128 input channels x 128 output channels (128x128
+ *     blocks);
+ *   - E4M3 is used for every FP8 tensor;
+ *   - the per-group scaling factors run along the GEMM inner dimension K and
+ *     are multiplied into the FP32 partial sums as the dequantization step
+ *     (page "kailasan.com recruit 147436", passage on promotion, Figure 7 (b));
+ *   - the GEMMs take FP8 operands and produce BF16 or FP32.
+ * Readings where the pages are silent: OCP E4M3FN (largest finite 448), scale
+ * s = fl32(amax / 448) per group, code = E4M3 round-to-nearest-even of
+ * fl32(x / s), all-zero group -> s = 0 and zero bytes, promotion after every
+ * 128-deep K block (one scale group).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers owned by the caller; the library never
+ *     allocates, frees or synchronizes.  bf16 data is passed as raw 16-bit
+ *     patterns, E4M3 data as bytes, scales as IEEE binary32.
+ *   - All tensors are dense and row-major.
+ *   - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the default
+ *     stream) and runs asynchronously.  Device faults surface at the caller's
+ *     next synchronization on that stream.
+ *   - Arguments are validated before anything is enqueued; on any error
+ *     nothing is written.  No C++ exception crosses this boundary.
+ *   - The library keeps no mutable global state: calls are reentrant and
+ *     thread-safe (concurrent calls on different streams must not share
+ *     output or workspace buffers).
+ *   - Sizes of zero (M = 0, T = 0, K = 0 for the quantizers) are valid no-ops.
+ *   - Inputs must be finite; NaN/Inf inputs are outside the contract and are
+ *     not checked.
+ */
+#ifndef FP8BLK_H_
+#define FP8BLK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP8_OK = 0,
+    FP8_ERR_NULL = 1,      /* a required pointer is NULL */
+    FP8_ERR_SHAPE = 2,     /* negative size, or a GEMM size not a multiple of 128 */
+    FP8_ERR_ALIGN = 3,     /* a GEMM operand pointer is not 16-byte aligned */
+    FP8_ERR_DTYPE = 4,     /* out_dtype is not one of fp8_out_dtype */
+    FP8_ERR_WORKSPACE = 5, /* workspace NULL with a nonzero size, or not 256-byte aligned */
+    FP8_ERR_HIP = 6        /* a HIP launch failed (hipGetLastError after the launch) */
+} fp8_status;
+
+typedef enum { FP8_OUT_F32 = 0, FP8_OUT_BF16 = 1 } fp8_out_dtype;
+
+/*
+ * 1x128 activation quantization (page "dssusan.co.kr qna 93378", Figure 7 (a):
+ * one scale per token per 128 channels; page "why-be.co.kr as_center 36949",
+ * passage on the quantization round trip: 128 BF16 values in, FP8 out).
+ *   x_bf16  [M][K] bf16, input
+ *   q_e4m3  [M][K] E4M3 bytes, output
+ *   scales  [M][ceil(K/128)] fp32, output; scales[m][g] = fl32(amax/448) of
+ *           channels [128g, min(128g+128, K)) of token m
+ * Any M, K >= 0 and any alignment (a partial last group holds K % 128
+ * channels).  Errors: FP8_ERR_NULL (a pointer NULL while M*K > 0),
+ * FP8_ERR_SHAPE (M or K negative), FP8_ERR_HIP.
+ */
+fp8_status fp8_quant_act_1x128(const void *x_bf16, int64_t M, int64_t K,
+                               void *q_e4m3, float *scales, void *hip_stream);
+
+/*
+ * 128x128 weight block quantization (page "dssusan.co.kr qna 93378",
+ * Figure 7 (a): one scale per 128 input x 128 output channels).
+ *   w_bf16  [N][K] bf16 (row n = output channel), input
+ *   q_e4m3  [N][K] E4M3 bytes, output
+ *   scales  [ceil(N/128)][ceil(K/128)] fp32, output
+ * Any N, K >= 0; edge blocks hold what remains.  A stack of E expert
+ * matrices [E][N][K] with N % 128 == 0 is quantized as one [E*N][K] call.
+ * Errors as for fp8_quant_act_1x128.
+ */
+fp8_status fp8_quant_weight_128x128(const void *w_bf16, int64_t N, int64_t K,
+                                    void *q_e4m3, float *scales,
+                                    void *hip_stream);
+
+/*
+ * Block-scaled FP8 GEMM (page "dssusan.co.kr qna 93378", passages on scaling
+ * along the inner dimension K and on FP8-in / BF16-or-FP32-out GEMMs; page
+ * "kailasan.com recruit 147436", Figure 7 (b): scaled partial sums added into
+ * FP32 accumulators):
+ *   C[m][n] = sum_kb a_scales[m][kb] * w_scales[n/128][kb]
+ *                    * sum_{k in block kb} a[m][k] * w[n][k]
+ *   a_e4m3    [M][K] E4M3, a_scales [M][K/128] fp32
+ *   w_e4m3    [N][K] E4M3, w_scales [N/128][K/128] fp32
+ *   c         [M][N], fp32 (FP8_OUT_F32) or bf16 by round-to-nearest-even of
+ *             the fp32 accumulator (FP8_OUT_BF16)
+ * K % 128 == 0 and N % 128 == 0 are required (FP8_ERR_SHAPE otherwise);
+ * a_e4m3, w_e4m3 and c must be 16-byte aligned (FP8_ERR_ALIGN).  M may be
+ * anything >= 0.
+ *   workspace / workspace_bytes: optional caller-owned device scratch
+ *   (256-byte aligned).  fp8_gemm_workspace_bytes() gives the size that
+ *   enables the split-K path for small M; with less (or NULL and 0) the
+ *   kernel runs without it.  Its contents need no initialization and are
+ *   undefined afterwards.
+ * Accumulation is FP32 in a fixed order: results are deterministic for a
+ * given shape and workspace size.
+ */
+fp8_status fp8_block_gemm(const void *a_e4m3, const float *a_scales,
+                          const void *w_e4m3, const float *w_scales, void *c,
+                          int out_dtype, int64_t M, int64_t N, int64_t K,
+                          void *workspace, size_t workspace_bytes,
+                          void *hip_stream);
+
+/*
+ * Grouped (MoE) block-scaled FP8 GEMM over expert-sorted tokens (page
+ * "kailasan.com recruit 147436", passage on the decoding stage: each expert
+ * sees a small batch of tokens and only its own parameters are loaded).
+ *   a_e4m3        [T][K] E4M3, rows sorted by expert; a_scales [T][K/128]
+ *   w_e4m3        [E][N][K] E4M3; w_scales [E][N/128][K/128]
+ *   group_offsets [E+1] int32 on the DEVICE: rows [off[e], off[e+1]) belong
+ *                 to expert e.  Offsets are clamped to [0, T]; a decreasing
+ *                 range is empty.  The host never reads them.
+ *   c             [T][N] fp32 or bf16; rows outside every expert's range are
+ *                 left untouched.
+ * Each routed row r of expert e gets C[r] = block GEMM of (a[r], W[e]).
+ * Requirements and errors as fp8_block_gemm, plus FP8_ERR_SHAPE for E <= 0
+ * while T > 0.  The workspace is accepted for interface symmetry and unused.
+ */
+fp8_status fp8_block_grouped_gemm(const void *a_e4m3, const float *a_scales,
+                                  const void *w_e4m3, const float *w_scales,
+                                  const int32_t *group_offsets, int64_t E,
+                                  int64_t T, void *c, int out_dtype, int64_t N,
+                                  int64_t K, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream);
+
+/* Workspace bytes that let fp8_block_gemm use its split-K path for this
+ * shape (0 when the shape does not use it). */
+size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int out_dtype);
+
+/* Static, human-readable name of a status code. */
+const char *fp8_status_string(fp8_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BLK_H_ */

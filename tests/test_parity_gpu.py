@@ -1,0 +1,273 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Quantizers: E4M3 bytes and fp32 scale bits must be identical.  GEMMs: the
+relative Frobenius error against the oracle's binary64 reference must be
+within 1e-3 (FP32 out) / 8e-3 (BF16 out), and within the level FP32
+accumulation actually gives.  Inputs come from the seeded generator; every
+oracle input is the generator's or the oracle's own output.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fp8_fine_grained_token_amd import binding as B
+from fp8_fine_grained_token_amd import inputs as I
+
+from .gpu_util import check_gemm, dev, dev_bf16, host, log, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = torch()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    yield
+    t.cuda.synchronize()
+
+
+def quant_act_gpu(bits):
+    q, s = B.fp8_quant_act_1x128(dev_bf16(bits))
+    return host(q), host(s)
+
+
+def assert_quant_equal(qg, sg, qo, so, what):
+    nbad = int((qg != qo).sum())
+    sbad = int((sg.view(np.uint32) != so.view(np.uint32)).sum())
+    log(f"  {what}: byte mismatches={nbad} scale mismatches={sbad}")
+    if nbad:
+        idx = np.argwhere(qg != qo)[:5]
+        log("  first mismatches (row, col, gpu, oracle):",
+            [(int(i), int(j), int(qg[i, j]), int(qo[i, j])) for i, j in idx])
+    assert nbad == 0 and sbad == 0
+
+
+# ---- activation quantizer ---------------------------------------------------
+
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 300), (17, 7168), (64, 1000), (5, 1001),
+                                 (33, 8), (2, 130)])
+def test_quant_act_shapes(M, K):
+    x, _ = I.activations(np.random.default_rng(M * 7 + K), M, K, 0.01, 50.0)
+    qo, so = oracle.quant_act_1x128(x)
+    qg, sg = quant_act_gpu(x)
+    assert_quant_equal(qg, sg, qo, so, f"act {M}x{K}")
+
+
+def test_quant_act_workload_4096x7168():
+    x, _ = I.config_quant(seed=0)
+    log("  oracle quantizing 4096x7168 ...")
+    qo, so = oracle.quant_act_1x128(x)
+    qg, sg = quant_act_gpu(x)
+    assert_quant_equal(qg, sg, qo, so, "act 4096x7168")
+
+
+def test_quant_act_special_groups():
+    K = 512
+    x = np.zeros((6, K), np.uint16)
+    x[1, :] = 0x8000                                   # all -0.0
+    x[2, 5] = 0x0001                                   # smallest subnormal amax
+    x[2, 130] = 0x8001
+    x[3, :128] = I.f32_to_bf16_bits(np.linspace(-1, 1, 128, dtype=np.float32))
+    x[4, :] = 0x7F7F                                   # largest finite everywhere
+    x[5, 256:384] = I.f32_to_bf16_bits(np.float32(448.0 * 2.0 ** -130) * np.ones(128, np.float32))
+    qo, so = oracle.quant_act_1x128(x)
+    qg, sg = quant_act_gpu(x)
+    assert_quant_equal(qg, sg, qo, so, "special groups")
+
+
+def test_quant_act_misaligned_pointer():
+    # a row-offset view whose base is only 2-byte aligned takes the general path
+    M, K = 9, 257
+    x, _ = I.activations(np.random.default_rng(3), M + 1, K)
+    t = torch()
+    big = dev_bf16(x)
+    view = big.view(-1)[K:].view(M, K)
+    q, s = B.fp8_quant_act_1x128(view)
+    qo, so = oracle.quant_act_1x128(np.ascontiguousarray(x[1:]))
+    assert_quant_equal(host(q), host(s), qo, so, "misaligned")
+    del t
+
+
+# ---- weight quantizer ---------------------------------------------------------
+
+@pytest.mark.parametrize("N,K", [(256, 512), (200, 130), (128, 7168), (2048, 7168), (3, 5)])
+def test_quant_weight_shapes(N, K):
+    w = I.weights(np.random.default_rng(N + K), (N, K))
+    qo, so = oracle.quant_weight_128x128(w)
+    q, s = B.fp8_quant_weight_128x128(dev_bf16(w))
+    assert_quant_equal(host(q), host(s), qo, so, f"weight {N}x{K}")
+
+
+# ---- dense GEMM -----------------------------------------------------------------
+
+def quantize(g):
+    qa, sa = oracle.quant_act_1x128(g.a_bf16)
+    qw, sw = oracle.quant_weight_128x128(g.w_bf16)
+    return qa, sa, qw, sw
+
+
+def run_gemm(qa, sa, qw, sw, out, workspace=None):
+    return B.fp8_block_gemm(dev(qa), dev(sa), dev(qw), dev(sw), out_dtype=out,
+                            workspace=workspace)
+
+
+def test_gemm_tiny_fp32_out():
+    g = I.config_tiny(seed=0)
+    qa, sa, qw, sw = quantize(g)
+    R = oracle.block_gemm(qa, sa, qw, sw)
+    check_gemm(run_gemm(qa, sa, qw, sw, "f32"), R, "f32", "tiny 128x256x512 f32")
+
+
+@pytest.mark.parametrize("M", [1, 15, 17, 129, 255, 300])
+@pytest.mark.parametrize("N,K", [(128, 128), (384, 640)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_ragged(M, N, K, out):
+    g = I.gemm_inputs(M, N, K, seed=M * 1000 + N + K, outlier_frac=0.01, outlier_mult=20.0)
+    qa, sa, qw, sw = quantize(g)
+    R = oracle.block_gemm(qa, sa, qw, sw)
+    check_gemm(run_gemm(qa, sa, qw, sw, out), R, out, f"{M}x{N}x{K} {out}")
+
+
+def test_gemm_decode_workload_with_and_without_workspace():
+    g = I.config_decode(seed=0)
+    qa, sa, qw, sw = quantize(g)
+    log("  oracle GEMM 256x2048x7168 ...")
+    R = oracle.block_gemm(qa, sa, qw, sw)
+    t = torch()
+    nbytes = B.fp8_gemm_workspace_bytes(256, 2048, 7168, "bf16")
+    assert nbytes > 0
+    ws = t.empty(nbytes, dtype=t.uint8, device="cuda")
+    c1 = run_gemm(qa, sa, qw, sw, "bf16", workspace=ws)
+    c2 = run_gemm(qa, sa, qw, sw, "bf16")
+    check_gemm(c1, R, "bf16", "decode split-K")
+    check_gemm(c2, R, "bf16", "decode no workspace")
+    c3 = run_gemm(qa, sa, qw, sw, "f32", workspace=ws)
+    check_gemm(c3, R, "f32", "decode split-K f32")
+
+
+def test_gemm_dense_workload_sampled_rows():
+    g = I.config_dense(seed=0)
+    qa, sa, qw, sw = quantize(g)
+    c = host(run_gemm(qa, sa, qw, sw, "bf16"))
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 2047, 2048, 4094, 4095],
+                                     np.random.default_rng(1).choice(4096, 22, replace=False)]))
+    log(f"  oracle GEMM on {rows.size} sampled rows of 4096x7168x7168 ...")
+    R = oracle.block_gemm(qa, sa, qw, sw, rows)
+    from .gpu_util import rel_fro
+    rf = rel_fro(c[rows], R)
+    log(f"  dense sampled rows: rel_fro={rf:.3e}")
+    assert np.isfinite(c).all()
+    assert rf <= 4e-3
+
+
+def test_gemm_power_of_two_metamorphic_and_deterministic():
+    # Scaling the activation scales by 2^j scales an FP32 result by exactly
+    # 2^j; two runs of the same call are bitwise identical.
+    g = I.gemm_inputs(200, 256, 1024, seed=9)
+    qa, sa, qw, sw = quantize(g)
+    c0 = host(run_gemm(qa, sa, qw, sw, "f32"))
+    c1 = host(run_gemm(qa, sa, qw, sw, "f32"))
+    c2 = host(run_gemm(qa, sa * np.float32(8.0), qw, sw, "f32"))
+    assert np.array_equal(c0.view(np.uint32), c1.view(np.uint32))
+    assert np.array_equal(c2, c0 * np.float32(8.0))
+
+
+def test_gemm_zero_scales_give_zero():
+    g = I.gemm_inputs(64, 128, 256, seed=10)
+    qa, sa, qw, sw = quantize(g)
+    c = host(run_gemm(qa, np.zeros_like(sa), qw, sw, "f32"))
+    assert np.all(c == 0)
+
+
+# ---- grouped GEMM -----------------------------------------------------------------
+
+def quantize_grouped(gi):
+    qa, sa = oracle.quant_act_1x128(gi.a_bf16)
+    E, N, K = gi.w_bf16.shape
+    qw, sw = oracle.quant_weight_128x128(gi.w_bf16.reshape(E * N, K))
+    return qa, sa, qw.reshape(E, N, K), sw.reshape(E, N // 128, K // 128)
+
+
+def run_grouped(qa, sa, qw, sw, off, out, c=None):
+    return B.fp8_block_grouped_gemm(dev(qa), dev(sa), dev(qw), dev(sw), dev(off.astype(np.int32)),
+                                    out_dtype=out, c=c)
+
+
+@pytest.mark.parametrize("counts,T", [
+    ([20, 0, 33, 1, 10], 70),        # empty expert and 6 unrouted rows at the end
+    ([0, 0, 300], 300),              # one expert holds every token
+    ([129, 127, 1, 0, 256], 513),
+    ([0, 0, 0], 16),                 # nothing routed: C untouched
+])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_grouped_edge_cases(counts, T, out):
+    E = len(counts)
+    gi = I.grouped_inputs(E, T, 256, 384, seed=sum(counts) + E, counts=counts)
+    qa, sa, qw, sw = quantize_grouped(gi)
+    R, found = oracle.grouped_gemm(qa, sa, qw, sw, gi.offsets)
+    t = torch()
+    dt = t.float32 if out == "f32" else t.bfloat16
+    c = t.full((T, 256), 7.0, dtype=dt, device="cuda")
+    run_grouped(qa, sa, qw, sw, gi.offsets, out, c=c)
+    ch = host(c)
+    routed = int(gi.offsets[-1])
+    assert np.all(ch[routed:] == 7.0), "unrouted rows were written"
+    if routed:
+        check_gemm(c[:routed], R[:routed], out, f"grouped {counts} {out}")
+
+
+def test_grouped_garbage_offsets_are_memory_safe():
+    # Offsets beyond T and decreasing ranges are clamped/empty: no fault, and
+    # rows outside [clamped off[0], clamped off[E]) stay untouched.
+    E, T = 4, 100
+    gi = I.grouped_inputs(E, T, 128, 256, seed=5, counts=[25, 25, 25, 25])
+    qa, sa, qw, sw = quantize_grouped(gi)
+    off = np.array([10, 60, 40, 90, 5000], dtype=np.int32)  # decreasing then past T
+    t = torch()
+    c = t.full((T, 128), 7.0, dtype=t.float32, device="cuda")
+    run_grouped(qa, sa, qw, sw, off, "f32", c=c)
+    t.cuda.synchronize()
+    ch = host(c)
+    assert np.all(ch[:10] == 7.0)
+    R, _ = oracle.grouped_gemm(qa, sa, qw, sw, np.array([10, 60, 60, 90, 100], np.int32))
+    # rows [10, 60) belong to expert 0, [60, 90) to expert 2 (expert 1 empty),
+    # [90, 100) to expert 3; rows [40, 60) are also claimed by expert 2's
+    # clamped range [40, 90) and so are not compared.
+    check_gemm(c[10:40], R[10:40], "f32", "garbage offsets expert 0")
+    check_gemm(c[90:100], R[90:100], "f32", "garbage offsets expert 3")
+
+
+def test_grouped_workload_sampled_rows():
+    gi = I.config_grouped(seed=0)
+    log("  quantizing grouped workload with the oracle ...")
+    qa, sa, qw, sw = quantize_grouped(gi)
+    c = host(run_grouped(qa, sa, qw, sw, gi.offsets, "bf16"))
+    off = gi.offsets
+    rng = np.random.default_rng(2)
+    rows = []
+    for e in range(gi.E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            rows += [lo, hi - 1] + list(rng.integers(lo, hi, size=1))
+    rows = np.unique(np.array(rows))
+    log(f"  oracle grouped GEMM on {rows.size} sampled rows ...")
+    R, found = oracle.grouped_gemm(qa, sa, qw, sw, off, rows)
+    assert found.all()
+    from .gpu_util import rel_fro
+    rf = rel_fro(c[rows], R)
+    log(f"  grouped sampled rows: rel_fro={rf:.3e}")
+    assert np.isfinite(c).all()
+    assert rf <= 4e-3
+
+
+def test_quant_then_gemm_chain_matches_oracle_chain():
+    # The GPU quantizer's output fed to the GPU GEMM equals the oracle chain.
+    g = I.gemm_inputs(96, 256, 768, seed=12, outlier_frac=0.01, outlier_mult=50.0)
+    qa_d, sa_d = B.fp8_quant_act_1x128(dev_bf16(g.a_bf16))
+    qw_d, sw_d = B.fp8_quant_weight_128x128(dev_bf16(g.w_bf16))
+    c = B.fp8_block_gemm(qa_d, sa_d, qw_d, sw_d, out_dtype="f32")
+    qa, sa, qw, sw = quantize(g)
+    R = oracle.block_gemm(qa, sa, qw, sw)
+    check_gemm(c, R, "f32", "quant->gemm chain")
