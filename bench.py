@@ -1,0 +1,298 @@
+"""Benchmark of the fine-grained FP8 hot path on one MI355X.
+
+One step = one pass of the hot path over one batch of tokens:
+  1x128 activation quantization of X bf16 [4096][7168] (0.1% outlier
+  channels x100) -> block-scaled FP8 GEMM with W [7168][7168] (quantized
+  128x128 once, before timing, as weights are) -> BF16 C [4096][7168].
+The metric is the step's FP8 GEMM throughput in TFLOP/s (2*M*N*K algorithmic
+flops per step over the measured step time, quantization included).
+
+Printed as one JSON line, with:
+  * roofline: the dominant kernel (the GEMM), its algorithmic flops over its
+    average duration measured with HIP events on its stream inside the timed
+    region, against the dense FP8 MFMA peak; traffic = HBM bytes per launch
+    from committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by the
+    copy-kernel calibration, or null if the kernel source changed since;
+  * parts: each kernel on its own workload (act quantizer GB/s vs HBM with
+    the caches flushed before every launch, dense / decode / grouped GEMM
+    TFLOP/s vs MFMA and GB/s vs HBM);
+  * cpu_baseline: the CPU oracle timed on this host on a bounded sample of
+    the same step (first 256 tokens).
+
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+       [--no-parts] [--no-cpu-baseline] [--copy-calib]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_dense_gemm.json")
+GEMM_SOURCE = os.path.join(ROOT, "fp8_fine_grained_token_amd", "csrc", "gemm.hip")
+
+M, N, K = 4096, 7168, 7168
+CPU_SAMPLE_ROWS = 256
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def dense_gemm_bytes(m, n, k, out_bytes=2):
+    return m * k + n * k + m * n * out_bytes + 4 * m * (k // 128) + 4 * (n // 128) * (k // 128)
+
+
+def quant_bytes(m, k):
+    return 2 * m * k + m * k + 4 * m * ((k + 127) // 128)
+
+
+def traffic_from_counters():
+    """HBM bytes per GEMM launch from the committed counter summary, or None
+    when it is missing or was taken on a different gemm.hip."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("gemm_source_sha256") != source_hash(GEMM_SOURCE):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """HIP events around launches on the current (torch) stream."""
+
+    def __init__(self, torch, n):
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+        self.i = 0
+
+    def start(self):
+        self.ev[self.i][0].record()
+
+    def stop(self):
+        self.ev[self.i][1].record()
+        self.i += 1
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.ev[: self.i]) / max(self.i, 1)
+
+    def median_ms(self):
+        v = sorted(a.elapsed_time(b) for a, b in self.ev[: self.i])
+        return v[len(v) // 2] if v else 0.0
+
+
+def to_dev_bf16(torch, bits):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def measure_parts(torch, F, I, X, qa, sa, qw, sw, C, iters=20):
+    """Each kernel on its own workload; caches flushed before every launch."""
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    parts = {}
+
+    def timed(fn, n):
+        t = Timer(torch, n)
+        for _ in range(n):
+            flush.fill_(1.0)
+            t.start()
+            fn()
+            t.stop()
+        torch.cuda.synchronize()
+        return t.median_ms()
+
+    # activation quantizer, 4096 x 7168
+    ms = timed(lambda: F.fp8_quant_act_1x128(X, qa, sa), iters)
+    b = quant_bytes(M, K)
+    parts["act_quant_4096x7168"] = {
+        "us": ms * 1e3, "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
+        "bytes": b}
+
+    # dense GEMM alone, 4096 x 7168 x 7168
+    ms = timed(lambda: F.fp8_block_gemm(qa, sa, qw, sw, out_dtype="bf16", c=C), iters)
+    fl = 2 * M * N * K
+    parts["dense_gemm_4096x7168x7168"] = {
+        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
+
+    # decode GEMM, 256 x 2048 x 7168 (split-K with workspace)
+    import numpy as np
+    gd = I.config_decode(seed=0)
+    xa = to_dev_bf16(torch, gd.a_bf16)
+    xw = to_dev_bf16(torch, gd.w_bf16)
+    da, dsa = F.fp8_quant_act_1x128(xa)
+    dw, dsw = F.fp8_quant_weight_128x128(xw)
+    nbytes = F.fp8_gemm_workspace_bytes(256, 2048, 7168, "bf16")
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda") if nbytes else None
+    dc = torch.empty((256, 2048), dtype=torch.bfloat16, device="cuda")
+    ms = timed(lambda: F.fp8_block_gemm(da, dsa, dw, dsw, out_dtype="bf16", c=dc, workspace=ws),
+               iters)
+    fl = 2 * 256 * 2048 * 7168
+    b = dense_gemm_bytes(256, 2048, 7168)
+    parts["decode_gemm_256x2048x7168"] = {
+        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
+        "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
+        "split_k_workspace_bytes": nbytes}
+    del xa, xw, da, dsa, dw, dsw, ws, dc
+
+    # grouped MoE GEMM, 32 experts / 8192 tokens, N=4096, K=7168
+    log("bench: generating the grouped workload ...")
+    gi = I.config_grouped(seed=0)
+    ga = to_dev_bf16(torch, gi.a_bf16)
+    gq, gsa = F.fp8_quant_act_1x128(ga)
+    del ga
+    gwb = to_dev_bf16(torch, gi.w_bf16.reshape(gi.E * gi.N, gi.K))
+    gw, gsw = F.fp8_quant_weight_128x128(gwb)
+    del gwb
+    gw = gw.view(gi.E, gi.N, gi.K)
+    gsw = gsw.view(gi.E, gi.N // 128, gi.K // 128)
+    off = torch.from_numpy(gi.offsets).cuda()
+    gc = torch.empty((gi.T, gi.N), dtype=torch.bfloat16, device="cuda")
+    ms = timed(lambda: F.fp8_block_grouped_gemm(gq, gsa, gw, gsw, off, out_dtype="bf16", c=gc),
+               iters)
+    fl = 2 * int(gi.counts.sum()) * gi.N * gi.K
+    b = (gi.T * gi.K + gi.E * gi.N * gi.K + gi.T * gi.N * 2 + 4 * gi.T * (gi.K // 128)
+         + 4 * gi.E * (gi.N // 128) * (gi.K // 128))
+    parts["grouped_gemm_e32_t8192_n4096_k7168"] = {
+        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
+        "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
+        "counts": [int(c) for c in gi.counts]}
+    del gq, gsa, gw, gsw, gc, flush
+    torch.cuda.empty_cache()
+    return parts
+
+
+def copy_calibration(torch, nbytes=1 << 30, iters=5):
+    """A plain device copy of known size, for scaling rocprofv3 counters."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(iters):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"copy_bytes_each_way": nbytes, "iters": iters}
+
+
+def cpu_baseline(I, X_bits, w_bits):
+    """The oracle on the first CPU_SAMPLE_ROWS tokens of the same step."""
+    import numpy as np
+    import oracle
+    x = np.ascontiguousarray(X_bits[:CPU_SAMPLE_ROWS])
+    qw, sw = oracle.quant_weight_128x128(w_bits)      # offline weights, not timed
+    t0 = time.perf_counter()
+    qa, sa = oracle.quant_act_1x128(x)
+    oracle.block_gemm(qa, sa, qw, sw)
+    dt = time.perf_counter() - t0
+    flops = 2 * CPU_SAMPLE_ROWS * N * K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"first {CPU_SAMPLE_ROWS} of {M} tokens: 1x128 quantization of "
+                      f"{CPU_SAMPLE_ROWS}x{K} + binary64 block-scaled GEMM "
+                      f"{CPU_SAMPLE_ROWS}x{N}x{K}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-parts", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the hot path is data-parallel and this "
+              "build runs it on a single MI355X (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_fine_grained_token_amd as F
+    from fp8_fine_grained_token_amd import inputs as I
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    F.lib()
+
+    log("bench: generating inputs ...")
+    X_bits, _ = I.config_quant(seed=0)                       # 4096 x 7168, outliers
+    w_bits = I.config_dense(seed=0).w_bf16                   # 7168 x 7168, N(0, 0.02)
+    X = to_dev_bf16(torch, X_bits)
+    Wb = to_dev_bf16(torch, w_bits)
+    qw, sw = F.fp8_quant_weight_128x128(Wb)                  # offline: once, untimed
+    qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+
+    gemm_t = Timer(torch, args.steps)
+    quant_t = Timer(torch, args.steps)
+
+    def step(timed):
+        if timed:
+            quant_t.start()
+        F.fp8_quant_act_1x128(X, qa, sa)
+        if timed:
+            quant_t.stop()
+            gemm_t.start()
+        F.fp8_block_gemm(qa, sa, qw, sw, out_dtype="bf16", c=C)
+        if timed:
+            gemm_t.stop()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) / args.steps * 1e3
+    flops = 2 * M * N * K
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    gemm_ms = gemm_t.mean_ms()
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    result = {
+        "metric": "FP8 block-scaled GEMM TFLOP/s + % FP8 MFMA peak; act-quant GB/s % HBM",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate, bf16 out)",
+        "data": "synthetic",
+        "config": {"workload": "prefill linear: 1x128 act-quant of 4096x7168 bf16 (0.1% outlier "
+                               "channels x100) + fp8_block_gemm M=4096 N=7168 K=7168 bf16 out",
+                   "M": M, "N": N, "K": K, "weights": "128x128-quantized once before timing",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "dense_gemm_kernel", "achieved": round(achieved, 2),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+                     "traffic": traffic_from_counters(),
+                     "gemm_us": round(gemm_ms * 1e3, 2),
+                     "act_quant_us_in_step": round(quant_t.mean_ms() * 1e3, 2)},
+    }
+    if args.copy_calib:
+        result["copy_calibration"] = copy_calibration(torch)
+    if not args.no_parts:
+        log("bench: per-kernel parts ...")
+        result["parts"] = measure_parts(torch, F, I, X, qa, sa, qw, sw, C)
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline ...")
+        result["cpu_baseline"] = cpu_baseline(I, X_bits, w_bits)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

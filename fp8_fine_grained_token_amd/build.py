@@ -34,7 +34,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB_PATH + ".tmp%d" % os.getpid()
     cmd = [
         hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
-        "-ffp-contract=off", "-fno-gpu-rdc",
+        "-ffp-contract=off", "-fno-gpu-rdc", "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",
         "-I" + os.path.join(os.path.dirname(HERE), "include"),
