@@ -93,20 +93,21 @@ struct TileCfg {
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns sit in one 128-block");
 };
 
+// One LDS pipeline stage: the A (token) and W (weight) tiles of one K block
+// and its scales.
 template <int BM, int BN>
-struct __align__(16) Smem {
-    uint8_t a[2][BM * 128];
-    uint8_t b[2][BN * 128];
-    float sa[2][BM];
-    float sw[2][64];
+struct __align__(16) Stage {
+    uint8_t a[BM * 128];
+    uint8_t b[BN * 128];
+    float sa[BM];
+    float sw[64];
 };
 
-// 16-byte chunk j of LDS row r is stored at chunk j ^ swz(r).  Rows r and
-// r ^ 1 sit in one 256-byte line, so the XOR key is taken from r >> 1: the
-// 16 rows one MFMA operand read touches land on 16 distinct 16-byte bank
-// groups.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int lds_off(int r, int chunk) { return r * 128 + ((chunk ^ swz(r)) << 4); }
+// 16-byte chunk j of LDS row r is stored at chunk j ^ (r & 7): the 8 rows
+// that one 8-lane group of an MFMA operand read touches land on 8 distinct
+// 16-byte bank groups, and a tile copy (8 lanes per 128-byte row) stays one
+// contiguous 128-byte row.
+__device__ __forceinline__ int lds_off(int r, int chunk) { return r * 128 + ((chunk ^ (r & 7)) << 4); }
 
 __device__ __forceinline__ v8i make_v8i(const uint4 &lo, const uint4 &hi) {
     v8i v;
@@ -116,32 +117,91 @@ __device__ __forceinline__ v8i make_v8i(const uint4 &lo, const uint4 &hi) {
 }
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
-typedef __attribute__((address_space(1))) void *glb_ptr_t;
 
-// Asynchronous global -> LDS copies (global_load_lds_dwordx4 / _dword): the
-// wave's 64 lanes fill 64 * 16 (or 64 * 4) consecutive LDS bytes starting at
-// the wave-uniform lds_wave_base, lane L at offset 16 L (4 L).
-__device__ __forceinline__ void load_lds16(const void *g, void *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((glb_ptr_t)(g), (lds_ptr_t)(lds_wave_base), 16, 0, 0);
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [base, base + bytes): loads whose per-lane offset
+// is at or past `bytes` return zero instead of reading memory.
+__device__ __forceinline__ v4i make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    v4i r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xFFFF);  // stride 0
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
 }
-__device__ __forceinline__ void load_lds4(const void *g, void *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((glb_ptr_t)(g), (lds_ptr_t)(lds_wave_base), 4, 0, 0);
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(uint32_t)(uintptr_t)(lds_ptr_t)(const_cast<void *>(p)));
+}
+
+// Asynchronous global -> LDS copies (buffer_load_dwordx4 / _dword with the
+// lds modifier): the wave's 64 lanes fill 64 * 16 (or 64 * 4) consecutive
+// LDS bytes from the wave-uniform LDS address in M0, lane L at offset 16 L
+// (4 L); voffset is the lane's byte offset in the buffer, soffset the K
+// block's.  They are written as inline assembly on purpose: the compiler
+// orders every LDS read after all outstanding LDS-DMA copies it knows of,
+// which would serialize the next block's copy with this block's MFMAs.
+// These instructions have no register results; the data they write is read
+// only after the explicit "s_waitcnt vmcnt(0)" and barrier that end each
+// main-loop iteration.
+__device__ __forceinline__ void copy16(const v4i &r, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(soff), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void copy4(const v4i &r, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(soff), "s"(lds)
+                 : "memory", "m0");
+}
+
+// Per-tile operand view for the main loop.  Rows [row0, row0 + rows) of A
+// and columns [n0, n0 + cols) of W are valid; the buffer bounds make every
+// other row read as zero, so ragged edges need no clamping.
+struct TileOperands {
+    v4i a, w, sa, sw;
+};
+
+template <class C>
+__device__ __forceinline__ TileOperands tile_operands(const uint8_t *a, const float *sa,
+                                                      const uint8_t *w, const float *sw,
+                                                      int64_t row0, int64_t rows, int64_t n0,
+                                                      int64_t cols, int64_t K, int G) {
+    TileOperands t;
+    const int64_t ra = rows < C::BM ? rows : C::BM;
+    const int64_t cw = cols < C::BN ? cols : C::BN;
+    t.a = make_rsrc(a + row0 * K, (uint32_t)(ra * K));
+    t.w = make_rsrc(w + n0 * K, (uint32_t)(cw * K));
+    t.sa = make_rsrc(sa + row0 * G, (uint32_t)(ra * G * 4));
+    const int64_t nb0 = n0 >> 7, nbs = ((n0 + cw - 1) >> 7) - nb0 + 1;
+    t.sw = make_rsrc(sw + nb0 * G, (uint32_t)(nbs * G * 4));
+    return t;
 }
 
 // Runs K blocks [kb0, kb1) of one BM x BN tile and leaves the FP32
-// accumulators in acc.  Rows are read at min(row0 + r, row_last) and columns
-// at min(n0 + c, n_last), so a ragged edge never reads outside the operands
-// (the extra rows/columns compute values that the caller does not store).
+// accumulators in acc.
 //
-// Pipeline (two LDS stages): at the top of iteration kb every wave issues
-// its direct global->LDS copies of block kb + 1 into the other stage, then
-// runs the MFMAs of block kb from LDS, then waits for its copies and meets
-// the others at one barrier.
+// Pipeline: two LDS stages.  At the top of an iteration every wave issues
+// its direct global->LDS copies of the next K block into the other stage,
+// then runs the current block from LDS: the weight fragments, then one
+// token fragment per 16-row tile, each followed by its MFMAs and promotion
+// FMAs.  Then the wave waits for its copies and meets the others at one
+// barrier, so the copies overlap the whole MFMA phase.
+//
+// Copy t of wave v fills LDS rows [8 (v + kWaves t), +8): lane L writes
+// physical chunk L % 8 of row L / 8, i.e. logical chunk (L % 8) ^ ((L / 8) & 7)
+// of that row.
 template <class C>
-__device__ __forceinline__ void tile_mainloop(
-    const uint8_t *__restrict__ a, const float *__restrict__ sa, const uint8_t *__restrict__ w,
-    const float *__restrict__ sw, int64_t row0, int64_t row_last, int64_t n0, int64_t n_last,
-    int64_t K, int G, int kb0, int kb1, Smem<C::BM, C::BN> &sm, v4f (&acc)[C::kTM][C::kTN]) {
+__device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K, int G, int kb0,
+                                              int kb1, int sw_first_block_of_wave,
+                                              Stage<C::BM, C::BN> *stages,
+                                              v4f (&acc)[C::kTM][C::kTN]) {
+    using S = Stage<C::BM, C::BN>;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -155,92 +215,107 @@ __device__ __forceinline__ void tile_mainloop(
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Global source of this lane for each of its wave's copy instructions.
-    // Copy t of wave w fills LDS rows [8 (w + kWaves t), +8); lane L writes
-    // physical chunk L % 8 of row L / 8, which holds logical chunk
-    // (L % 8) ^ swz(row).
-    const uint8_t *ga[C::kALoads];
-    const uint8_t *gb[C::kBLoads];
-#pragma unroll
-    for (int t = 0; t < C::kALoads; ++t) {
-        const int r = 8 * (wave + C::kWaves * t) + (lane >> 3);
-        const int chunk = (lane & 7) ^ swz(r);
-        ga[t] = a + min(row0 + r, row_last) * K + chunk * 16;
-    }
-#pragma unroll
-    for (int t = 0; t < C::kBLoads; ++t) {
-        const int r = 8 * (wave + C::kWaves * t) + (lane >> 3);
-        const int chunk = (lane & 7) ^ swz(r);
-        gb[t] = w + min(n0 + r, n_last) * K + chunk * 16;
-    }
-    // Scales: waves 0 .. kSaLoads-1 copy 64 activation-scale rows each; the
-    // last wave copies the weight scales of the tile's 128-column blocks.
-    const float *gs;
-    if (wave < C::kSaLoads)
-        gs = sa + min(row0 + 64 * wave + lane, row_last) * G;
-    else
-        gs = sw + min((n0 >> 7) + lane, n_last >> 7) * G;
+    const uint32_t copy_voff =
+        (uint32_t)(((lane >> 3) * K) + (((lane & 7) ^ ((lane >> 3) & 7)) << 4));
+    const uint32_t rowstep = (uint32_t)(8 * C::kWaves * K);  // between copies t and t+1
+    const uint32_t wave_voff = (uint32_t)(8 * wave * K) + copy_voff;
+    // Activation scales land transposed in LDS: scale row m (within the
+    // tile) at float (m % 16) * (BM / 16) + m / 16, so a lane later reads the
+    // scales of its token (lane % 16) in all of its M tiles contiguously.
+    // The lane writing position q = 64 wave + lane loads row
+    // (q % (BM / 16)) * 16 + q / (BM / 16).
+    const int sa_q = 64 * wave + lane;
+    const uint32_t sa_voff =
+        (uint32_t)((((sa_q % (C::BM / 16)) * 16) + sa_q / (C::BM / 16)) * G * 4);
+    const uint32_t sw_voff = (uint32_t)(lane * G * 4);
+    // LDS destinations of this wave's copies in stage 0; stage 1 is
+    // sizeof(S) bytes further.
+    const uint32_t lds_a0 = lds_addr(&stages[0].a[1024 * wave]);
+    const uint32_t lds_b0 = lds_addr(&stages[0].b[1024 * wave]);
+    const uint32_t lds_sa0 = lds_addr(&stages[0].sa[64 * (wave < C::kSaLoads ? wave : 0)]);
+    const uint32_t lds_sw0 = lds_addr(&stages[0].sw[0]);
 
     auto issue = [&](int kb, int st) {
-        const int64_t koff = (int64_t)kb * 128;
+        const uint32_t soff = (uint32_t)kb * 128u;
+        const uint32_t so = (uint32_t)(st * sizeof(S));
 #pragma unroll
         for (int t = 0; t < C::kALoads; ++t)
-            load_lds16(ga[t] + koff, &sm.a[st][1024 * (wave + C::kWaves * t)]);
+            copy16(op.a, wave_voff + t * rowstep, soff, lds_a0 + so + 1024 * C::kWaves * t);
 #pragma unroll
         for (int t = 0; t < C::kBLoads; ++t)
-            load_lds16(gb[t] + koff, &sm.b[st][1024 * (wave + C::kWaves * t)]);
+            copy16(op.w, wave_voff + t * rowstep, soff, lds_b0 + so + 1024 * C::kWaves * t);
         if (wave < C::kSaLoads)
-            load_lds4(gs + kb, &sm.sa[st][64 * wave]);
+            copy4(op.sa, sa_voff, (uint32_t)kb * 4u, lds_sa0 + so);
         else if (wave == C::kWaves - 1)
-            load_lds4(gs + kb, &sm.sw[st][0]);
+            copy4(op.sw, sw_voff, (uint32_t)kb * 4u, lds_sw0 + so);
+    };
+
+    // LDS byte offsets of this lane's two 16-byte operand chunks inside a
+    // 16-row tile (the row's low 3 bits equal lr's).
+    const int frag0 = lr * 128 + (((2 * lk) ^ (lr & 7)) << 4);
+    const int frag1 = lr * 128 + (((2 * lk + 1) ^ (lr & 7)) << 4);
+    const int a_base = wm * C::WM * 128;
+    const int b_base = wn * C::WN * 128;
+
+    // The MFMA runs with the weight fragment as its A operand and the token
+    // fragment as its B operand, so it produces the transposed 16x16 tile
+    // D[n][m]: lane L holds outputs n = 4 (L / 16) + e (e < 4), m = L % 16.
+    // The activation scale is then one value per lane per M tile and the
+    // weight scale one value per wave.
+    auto compute = [&](const S &st) {
+        const uint8_t *la = st.a + a_base;
+        const uint8_t *lb = st.b + b_base;
+        v8i wfr[C::kTN];
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j) {
+            const uint4 lo = *reinterpret_cast<const uint4 *>(lb + j * 2048 + frag0);
+            const uint4 hi = *reinterpret_cast<const uint4 *>(lb + j * 2048 + frag1);
+            wfr[j] = make_v8i(lo, hi);
+        }
+        const float swv = st.sw[sw_first_block_of_wave];
+        float sc[C::kTM];
+        const float *sa_lane = &st.sa[lr * (C::BM / 16) + wm * C::kTM];
+#pragma unroll
+        for (int i = 0; i < C::kTM; i += 4) {
+            const float4 s4 = *reinterpret_cast<const float4 *>(sa_lane + i);
+            sc[i] = s4.x * swv;
+            sc[i + 1] = s4.y * swv;
+            sc[i + 2] = s4.z * swv;
+            sc[i + 3] = s4.w * swv;
+        }
+#pragma unroll
+        for (int i = 0; i < C::kTM; ++i) {
+            const uint4 lo = *reinterpret_cast<const uint4 *>(la + i * 2048 + frag0);
+            const uint4 hi = *reinterpret_cast<const uint4 *>(la + i * 2048 + frag1);
+            const v8i af = make_v8i(lo, hi);
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j) {
+                const v4f p = mfma_e4m3(wfr[j], af);
+                acc[i][j][0] = __builtin_fmaf(p[0], sc[i], acc[i][j][0]);
+                acc[i][j][1] = __builtin_fmaf(p[1], sc[i], acc[i][j][1]);
+                acc[i][j][2] = __builtin_fmaf(p[2], sc[i], acc[i][j][2]);
+                acc[i][j][3] = __builtin_fmaf(p[3], sc[i], acc[i][j][3]);
+            }
+        }
     };
 
     issue(kb0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    const int sw_slot = (int)(((n0 + wn * C::WN) >> 7) - (n0 >> 7));
     for (int kb = kb0; kb < kb1; ++kb) {
         const int st = (kb - kb0) & 1;
         if (kb + 1 < kb1) issue(kb + 1, st ^ 1);
-
-        const uint8_t *la = sm.a[st];
-        const uint8_t *lb = sm.b[st];
-        v8i bfr[C::kTN];
-#pragma unroll
-        for (int j = 0; j < C::kTN; ++j) {
-            const int r = wn * C::WN + j * 16 + lr;
-            const uint4 lo = *reinterpret_cast<const uint4 *>(lb + lds_off(r, 2 * lk));
-            const uint4 hi = *reinterpret_cast<const uint4 *>(lb + lds_off(r, 2 * lk + 1));
-            bfr[j] = make_v8i(lo, hi);
-        }
-        const float swv = sm.sw[st][sw_slot];
-#pragma unroll
-        for (int i = 0; i < C::kTM; ++i) {
-            const int r = wm * C::WM + i * 16 + lr;
-            const uint4 lo = *reinterpret_cast<const uint4 *>(la + lds_off(r, 2 * lk));
-            const uint4 hi = *reinterpret_cast<const uint4 *>(la + lds_off(r, 2 * lk + 1));
-            const v8i af = make_v8i(lo, hi);
-            const float4 s4 =
-                *reinterpret_cast<const float4 *>(&sm.sa[st][wm * C::WM + i * 16 + 4 * lk]);
-            const float sc0 = s4.x * swv, sc1 = s4.y * swv, sc2 = s4.z * swv, sc3 = s4.w * swv;
-#pragma unroll
-            for (int j = 0; j < C::kTN; ++j) {
-                const v4f p = mfma_e4m3(af, bfr[j]);
-                acc[i][j][0] = __builtin_fmaf(p[0], sc0, acc[i][j][0]);
-                acc[i][j][1] = __builtin_fmaf(p[1], sc1, acc[i][j][1]);
-                acc[i][j][2] = __builtin_fmaf(p[2], sc2, acc[i][j][2]);
-                acc[i][j][3] = __builtin_fmaf(p[3], sc3, acc[i][j][3]);
-            }
-        }
+        compute(stages[st]);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     }
 }
 
 // Writes the accumulators of one tile: rows [row0, row_end) and columns
-// [n0, N) are stored; the MFMA output layout puts rows 4*(lane/16) + e and
-// column lane % 16 of each 16x16 tile in a lane.
+// [n0, N) are stored.  acc[i][j] holds, for token m = 16 i + lane % 16 of the
+// wave's rows, the four consecutive outputs n = 16 j + 4 (lane / 16) + e of
+// the wave's columns: one 8-byte (bf16) or 16-byte (fp32) store each.
 template <class C, int OUT>
 __device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], void *c, int64_t ldc,
                                            int64_t row0, int64_t row_end, int64_t n0,
@@ -250,22 +325,25 @@ __device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], voi
     const int wm = wave / C::kWavesN;
     const int wn = wave % C::kWavesN;
 #pragma unroll
-    for (int i = 0; i < C::kTM; ++i)
+    for (int i = 0; i < C::kTM; ++i) {
+        const int64_t row = row0 + wm * C::WM + i * 16 + (lane & 15);
+        if (row >= row_end) continue;
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) {
-            const int64_t col = n0 + wn * C::WN + j * 16 + (lane & 15);
-            if (col >= N) continue;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t row = row0 + wm * C::WM + i * 16 + 4 * (lane >> 4) + e;
-                if (row >= row_end) continue;
-                const float v = acc[i][j][e];
-                if (OUT == kOutBF16)
-                    static_cast<uint16_t *>(c)[row * ldc + col] = (uint16_t)f32_to_bf16_bits(v);
-                else
-                    static_cast<float *>(c)[row * ldc + col] = v;
+            const int64_t col = n0 + wn * C::WN + j * 16 + 4 * (lane >> 4);
+            if (col >= N) continue;  // N is a multiple of 128: all four or none
+            const v4f v = acc[i][j];
+            if (OUT == kOutBF16) {
+                uint2 o;
+                o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+                o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(c) + row * ldc + col) = o;
+            } else {
+                *reinterpret_cast<float4 *>(static_cast<float *>(c) + row * ldc + col) =
+                    make_float4(v[0], v[1], v[2], v[3]);
             }
         }
+    }
 }
 
 // Logical tile index of this workgroup after the XCD remap (gridDim.x is a
@@ -277,7 +355,7 @@ __device__ __forceinline__ int xcd_logical_tile() {
 
 template <class C, int OUT>
 __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
-    __shared__ Smem<C::BM, C::BN> sm;
+    __shared__ Stage<C::BM, C::BN> stages[2];
     const int logical = xcd_logical_tile();
     if (logical >= p.ntiles) return;
     const int per_split = p.tiles_m * p.tiles_n;
@@ -299,7 +377,11 @@ __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
     const int kb1 = min(kb0 + p.kb_per_split, p.G);
 
     v4f acc[C::kTM][C::kTN];
-    tile_mainloop<C>(p.a, p.sa, p.w, p.sw, row0, p.M - 1, n0, p.N - 1, p.K, p.G, kb0, kb1, sm, acc);
+    const TileOperands op =
+        tile_operands<C>(p.a, p.sa, p.w, p.sw, row0, p.M - row0, n0, p.N - n0, p.K, p.G);
+    const int wn = (threadIdx.x >> 6) % C::kWavesN;
+    const int sw_slot = (int)(((n0 + wn * C::WN) >> 7) - (n0 >> 7));
+    tile_mainloop<C>(op, p.K, p.G, kb0, kb1, sw_slot, stages, acc);
     if (OUT == kOutPartial)
         tile_store<C, kOutF32>(acc, p.partial + (int64_t)ks * p.M * p.N, p.N, row0, p.M, n0, p.N);
     else
@@ -337,7 +419,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 // sized for the worst case (ceil(T/BM) + E) * tiles_n, surplus tiles exit.
 template <class C, int OUT>
 __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p) {
-    __shared__ Smem<C::BM, C::BN> sm;
+    __shared__ Stage<C::BM, C::BN> stages[2];
     __shared__ int64_t info[4];
     const int logical = xcd_logical_tile();
     if (threadIdx.x == 0) {
@@ -373,7 +455,11 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p)
     const uint8_t *w = p.w + e * p.N * p.K;
     const float *sw = p.sw + e * (int64_t)p.NB * p.G;
     v4f acc[C::kTM][C::kTN];
-    tile_mainloop<C>(p.a, p.sa, w, sw, row0, row_end - 1, n0, p.N - 1, p.K, p.G, 0, p.G, sm, acc);
+    const TileOperands op =
+        tile_operands<C>(p.a, p.sa, w, sw, row0, row_end - row0, n0, p.N - n0, p.K, p.G);
+    const int wn = (threadIdx.x >> 6) % C::kWavesN;
+    const int sw_slot = (int)(((n0 + wn * C::WN) >> 7) - (n0 >> 7));
+    tile_mainloop<C>(op, p.K, p.G, 0, p.G, sw_slot, stages, acc);
     tile_store<C, OUT>(acc, p.c, p.N, row0, row_end, n0, p.N);
 }
 
