@@ -74,6 +74,36 @@ struct QuotientCtx {
     }
 };
 
+// fl32(amax / 448) for amax >= 2^-60 by division by a constant: with
+// R = fl32(1/448), q0 = amax R is within an ulp, the residual amax - 448 q0
+// is exact by FMA, and q0 + residual R rounds to the correctly rounded
+// quotient (Markstein's method; equal to the IEEE divide for every bf16
+// amax in that range).
+__device__ __forceinline__ float scale_fast(float amax) {
+    constexpr float R = 1.0f / kE4M3Max;
+    const float q0 = amax * R;
+    const float e = __builtin_fmaf(-q0, kE4M3Max, amax);
+    return __builtin_fmaf(e, R, q0);
+}
+
+// Quotient of the fast path (amax >= 2^-60, see QuotientCtx), clamped.
+__device__ __forceinline__ float quot_fast(float x, float s, float r) {
+    const float a = fabsf(x);
+    const float q0 = a * r;
+    const float e = __builtin_fmaf(-q0, s, a);
+    const float y = __builtin_copysignf(__builtin_fmaf(e, r, q0), x);
+    return __builtin_amdgcn_fmed3f(y, -kE4M3Max, kE4M3Max);
+}
+
+// Max over the 8 lanes of one half DPP row (two quad permutations, then the
+// half-row mirror).
+__device__ __forceinline__ float row8_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
+    return v;
+}
+
 // Two fp32 -> two OCP E4M3 bytes (gfx950 v_cvt_pk_fp8_f32, round to nearest
 // even) packed into the low (kHi = false) or high 16 bits of `old`.
 template <bool kHi>

@@ -23,45 +23,85 @@ namespace fp8blk {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kQuantThreads = 256;
-constexpr int kQuantUnroll = 4;  // chunks of 8 elements per thread per block
 
-// Fast path: K % 128 == 0, x 16-byte and q 8-byte aligned.  The tensor is a
-// flat sequence of 128-element groups; chunk c (8 elements) belongs to group
-// c / 16 and its scale index is that group index (scales are [M][K/128]).
+// Fast path: K % 128 == 0, x and q 16-byte aligned.  The tensor is a flat
+// sequence of 128-element groups.  Eight lanes own one group, 16 elements
+// (32 bytes) each: unit c (16 elements) belongs to group c / 8, whose scale
+// index is that group index (scales are [M][K/128]).  A wave streams 2 KiB
+// of bf16 per unit step and stores 1 KiB of E4M3.  When every group of the
+// wave has amax >= 2^-60 (the normal case) a branch-free path runs: scale
+// by constant division, reciprocal by one IEEE divide per lane, and the
+// reciprocal + FMA quotient per element; otherwise the wave takes the
+// general per-group selection (all-zero, tiny or ordinary groups).
+constexpr int kFlatUnroll = 2;  // 16-element units per thread per block
+
 __global__ __launch_bounds__(kQuantThreads) void quant_act_flat_kernel(
-    const u32x4 *__restrict__ x, u32x2 *__restrict__ q, float *__restrict__ scales,
-    int64_t n_chunks) {
-    const int64_t base = (int64_t)blockIdx.x * (kQuantThreads * kQuantUnroll) + threadIdx.x;
-    uint4 v[kQuantUnroll];
+    const u32x4 *__restrict__ x, u32x4 *__restrict__ q, float *__restrict__ scales,
+    int64_t n_units) {
+    const int64_t base = (int64_t)blockIdx.x * (kQuantThreads * kFlatUnroll) + threadIdx.x;
+    u32x4 v[kFlatUnroll][2];
 #pragma unroll
-    for (int u = 0; u < kQuantUnroll; ++u) {
+    for (int u = 0; u < kFlatUnroll; ++u) {
         const int64_t c = base + (int64_t)u * kQuantThreads;
-        if (c < n_chunks) {
-            const u32x4 t = __builtin_nontemporal_load(x + c);
-            v[u] = make_uint4(t.x, t.y, t.z, t.w);
+        if (c < n_units) {
+            v[u][0] = __builtin_nontemporal_load(x + 2 * c);
+            v[u][1] = __builtin_nontemporal_load(x + 2 * c + 1);
         } else {
-            v[u] = make_uint4(0, 0, 0, 0);
+            v[u][0] = u32x4{0, 0, 0, 0};
+            v[u][1] = u32x4{0, 0, 0, 0};
         }
     }
 #pragma unroll
-    for (int u = 0; u < kQuantUnroll; ++u) {
+    for (int u = 0; u < kFlatUnroll; ++u) {
         const int64_t c = base + (int64_t)u * kQuantThreads;
-        float f[8];
-        unpack8(v[u], f);
-        // n_chunks is a multiple of 16 and rows start at multiples of 16, so
-        // a DPP row is entirely in or out of range; all lanes join the DPP.
-        const float amax = row16_max(absmax8(f));
-        const QuotientCtx qc(amax);
-        const uint2 out = quant8(f, qc);
-        if (c < n_chunks) {
-            u32x2 o;
-            o.x = out.x;
-            o.y = out.y;
+        const bool in = c < n_units;
+        float f[16];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const u32x4 t = v[u][h];
+            f[8 * h + 0] = bf16_lo(t.x); f[8 * h + 1] = bf16_hi(t.x);
+            f[8 * h + 2] = bf16_lo(t.y); f[8 * h + 3] = bf16_hi(t.y);
+            f[8 * h + 4] = bf16_lo(t.z); f[8 * h + 5] = bf16_hi(t.z);
+            f[8 * h + 6] = bf16_lo(t.w); f[8 * h + 7] = bf16_hi(t.w);
+        }
+        float m = fabsf(f[0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) m = fmaxf(m, fabsf(f[i]));
+        // n_units is a multiple of 8 and groups start at multiples of 8, so
+        // an 8-lane group is entirely in or out of range.
+        const float amax = row8_max(m);
+        float y[16];
+        float s;
+        if (__all(!in || amax >= 0x1p-60f)) {
+            s = scale_fast(amax);
+            const float r = 1.0f / s;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) y[i] = quot_fast(f[i], s, r);
+        } else {
+            const QuotientCtx qc(amax);
+            s = qc.s;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) y[i] = qc(f[i]);
+        }
+        u32x4 o;
+        uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+        w0 = cvt_pk_e4m3<false>(y[0], y[1], w0);
+        w0 = cvt_pk_e4m3<true>(y[2], y[3], w0);
+        w1 = cvt_pk_e4m3<false>(y[4], y[5], w1);
+        w1 = cvt_pk_e4m3<true>(y[6], y[7], w1);
+        w2 = cvt_pk_e4m3<false>(y[8], y[9], w2);
+        w2 = cvt_pk_e4m3<true>(y[10], y[11], w2);
+        w3 = cvt_pk_e4m3<false>(y[12], y[13], w3);
+        w3 = cvt_pk_e4m3<true>(y[14], y[15], w3);
+        o.x = w0;
+        o.y = w1;
+        o.z = w2;
+        o.w = w3;
+        if (in) {
             __builtin_nontemporal_store(o, q + c);
-            if ((threadIdx.x & 15) == 0) scales[c >> 4] = qc.s;
+            if ((threadIdx.x & 7) == 0) scales[c >> 3] = s;
         }
     }
 }
@@ -162,13 +202,13 @@ hipError_t launch_quant_act_1x128(const void *x, int64_t M, int64_t K, void *q, 
                                   hipStream_t stream) {
     const int64_t G = (K + kGroup - 1) / kGroup;
     const bool vec = (K % 8 == 0) && aligned(x, 16) && aligned(q, 8);
-    if (K % kGroup == 0 && vec) {
-        const int64_t n_chunks = M * K / 8;
-        const int64_t per_block = (int64_t)kQuantThreads * kQuantUnroll;
-        const int64_t blocks = (n_chunks + per_block - 1) / per_block;
+    if (K % kGroup == 0 && aligned(x, 16) && aligned(q, 16)) {
+        const int64_t n_units = M * K / 16;
+        const int64_t per_block = (int64_t)kQuantThreads * kFlatUnroll;
+        const int64_t blocks = (n_units + per_block - 1) / per_block;
         hipLaunchKernelGGL(quant_act_flat_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0,
-                           stream, static_cast<const u32x4 *>(x), static_cast<u32x2 *>(q), scales,
-                           n_chunks);
+                           stream, static_cast<const u32x4 *>(x), static_cast<u32x4 *>(q), scales,
+                           n_units);
     } else {
         const int64_t groups = M * G;
         const int64_t per_block = kQuantThreads / 16;
