@@ -70,8 +70,9 @@ struct GemmParams {
     int group_m;             // tile-order grouping height (in M tiles)
 };
 
-template <int BM_, int BN_, int WAVES_M, int WAVES_N>
+template <int BM_, int BN_, int WAVES_M, int WAVES_N, int STAGES>
 struct TileCfg {
+    static constexpr int kStages = STAGES;
     static constexpr int BM = BM_;
     static constexpr int BN = BN_;
     static constexpr int kWavesM = WAVES_M;
@@ -91,23 +92,37 @@ struct TileCfg {
     static_assert(BM % 64 == 0 && kSaLoads <= kWaves - 1, "scale loader");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns sit in one 128-block");
+    static_assert(STAGES >= 2, "pipeline");
+    static_assert(kTM % 4 == 0, "scale reads cover four M tiles");
+    // copy instructions each wave issues per K block (A, W, one scale copy)
+    static constexpr int kCopiesPerBlock = kALoads + kBLoads + 1;
+    static_assert((STAGES - 2) * kCopiesPerBlock <= 63, "vmcnt range");
 };
 
 // One LDS pipeline stage: the A (token) and W (weight) tiles of one K block
-// and its scales.
+// and its scales, padded to a multiple of 4 KiB so that every 16-row operand
+// tile starts 2 KiB-aligned (the bank layout below assumes it).
 template <int BM, int BN>
-struct __align__(16) Stage {
+struct StageData {
     uint8_t a[BM * 128];
     uint8_t b[BN * 128];
     float sa[BM];
     float sw[64];
 };
+template <int BM, int BN>
+struct __align__(4096) Stage : StageData<BM, BN> {
+    uint8_t pad[(4096 - sizeof(StageData<BM, BN>) % 4096) % 4096];
+};
 
-// 16-byte chunk j of LDS row r is stored at chunk j ^ (r & 7): the 8 rows
-// that one 8-lane group of an MFMA operand read touches land on 8 distinct
-// 16-byte bank groups, and a tile copy (8 lanes per 128-byte row) stays one
-// contiguous 128-byte row.
-__device__ __forceinline__ int lds_off(int r, int chunk) { return r * 128 + ((chunk ^ (r & 7)) << 4); }
+// LDS layout of an operand tile: rows of 128 bytes (one K block); 16-byte
+// chunk c of row r is stored at chunk c ^ key(r), key(r) = (r & 7) ^ ((r >> 3)
+// & 1).  With it, an MFMA operand read (16 lanes reading one chunk of 16
+// consecutive rows, four such groups) runs at the full 16 bytes per lane
+// per ds_read_b128 issue slot without bank conflicts on gfx950 (found by
+// measuring the LDS bank-conflict counters over candidate layouts; plain
+// r & 7 costs twice the cycles).  Tile copies still write whole 128-byte
+// rows.
+__device__ __forceinline__ int swz_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 __device__ __forceinline__ v8i make_v8i(const uint4 &lo, const uint4 &hi) {
     v8i v;
@@ -186,16 +201,23 @@ __device__ __forceinline__ TileOperands tile_operands(const uint8_t *a, const fl
 // Runs K blocks [kb0, kb1) of one BM x BN tile and leaves the FP32
 // accumulators in acc.
 //
-// Pipeline: two LDS stages.  At the top of an iteration every wave issues
-// its direct global->LDS copies of the next K block into the other stage,
-// then runs the current block from LDS: the weight fragments, then one
-// token fragment per 16-row tile, each followed by its MFMAs and promotion
-// FMAs.  Then the wave waits for its copies and meets the others at one
-// barrier, so the copies overlap the whole MFMA phase.
+// Pipeline over kStages LDS stages.  With two stages, an iteration issues the
+// direct global->LDS copies of the next K block into the other stage, runs
+// the current block from LDS (the weight fragments, then one token fragment
+// per 16-row tile, each followed by its MFMAs and promotion FMAs), then waits
+// for its copies and meets the other waves at one barrier, so the copies
+// overlap the whole MFMA phase.  With S >= 3 stages the copies run
+// D = S - 2 blocks ahead: an iteration issues block kb + D into the stage
+// last read in iteration kb - 2 (every wave has passed the barrier of
+// iteration kb - 1 since), waits until only the D newer blocks' copies are
+// outstanding, meets the others at a barrier and computes block kb.  Every
+// wave issues exactly kCopiesPerBlock copies per block (waves without
+// activation scales to fetch copy the weight scales), so the wait count is
+// uniform.
 //
 // Copy t of wave v fills LDS rows [8 (v + kWaves t), +8): lane L writes
-// physical chunk L % 8 of row L / 8, i.e. logical chunk (L % 8) ^ ((L / 8) & 7)
-// of that row.
+// physical chunk L % 8 of row L / 8 of that block, i.e. the row's logical
+// chunk (L % 8) ^ key(row).
 template <class C>
 __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K, int G, int kb0,
                                               int kb1, int sw_first_block_of_wave,
@@ -215,18 +237,22 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const uint32_t copy_voff =
-        (uint32_t)(((lane >> 3) * K) + (((lane & 7) ^ ((lane >> 3) & 7)) << 4));
+    // copy lane L fills physical chunk L % 8 of tile row 8 b + L / 8 (b = wave
+    // + kWaves t, of the same parity as wave since kWaves is even), which
+    // holds logical chunk (L % 8) ^ key(row)
+    const uint32_t copy_voff = (uint32_t)(((lane >> 3) * K) +
+                                          (((lane & 7) ^ ((lane >> 3) & 7) ^ (wave & 1)) << 4));
     const uint32_t rowstep = (uint32_t)(8 * C::kWaves * K);  // between copies t and t+1
     const uint32_t wave_voff = (uint32_t)(8 * wave * K) + copy_voff;
-    // Activation scales land transposed in LDS: scale row m (within the
-    // tile) at float (m % 16) * (BM / 16) + m / 16, so a lane later reads the
-    // scales of its token (lane % 16) in all of its M tiles contiguously.
-    // The lane writing position q = 64 wave + lane loads row
-    // (q % (BM / 16)) * 16 + q / (BM / 16).
-    const int sa_q = 64 * wave + lane;
+    // Activation scales of the tile's rows go to LDS grouped by 4 M tiles:
+    // row m = 16 (4 q + e) + r sits at float 4 (16 q + r) + e, so a lane reads
+    // the scales of its token r = lane % 16 in four of its M tiles with one
+    // 16-byte read, and the 16 lanes of a read hit 16 distinct 16-byte bank
+    // groups.  The lane writing float P = 64 wave + lane loads row
+    // 16 (4 (P / 64) + P % 4) + (P / 4) % 16.
+    const int sa_p = 64 * wave + lane;
     const uint32_t sa_voff =
-        (uint32_t)((((sa_q % (C::BM / 16)) * 16) + sa_q / (C::BM / 16)) * G * 4);
+        (uint32_t)((16 * (4 * (sa_p >> 6) + (sa_p & 3)) + ((sa_p >> 2) & 15)) * G * 4);
     const uint32_t sw_voff = (uint32_t)(lane * G * 4);
     // LDS destinations of this wave's copies in stage 0; stage 1 is
     // sizeof(S) bytes further.
@@ -246,14 +272,14 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             copy16(op.w, wave_voff + t * rowstep, soff, lds_b0 + so + 1024 * C::kWaves * t);
         if (wave < C::kSaLoads)
             copy4(op.sa, sa_voff, (uint32_t)kb * 4u, lds_sa0 + so);
-        else if (wave == C::kWaves - 1)
+        else
             copy4(op.sw, sw_voff, (uint32_t)kb * 4u, lds_sw0 + so);
     };
 
     // LDS byte offsets of this lane's two 16-byte operand chunks inside a
-    // 16-row tile (the row's low 3 bits equal lr's).
-    const int frag0 = lr * 128 + (((2 * lk) ^ (lr & 7)) << 4);
-    const int frag1 = lr * 128 + (((2 * lk + 1) ^ (lr & 7)) << 4);
+    // 16-row tile (row lr of the tile; tiles start at multiples of 16 rows).
+    const int frag0 = lr * 128 + (((2 * lk) ^ swz_key(lr)) << 4);
+    const int frag1 = lr * 128 + (((2 * lk + 1) ^ swz_key(lr)) << 4);
     const int a_base = wm * C::WM * 128;
     const int b_base = wn * C::WN * 128;
 
@@ -274,10 +300,10 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         }
         const float swv = st.sw[sw_first_block_of_wave];
         float sc[C::kTM];
-        const float *sa_lane = &st.sa[lr * (C::BM / 16) + wm * C::kTM];
+        const float *sa_lane = &st.sa[4 * ((wm * C::kTM / 4) * 16 + lr)];
 #pragma unroll
         for (int i = 0; i < C::kTM; i += 4) {
-            const float4 s4 = *reinterpret_cast<const float4 *>(sa_lane + i);
+            const float4 s4 = *reinterpret_cast<const float4 *>(sa_lane + 16 * i);
             sc[i] = s4.x * swv;
             sc[i + 1] = s4.y * swv;
             sc[i + 2] = s4.z * swv;
@@ -299,16 +325,32 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         }
     };
 
-    issue(kb0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    for (int kb = kb0; kb < kb1; ++kb) {
-        const int st = (kb - kb0) & 1;
-        if (kb + 1 < kb1) issue(kb + 1, st ^ 1);
-        compute(stages[st]);
+    if constexpr (C::kStages == 2) {
+        issue(kb0, 0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        for (int kb = kb0; kb < kb1; ++kb) {
+            const int st = (kb - kb0) & 1;
+            if (kb + 1 < kb1) issue(kb + 1, st ^ 1);
+            compute(stages[st]);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
+    } else {
+        constexpr int D = C::kStages - 2;
+        for (int d = 0; d < D; ++d)
+            if (kb0 + d < kb1) issue(kb0 + d, d);
+        for (int kb = kb0; kb < kb1; ++kb) {
+            const int i = kb - kb0;
+            if (kb + D < kb1) {
+                issue(kb + D, (i + D) % C::kStages);
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D * C::kCopiesPerBlock) : "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            __syncthreads();
+            compute(stages[i % C::kStages]);
+        }
     }
 }
 
@@ -355,7 +397,7 @@ __device__ __forceinline__ int xcd_logical_tile() {
 
 template <class C, int OUT>
 __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
-    __shared__ Stage<C::BM, C::BN> stages[2];
+    __shared__ Stage<C::BM, C::BN> stages[C::kStages];
     const int logical = xcd_logical_tile();
     if (logical >= p.ntiles) return;
     const int per_split = p.tiles_m * p.tiles_n;
@@ -419,7 +461,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 // sized for the worst case (ceil(T/BM) + E) * tiles_n, surplus tiles exit.
 template <class C, int OUT>
 __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p) {
-    __shared__ Stage<C::BM, C::BN> stages[2];
+    __shared__ Stage<C::BM, C::BN> stages[C::kStages];
     __shared__ int64_t info[4];
     const int logical = xcd_logical_tile();
     if (threadIdx.x == 0) {
@@ -465,11 +507,12 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p)
 
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
-// Tile shapes: 256 x 256 on 8 waves (wave tile 128 x 64) for GEMMs that fill
-// the GPU; 128 x 128 on 4 waves (wave tile 64 x 64) for small ones, with
-// split-K when even those tiles cannot occupy the 256 CUs.
-using BigTile = TileCfg<256, 256, 2, 4>;
-using SmallTile = TileCfg<128, 128, 2, 2>;
+// Tile shapes: 256 x 256 on 8 waves (wave tile 128 x 64, two LDS stages)
+// for GEMMs that fill the GPU; 128 x 128 on 4 waves (wave tile 64 x 64,
+// four stages: copies two K blocks ahead) for small ones, with split-K when
+// even those tiles cannot occupy the 256 CUs.
+using BigTile = TileCfg<256, 256, 2, 4, 2>;
+using SmallTile = TileCfg<128, 128, 2, 2, 4>;
 constexpr int kCUs = 256;
 
 struct Plan {
