@@ -13,9 +13,10 @@ Printed as one JSON line, with:
     region, against the dense FP8 MFMA peak; traffic = HBM bytes per launch
     from committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by the
     copy-kernel calibration, or null if the kernel source changed since;
-  * parts: each kernel on its own workload (act quantizer GB/s vs HBM with
-    the caches flushed before every launch, dense / decode / grouped GEMM
-    TFLOP/s vs MFMA and GB/s vs HBM);
+  * parts: each kernel on its own workload with the caches flushed before
+    every launch (act quantizer GB/s vs HBM, beside a plain device copy of
+    the same byte count; dense / decode / grouped GEMM TFLOP/s vs MFMA and
+    GB/s vs HBM);
   * cpu_baseline: the CPU oracle timed on this host on a bounded sample of
     the same step (first 256 tokens).
 
@@ -103,14 +104,17 @@ def to_dev_bf16(torch, bits):
 
 
 def measure_parts(torch, F, I, X, qa, sa, qw, sw, C, iters=20):
-    """Each kernel on its own workload; caches flushed before every launch."""
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+    """Each kernel on its own workload.  Before every launch a 512 MB buffer
+    is read (twice the 256 MB Infinity Cache), so operands come from HBM; a
+    read leaves no dirty lines whose write-back would land in the timed
+    launch."""
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     parts = {}
 
     def timed(fn, n):
         t = Timer(torch, n)
         for _ in range(n):
-            flush.fill_(1.0)
+            flush.sum()
             t.start()
             fn()
             t.stop()
@@ -124,6 +128,16 @@ def measure_parts(torch, F, I, X, qa, sa, qw, sw, C, iters=20):
         "us": ms * 1e3, "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
         "bytes": b}
 
+    # context: a plain device copy moving the quantizer's byte count
+    # (44.5 MB read + 44.5 MB written), timed the same way
+    src = torch.empty(quant_bytes(M, K) // 2, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src), iters)
+    parts["copy_reference_same_bytes"] = {
+        "us": ms * 1e3, "GB/s": 2 * src.numel() / ms / 1e6,
+        "frac_hbm": 2 * src.numel() / ms / 1e6 / PEAK_HBM_GBS}
+    del src, dst
+
     # dense GEMM alone, 4096 x 7168 x 7168
     ms = timed(lambda: F.fp8_block_gemm(qa, sa, qw, sw, out_dtype="bf16", c=C), iters)
     fl = 2 * M * N * K
@@ -131,7 +145,6 @@ def measure_parts(torch, F, I, X, qa, sa, qw, sw, C, iters=20):
         "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
 
     # decode GEMM, 256 x 2048 x 7168 (split-K with workspace)
-    import numpy as np
     gd = I.config_decode(seed=0)
     xa = to_dev_bf16(torch, gd.a_bf16)
     xw = to_dev_bf16(torch, gd.w_bf16)

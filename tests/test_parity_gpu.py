@@ -162,6 +162,20 @@ def test_gemm_dense_workload_sampled_rows():
     assert rf <= 4e-3
 
 
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_big_tiles_ragged_edges(out):
+    # Enough 256x256 tiles to take the large-tile path, with a partial last
+    # M tile (4000 = 15*256 + 160) and a partial last N tile (7040 = 27*256 +
+    # 128): compared on rows from every M tile, including the last ones.
+    M, N, K = 4000, 7040, 384
+    g = I.gemm_inputs(M, N, K, seed=77, outlier_frac=0.01, outlier_mult=20.0)
+    qa, sa, qw, sw = quantize(g)
+    c = run_gemm(qa, sa, qw, sw, out)
+    rows = np.unique(np.concatenate([np.arange(0, M, 97), [255, 256, 3839, 3840, 3999]]))
+    R = oracle.block_gemm(qa, sa, qw, sw, rows)
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, out, f"big tiles ragged {out}")
+
+
 def test_gemm_power_of_two_metamorphic_and_deterministic():
     # Scaling the activation scales by 2^j scales an FP32 result by exactly
     # 2^j; two runs of the same call are bitwise identical.
