@@ -15,13 +15,14 @@
 // already lands in the register file the FMAs read.
 //
 // Structure of one workgroup tile (BM x BN, K stepped 128 at a time):
-//   - A (BM x 128 bytes) and W (BN x 128 bytes) tiles plus the tile's
-//     activation scales for the K block are staged in LDS, double buffered:
-//     the next block's global loads are in flight while the MFMAs of the
-//     current one run; one barrier per K block.
+//   - A (BM x 128 bytes) and W (BN x 128 bytes) tiles plus the weight
+//     scales of the K block are staged in LDS by direct global->LDS copies:
+//     the next block's copies are in flight while the MFMAs of the current
+//     one run; one barrier per K block.  The tile's activation scales are
+//     fetched eight K blocks at a time into a separate double buffer.
 //   - LDS rows are 128 bytes; 16-byte chunk j of row r is stored at chunk
-//     j ^ (r & 7), so the MFMA operand reads (16 rows x 32 bytes per lane
-//     group) and the tile stores are bank-conflict free.
+//     j ^ key(r), so the MFMA operand reads (16 rows x 32 bytes per lane
+//     group) are bank-conflict free.
 //   - Waves are arranged (BM/WM) x (BN/WN); each owns a WM x WN sub-tile of
 //     (WM/16) x (WN/16) MFMA tiles and their FP32 accumulators.
 //   - blockIdx is remapped so that each XCD (hardware dispatches consecutive
@@ -86,32 +87,50 @@ struct TileCfg {
     // direct global->LDS loads: one wave instruction fills 8 rows x 128 B
     static constexpr int kALoads = BM / 8 / kWaves;
     static constexpr int kBLoads = BN / 8 / kWaves;
-    static constexpr int kSaLoads = BM / 64;  // one dword per lane per row
-    static constexpr int kSwSlots = 64;
+    // activation scales come in chunks of kScaleChunk K blocks: 16 bytes
+    // (4 blocks) per lane, so one wave instruction fetches 64 row-halves
+    static constexpr int kScaleChunk = 8;
+    static constexpr int kScaleLoads = 2 * BM / 64 / kWaves;
     static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "loader");
-    static_assert(BM % 64 == 0 && kSaLoads <= kWaves - 1, "scale loader");
+    static_assert(kScaleLoads >= 1 && 2 * BM == 64 * kWaves * kScaleLoads, "scale loader");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns sit in one 128-block");
     static_assert(STAGES >= 2, "pipeline");
-    static_assert(kTM % 4 == 0, "scale reads cover four M tiles");
-    // copy instructions each wave issues per K block (A, W, one scale copy)
+    // a scale chunk buffer is reloaded kScaleChunk blocks after its last use
+    // was issued; with copies D = STAGES - 2 blocks ahead that use has ended
+    // on every wave once D <= kScaleChunk - 1
+    static_assert(STAGES - 2 <= kScaleChunk - 1, "scale chunk double buffer");
+    // copy instructions each wave issues per K block (A, W, weight scales);
+    // a scale chunk adds kScaleLoads more every kScaleChunk blocks
     static constexpr int kCopiesPerBlock = kALoads + kBLoads + 1;
     static_assert((STAGES - 2) * kCopiesPerBlock <= 63, "vmcnt range");
 };
 
 // One LDS pipeline stage: the A (token) and W (weight) tiles of one K block
-// and its scales, padded to a multiple of 4 KiB so that every 16-row operand
-// tile starts 2 KiB-aligned (the bank layout below assumes it).
+// and the weight scales of the tile's 128-column blocks, padded to a multiple
+// of 4 KiB so that every 16-row operand tile starts 2 KiB-aligned (the bank
+// layout below assumes it).
 template <int BM, int BN>
 struct StageData {
     uint8_t a[BM * 128];
     uint8_t b[BN * 128];
-    float sa[BM];
     float sw[64];
 };
 template <int BM, int BN>
 struct __align__(4096) Stage : StageData<BM, BN> {
     uint8_t pad[(4096 - sizeof(StageData<BM, BN>) % 4096) % 4096];
+};
+
+// Activation scales of the tile's BM rows for kScaleChunk = 8 consecutive K
+// blocks, double buffered.  The scales are stored [M][K/128] in memory, so a
+// row's scales for one K block each sit in a different cache line; fetching
+// eight blocks per row at once (two 16-byte pieces) makes one L2 request
+// serve eight blocks instead of one.  Piece h of row r of buffer b holds
+// blocks 8 c + 4 h .. + 3 at float4 index (2 b + h) BM + r: the 16 lanes that
+// read one M tile's rows hit 16 distinct 16-byte bank groups.
+template <int BM>
+struct ScaleChunks {
+    float v[2][2][BM][4];
 };
 
 // LDS layout of an operand tile: rows of 128 bytes (one K block); 16-byte
@@ -209,11 +228,12 @@ __device__ __forceinline__ TileOperands tile_operands(const uint8_t *a, const fl
 // overlap the whole MFMA phase.  With S >= 3 stages the copies run
 // D = S - 2 blocks ahead: an iteration issues block kb + D into the stage
 // last read in iteration kb - 2 (every wave has passed the barrier of
-// iteration kb - 1 since), waits until only the D newer blocks' copies are
-// outstanding, meets the others at a barrier and computes block kb.  Every
-// wave issues exactly kCopiesPerBlock copies per block (waves without
-// activation scales to fetch copy the weight scales), so the wait count is
-// uniform.
+// iteration kb - 1 since), waits until at most the copies of the D newer
+// blocks are outstanding, meets the others at a barrier and computes block
+// kb.  Every wave issues the same copies, so the wait count is uniform; the
+// activation-scale chunk of a block is issued before the block's operand
+// copies, so the wait also covers it (an extra chunk copy among the newer
+// ones only makes the wait stricter).
 //
 // Copy t of wave v fills LDS rows [8 (v + kWaves t), +8): lane L writes
 // physical chunk L % 8 of row L / 8 of that block, i.e. the row's logical
@@ -222,6 +242,7 @@ template <class C>
 __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K, int G, int kb0,
                                               int kb1, int sw_first_block_of_wave,
                                               Stage<C::BM, C::BN> *stages,
+                                              ScaleChunks<C::BM> *chunks,
                                               v4f (&acc)[C::kTM][C::kTN]) {
     using S = Stage<C::BM, C::BN>;
     const int tid = threadIdx.x;
@@ -244,24 +265,32 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
                                           (((lane & 7) ^ ((lane >> 3) & 7) ^ (wave & 1)) << 4));
     const uint32_t rowstep = (uint32_t)(8 * C::kWaves * K);  // between copies t and t+1
     const uint32_t wave_voff = (uint32_t)(8 * wave * K) + copy_voff;
-    // Activation scales of the tile's rows go to LDS grouped by 4 M tiles:
-    // row m = 16 (4 q + e) + r sits at float 4 (16 q + r) + e, so a lane reads
-    // the scales of its token r = lane % 16 in four of its M tiles with one
-    // 16-byte read, and the 16 lanes of a read hit 16 distinct 16-byte bank
-    // groups.  The lane writing float P = 64 wave + lane loads row
-    // 16 (4 (P / 64) + P % 4) + (P / 4) % 16.
-    const int sa_p = 64 * wave + lane;
-    const uint32_t sa_voff =
-        (uint32_t)((16 * (4 * (sa_p >> 6) + (sa_p & 3)) + ((sa_p >> 2) & 15)) * G * 4);
+    // Scale chunk copy t of wave v fills float4 slots q = 64 (v + kWaves t) + L
+    // of a chunk buffer: piece h = q / BM of row r = q % BM.
+    uint32_t sa_voff[C::kScaleLoads];
+#pragma unroll
+    for (int t = 0; t < C::kScaleLoads; ++t) {
+        const int q = 64 * (wave + C::kWaves * t) + lane;
+        sa_voff[t] = (uint32_t)((q % C::BM) * G * 4 + (q / C::BM) * 16);
+    }
     const uint32_t sw_voff = (uint32_t)(lane * G * 4);
-    // LDS destinations of this wave's copies in stage 0; stage 1 is
-    // sizeof(S) bytes further.
+    // LDS destinations of this wave's copies in stage 0 (stage s is s *
+    // sizeof(S) bytes further) and in scale chunk buffer 0.
     const uint32_t lds_a0 = lds_addr(&stages[0].a[1024 * wave]);
     const uint32_t lds_b0 = lds_addr(&stages[0].b[1024 * wave]);
-    const uint32_t lds_sa0 = lds_addr(&stages[0].sa[64 * (wave < C::kSaLoads ? wave : 0)]);
     const uint32_t lds_sw0 = lds_addr(&stages[0].sw[0]);
+    const uint32_t lds_sc0 =
+        lds_addr(reinterpret_cast<const uint8_t *>(&chunks->v[0][0][0][0]) + 1024 * wave);
 
     auto issue = [&](int kb, int st) {
+        if (kb == kb0 || (kb & (C::kScaleChunk - 1)) == 0) {
+            const int c = kb / C::kScaleChunk;
+            const uint32_t so = (uint32_t)((c & 1) * sizeof(chunks->v[0]));
+#pragma unroll
+            for (int t = 0; t < C::kScaleLoads; ++t)
+                copy16(op.sa, sa_voff[t], (uint32_t)c * (4u * C::kScaleChunk),
+                       lds_sc0 + so + 1024 * C::kWaves * t);
+        }
         const uint32_t soff = (uint32_t)kb * 128u;
         const uint32_t so = (uint32_t)(st * sizeof(S));
 #pragma unroll
@@ -270,10 +299,9 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 #pragma unroll
         for (int t = 0; t < C::kBLoads; ++t)
             copy16(op.w, wave_voff + t * rowstep, soff, lds_b0 + so + 1024 * C::kWaves * t);
-        if (wave < C::kSaLoads)
-            copy4(op.sa, sa_voff, (uint32_t)kb * 4u, lds_sa0 + so);
-        else
-            copy4(op.sw, sw_voff, (uint32_t)kb * 4u, lds_sw0 + so);
+        // every wave fetches the (one or two) weight scales of the block to
+        // the same LDS words; the duplicates carry identical values
+        copy4(op.sw, sw_voff, (uint32_t)kb * 4u, lds_sw0 + so);
     };
 
     // LDS byte offsets of this lane's two 16-byte operand chunks inside a
@@ -288,7 +316,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     // D[n][m]: lane L holds outputs n = 4 (L / 16) + e (e < 4), m = L % 16.
     // The activation scale is then one value per lane per M tile and the
     // weight scale one value per wave.
-    auto compute = [&](const S &st) {
+    auto compute = [&](const S &st, int kb) {
         const uint8_t *la = st.a + a_base;
         const uint8_t *lb = st.b + b_base;
         v8i wfr[C::kTN];
@@ -299,30 +327,42 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             wfr[j] = make_v8i(lo, hi);
         }
         const float swv = st.sw[sw_first_block_of_wave];
+        const float *sa_lane =
+            &chunks->v[(kb / C::kScaleChunk) & 1][(kb >> 2) & 1][wm * C::WM + lr][kb & 3];
         float sc[C::kTM];
-        const float *sa_lane = &st.sa[4 * ((wm * C::kTM / 4) * 16 + lr)];
 #pragma unroll
-        for (int i = 0; i < C::kTM; i += 4) {
-            const float4 s4 = *reinterpret_cast<const float4 *>(sa_lane + 16 * i);
-            sc[i] = s4.x * swv;
-            sc[i + 1] = s4.y * swv;
-            sc[i + 2] = s4.z * swv;
-            sc[i + 3] = s4.w * swv;
-        }
-#pragma unroll
-        for (int i = 0; i < C::kTM; ++i) {
+        for (int i = 0; i < C::kTM; ++i) sc[i] = sa_lane[64 * i] * swv;
+        auto afrag = [&](int i) {
             const uint4 lo = *reinterpret_cast<const uint4 *>(la + i * 2048 + frag0);
             const uint4 hi = *reinterpret_cast<const uint4 *>(la + i * 2048 + frag1);
-            const v8i af = make_v8i(lo, hi);
+            return make_v8i(lo, hi);
+        };
+        // The promotion of each MFMA result is issued after the next MFMA, so
+        // the VALU FMAs never wait on the MFMA that produced their operand, and
+        // the next A fragment is read from LDS one row of tiles ahead.
+        auto promote = [&](int i, int j, const v4f &p) {
+            acc[i][j][0] = __builtin_fmaf(p[0], sc[i], acc[i][j][0]);
+            acc[i][j][1] = __builtin_fmaf(p[1], sc[i], acc[i][j][1]);
+            acc[i][j][2] = __builtin_fmaf(p[2], sc[i], acc[i][j][2]);
+            acc[i][j][3] = __builtin_fmaf(p[3], sc[i], acc[i][j][3]);
+        };
+        v8i af = afrag(0);
+        v4f p_prev{};
+        int pi = -1, pj = 0;
+#pragma unroll
+        for (int i = 0; i < C::kTM; ++i) {
+            const v8i af_next = afrag(i + 1 < C::kTM ? i + 1 : i);
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j) {
                 const v4f p = mfma_e4m3(wfr[j], af);
-                acc[i][j][0] = __builtin_fmaf(p[0], sc[i], acc[i][j][0]);
-                acc[i][j][1] = __builtin_fmaf(p[1], sc[i], acc[i][j][1]);
-                acc[i][j][2] = __builtin_fmaf(p[2], sc[i], acc[i][j][2]);
-                acc[i][j][3] = __builtin_fmaf(p[3], sc[i], acc[i][j][3]);
+                if (pi >= 0) promote(pi, pj, p_prev);
+                p_prev = p;
+                pi = i;
+                pj = j;
             }
+            af = af_next;
         }
+        promote(pi, pj, p_prev);
     };
 
     if constexpr (C::kStages == 2) {
@@ -332,7 +372,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         for (int kb = kb0; kb < kb1; ++kb) {
             const int st = (kb - kb0) & 1;
             if (kb + 1 < kb1) issue(kb + 1, st ^ 1);
-            compute(stages[st]);
+            compute(stages[st], kb);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         }
@@ -349,7 +389,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
             __syncthreads();
-            compute(stages[i % C::kStages]);
+            compute(stages[i % C::kStages], kb);
         }
     }
 }
@@ -398,6 +438,7 @@ __device__ __forceinline__ int xcd_logical_tile() {
 template <class C, int OUT>
 __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
     __shared__ Stage<C::BM, C::BN> stages[C::kStages];
+    __shared__ ScaleChunks<C::BM> chunks;
     const int logical = xcd_logical_tile();
     if (logical >= p.ntiles) return;
     const int per_split = p.tiles_m * p.tiles_n;
@@ -423,7 +464,7 @@ __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
         tile_operands<C>(p.a, p.sa, p.w, p.sw, row0, p.M - row0, n0, p.N - n0, p.K, p.G);
     const int wn = (threadIdx.x >> 6) % C::kWavesN;
     const int sw_slot = (int)(((n0 + wn * C::WN) >> 7) - (n0 >> 7));
-    tile_mainloop<C>(op, p.K, p.G, kb0, kb1, sw_slot, stages, acc);
+    tile_mainloop<C>(op, p.K, p.G, kb0, kb1, sw_slot, stages, &chunks, acc);
     if (OUT == kOutPartial)
         tile_store<C, kOutF32>(acc, p.partial + (int64_t)ks * p.M * p.N, p.N, row0, p.M, n0, p.N);
     else
@@ -462,6 +503,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 template <class C, int OUT>
 __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p) {
     __shared__ Stage<C::BM, C::BN> stages[C::kStages];
+    __shared__ ScaleChunks<C::BM> chunks;
     __shared__ int64_t info[4];
     const int logical = xcd_logical_tile();
     if (threadIdx.x == 0) {
@@ -501,7 +543,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p)
         tile_operands<C>(p.a, p.sa, w, sw, row0, row_end - row0, n0, p.N - n0, p.K, p.G);
     const int wn = (threadIdx.x >> 6) % C::kWavesN;
     const int sw_slot = (int)(((n0 + wn * C::WN) >> 7) - (n0 >> 7));
-    tile_mainloop<C>(op, p.K, p.G, 0, p.G, sw_slot, stages, acc);
+    tile_mainloop<C>(op, p.K, p.G, 0, p.G, sw_slot, stages, &chunks, acc);
     tile_store<C, OUT>(acc, p.c, p.N, row0, row_end, n0, p.N);
 }
 
