@@ -90,9 +90,11 @@ struct TileCfg {
     // activation scales come in chunks of kScaleChunk K blocks: 16 bytes
     // (4 blocks) per lane, so one wave instruction fetches 64 row-halves
     static constexpr int kScaleChunk = 8;
-    static constexpr int kScaleLoads = 2 * BM / 64 / kWaves;
+    static constexpr int kScaleCopies = 2 * BM / 64;  // per chunk, over all waves
+    static constexpr int kScaleLoads = (kScaleCopies + kWaves - 1) / kWaves;  // per wave, at most
     static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "loader");
-    static_assert(kScaleLoads >= 1 && 2 * BM == 64 * kWaves * kScaleLoads, "scale loader");
+    static_assert(BM % 32 == 0, "scale loader");
+    static_assert(((BM + BN) * 128) % 4096 == 0, "stage size");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns sit in one 128-block");
     static_assert(STAGES >= 2, "pipeline");
@@ -106,19 +108,13 @@ struct TileCfg {
     static_assert((STAGES - 2) * kCopiesPerBlock <= 63, "vmcnt range");
 };
 
-// One LDS pipeline stage: the A (token) and W (weight) tiles of one K block
-// and the weight scales of the tile's 128-column blocks, padded to a multiple
-// of 4 KiB so that every 16-row operand tile starts 2 KiB-aligned (the bank
-// layout below assumes it).
+// One LDS pipeline stage: the A (token) and W (weight) tiles of one K block.
+// Every 16-row operand tile starts 2 KiB-aligned (the bank layout below
+// assumes it).
 template <int BM, int BN>
-struct StageData {
+struct __align__(4096) Stage {
     uint8_t a[BM * 128];
     uint8_t b[BN * 128];
-    float sw[64];
-};
-template <int BM, int BN>
-struct __align__(4096) Stage : StageData<BM, BN> {
-    uint8_t pad[(4096 - sizeof(StageData<BM, BN>) % 4096) % 4096];
 };
 
 // Activation scales of the tile's BM rows for kScaleChunk = 8 consecutive K
@@ -131,6 +127,16 @@ struct __align__(4096) Stage : StageData<BM, BN> {
 template <int BM>
 struct ScaleChunks {
     float v[2][2][BM][4];
+};
+
+// Everything a workgroup keeps in LDS: the operand stages, the activation
+// scale chunks and, per stage, the weight scales of the tile's (one or two)
+// 128-column blocks for that stage's K block.
+template <class C>
+struct TileLds {
+    Stage<C::BM, C::BN> stages[C::kStages];
+    ScaleChunks<C::BM> chunks;
+    float sw[C::kStages][64];
 };
 
 // LDS layout of an operand tile: rows of 128 bytes (one K block); 16-byte
@@ -241,8 +247,7 @@ __device__ __forceinline__ TileOperands tile_operands(const uint8_t *a, const fl
 template <class C>
 __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K, int G, int kb0,
                                               int kb1, int sw_first_block_of_wave,
-                                              Stage<C::BM, C::BN> *stages,
-                                              ScaleChunks<C::BM> *chunks,
+                                              TileLds<C> &L,
                                               v4f (&acc)[C::kTM][C::kTN]) {
     using S = Stage<C::BM, C::BN>;
     const int tid = threadIdx.x;
@@ -274,22 +279,24 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         sa_voff[t] = (uint32_t)((q % C::BM) * G * 4 + (q / C::BM) * 16);
     }
     const uint32_t sw_voff = (uint32_t)(lane * G * 4);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // for uniform branches
     // LDS destinations of this wave's copies in stage 0 (stage s is s *
     // sizeof(S) bytes further) and in scale chunk buffer 0.
-    const uint32_t lds_a0 = lds_addr(&stages[0].a[1024 * wave]);
-    const uint32_t lds_b0 = lds_addr(&stages[0].b[1024 * wave]);
-    const uint32_t lds_sw0 = lds_addr(&stages[0].sw[0]);
+    const uint32_t lds_a0 = lds_addr(&L.stages[0].a[1024 * wave]);
+    const uint32_t lds_b0 = lds_addr(&L.stages[0].b[1024 * wave]);
+    const uint32_t lds_sw0 = lds_addr(&L.sw[0][0]);
     const uint32_t lds_sc0 =
-        lds_addr(reinterpret_cast<const uint8_t *>(&chunks->v[0][0][0][0]) + 1024 * wave);
+        lds_addr(reinterpret_cast<const uint8_t *>(&L.chunks.v[0][0][0][0]) + 1024 * wave);
 
     auto issue = [&](int kb, int st) {
         if (kb == kb0 || (kb & (C::kScaleChunk - 1)) == 0) {
             const int c = kb / C::kScaleChunk;
-            const uint32_t so = (uint32_t)((c & 1) * sizeof(chunks->v[0]));
+            const uint32_t so = (uint32_t)((c & 1) * sizeof(L.chunks.v[0]));
 #pragma unroll
             for (int t = 0; t < C::kScaleLoads; ++t)
-                copy16(op.sa, sa_voff[t], (uint32_t)c * (4u * C::kScaleChunk),
-                       lds_sc0 + so + 1024 * C::kWaves * t);
+                if (wave_u + C::kWaves * t < C::kScaleCopies)
+                    copy16(op.sa, sa_voff[t], (uint32_t)c * (4u * C::kScaleChunk),
+                           lds_sc0 + so + 1024 * C::kWaves * t);
         }
         const uint32_t soff = (uint32_t)kb * 128u;
         const uint32_t so = (uint32_t)(st * sizeof(S));
@@ -301,7 +308,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             copy16(op.w, wave_voff + t * rowstep, soff, lds_b0 + so + 1024 * C::kWaves * t);
         // every wave fetches the (one or two) weight scales of the block to
         // the same LDS words; the duplicates carry identical values
-        copy4(op.sw, sw_voff, (uint32_t)kb * 4u, lds_sw0 + so);
+        copy4(op.sw, sw_voff, (uint32_t)kb * 4u, lds_sw0 + (uint32_t)st * sizeof(L.sw[0]));
     };
 
     // LDS byte offsets of this lane's two 16-byte operand chunks inside a
@@ -316,9 +323,9 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     // D[n][m]: lane L holds outputs n = 4 (L / 16) + e (e < 4), m = L % 16.
     // The activation scale is then one value per lane per M tile and the
     // weight scale one value per wave.
-    auto compute = [&](const S &st, int kb) {
-        const uint8_t *la = st.a + a_base;
-        const uint8_t *lb = st.b + b_base;
+    auto compute = [&](int s, int kb) {
+        const uint8_t *la = L.stages[s].a + a_base;
+        const uint8_t *lb = L.stages[s].b + b_base;
         v8i wfr[C::kTN];
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) {
@@ -326,9 +333,9 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             const uint4 hi = *reinterpret_cast<const uint4 *>(lb + j * 2048 + frag1);
             wfr[j] = make_v8i(lo, hi);
         }
-        const float swv = st.sw[sw_first_block_of_wave];
+        const float swv = L.sw[s][sw_first_block_of_wave];
         const float *sa_lane =
-            &chunks->v[(kb / C::kScaleChunk) & 1][(kb >> 2) & 1][wm * C::WM + lr][kb & 3];
+            &L.chunks.v[(kb / C::kScaleChunk) & 1][(kb >> 2) & 1][wm * C::WM + lr][kb & 3];
         float sc[C::kTM];
 #pragma unroll
         for (int i = 0; i < C::kTM; ++i) sc[i] = sa_lane[64 * i] * swv;
@@ -372,7 +379,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         for (int kb = kb0; kb < kb1; ++kb) {
             const int st = (kb - kb0) & 1;
             if (kb + 1 < kb1) issue(kb + 1, st ^ 1);
-            compute(stages[st], kb);
+            compute(st, kb);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         }
@@ -389,7 +396,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
             __syncthreads();
-            compute(stages[i % C::kStages], kb);
+            compute(i % C::kStages, kb);
         }
     }
 }
@@ -437,8 +444,7 @@ __device__ __forceinline__ int xcd_logical_tile() {
 
 template <class C, int OUT>
 __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
-    __shared__ Stage<C::BM, C::BN> stages[C::kStages];
-    __shared__ ScaleChunks<C::BM> chunks;
+    __shared__ TileLds<C> lds;
     const int logical = xcd_logical_tile();
     if (logical >= p.ntiles) return;
     const int per_split = p.tiles_m * p.tiles_n;
@@ -464,7 +470,7 @@ __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
         tile_operands<C>(p.a, p.sa, p.w, p.sw, row0, p.M - row0, n0, p.N - n0, p.K, p.G);
     const int wn = (threadIdx.x >> 6) % C::kWavesN;
     const int sw_slot = (int)(((n0 + wn * C::WN) >> 7) - (n0 >> 7));
-    tile_mainloop<C>(op, p.K, p.G, kb0, kb1, sw_slot, stages, &chunks, acc);
+    tile_mainloop<C>(op, p.K, p.G, kb0, kb1, sw_slot, lds, acc);
     if (OUT == kOutPartial)
         tile_store<C, kOutF32>(acc, p.partial + (int64_t)ks * p.M * p.N, p.N, row0, p.M, n0, p.N);
     else
@@ -498,32 +504,40 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 // expert, N tile by N tile, and the expert's M tiles are consecutive, so the
 // M tiles that share one W tile run next to each other on one XCD.  The
 // offsets live on the device: thread 0 walks them (clamped to [0, T]; a
-// decreasing range is empty) to find this tile's expert, and the grid is
-// sized for the worst case (ceil(T/BM) + E) * tiles_n, surplus tiles exit.
+// decreasing range is empty), counts the real tiles R, gives each XCD a
+// contiguous range of ceil(R / 8) of them (the grid is sized for the worst
+// case (ceil(T / BM) + E) * tiles_n, so sizing the ranges by the grid would
+// leave the last XCDs idle) and finds this tile's expert; surplus
+// workgroups exit.
 template <class C, int OUT>
 __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p) {
-    __shared__ Stage<C::BM, C::BN> stages[C::kStages];
-    __shared__ ScaleChunks<C::BM> chunks;
+    __shared__ TileLds<C> lds;
     __shared__ int64_t info[4];
-    const int logical = xcd_logical_tile();
     if (threadIdx.x == 0) {
-        int64_t rem = logical;
+        auto clamp_t = [&](int64_t v) { return v < 0 ? (int64_t)0 : (v > p.M ? p.M : v); };
+        auto m_tiles = [&](int e) {
+            const int64_t lo = clamp_t(p.offsets[e]), hi = clamp_t(p.offsets[e + 1]);
+            return hi > lo ? (hi - lo + C::BM - 1) / C::BM : (int64_t)0;
+        };
+        int64_t total = 0;
+        for (int e = 0; e < p.E; ++e) total += m_tiles(e) * p.tiles_n;
+        const int64_t per = (total + kNumXcd - 1) / kNumXcd;
+        const int64_t slot = blockIdx.x / kNumXcd;
+        int64_t rem = (blockIdx.x % kNumXcd) * per + slot;
         int64_t e_hit = -1, r0 = 0, r1 = 0, tn = 0;
-        for (int e = 0; e < p.E; ++e) {
-            int64_t lo = p.offsets[e], hi = p.offsets[e + 1];
-            lo = lo < 0 ? 0 : (lo > p.M ? p.M : lo);
-            hi = hi < 0 ? 0 : (hi > p.M ? p.M : hi);
-            const int64_t cnt = hi > lo ? hi - lo : 0;
-            const int64_t mt = (cnt + C::BM - 1) / C::BM;
-            const int64_t tiles = mt * p.tiles_n;
-            if (rem < tiles) {
-                e_hit = e;
-                tn = rem / mt;
-                r0 = lo + (rem - tn * mt) * C::BM;
-                r1 = hi;
-                break;
+        if (slot < per && rem < total) {
+            for (int e = 0; e < p.E; ++e) {
+                const int64_t mt = m_tiles(e);
+                const int64_t tiles = mt * p.tiles_n;
+                if (rem < tiles) {
+                    e_hit = e;
+                    tn = rem / mt;
+                    r0 = clamp_t(p.offsets[e]) + (rem - tn * mt) * C::BM;
+                    r1 = clamp_t(p.offsets[e + 1]);
+                    break;
+                }
+                rem -= tiles;
             }
-            rem -= tiles;
         }
         info[0] = e_hit;
         info[1] = r0;
@@ -543,7 +557,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p)
         tile_operands<C>(p.a, p.sa, w, sw, row0, row_end - row0, n0, p.N - n0, p.K, p.G);
     const int wn = (threadIdx.x >> 6) % C::kWavesN;
     const int sw_slot = (int)(((n0 + wn * C::WN) >> 7) - (n0 >> 7));
-    tile_mainloop<C>(op, p.K, p.G, 0, p.G, sw_slot, stages, &chunks, acc);
+    tile_mainloop<C>(op, p.K, p.G, 0, p.G, sw_slot, lds, acc);
     tile_store<C, OUT>(acc, p.c, p.N, row0, row_end, n0, p.N);
 }
 
@@ -552,9 +566,12 @@ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 // Tile shapes: 256 x 256 on 8 waves (wave tile 128 x 64, two LDS stages)
 // for GEMMs that fill the GPU; 128 x 128 on 4 waves (wave tile 64 x 64,
 // four stages: copies two K blocks ahead) for small ones, with split-K when
-// even those tiles cannot occupy the 256 CUs.
+// even those tiles cannot occupy the 256 CUs; 128 x 256 on 8 waves (wave
+// tile 64 x 64, three stages) for the grouped GEMM, whose experts' token
+// counts make 128-row granularity worth keeping.
 using BigTile = TileCfg<256, 256, 2, 4, 2>;
 using SmallTile = TileCfg<128, 128, 2, 2, 4>;
+using MidTile = TileCfg<128, 256, 2, 4, 3>;
 constexpr int kCUs = 256;
 
 struct Plan {
@@ -641,7 +658,7 @@ hipError_t launch_block_gemm(const void *a, const float *sa, const void *w, cons
 hipError_t launch_grouped_gemm(const void *a, const float *sa, const void *w, const float *sw,
                                const int32_t *offsets, int64_t E, int64_t T, void *c,
                                bool bf16_out, int64_t N, int64_t K, hipStream_t stream) {
-    using C = SmallTile;
+    using C = MidTile;
     GemmParams p{};
     p.a = static_cast<const uint8_t *>(a);
     p.sa = sa;
