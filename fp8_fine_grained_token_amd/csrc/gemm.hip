@@ -404,32 +404,75 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 // Writes the accumulators of one tile: rows [row0, row_end) and columns
 // [n0, N) are stored.  acc[i][j] holds, for token m = 16 i + lane % 16 of the
 // wave's rows, the four consecutive outputs n = 16 j + 4 (lane / 16) + e of
-// the wave's columns: one 8-byte (bf16) or 16-byte (fp32) store each.
+// the wave's columns.  Stored directly, one instruction would write 16 rows
+// x 32 bytes (bf16); instead the tile goes through the (now free) LDS stages
+// in row-major order and leaves in 16-byte pieces of whole rows, so that
+// every store instruction writes full 128-byte lines.  Rows that do not fit
+// in the stages at once (fp32 output of a 256 x 256 tile) go in passes of
+// whole wave rows.  Inside an LDS row, the 32-byte piece q of row r is kept
+// at piece q ^ (r % 16) (bounded by the row length), which spreads the 16
+// rows a wave writes at once over the banks.
 template <class C, int OUT>
-__device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], void *c, int64_t ldc,
-                                           int64_t row0, int64_t row_end, int64_t n0,
-                                           int64_t N) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+__device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], TileLds<C> &L,
+                                           void *c, int64_t ldc, int64_t row0, int64_t row_end,
+                                           int64_t n0, int64_t N) {
+    constexpr int kOB = OUT == kOutBF16 ? 2 : 4;  // bytes per output element
+    constexpr int kRB = C::BN * kOB;              // bytes per tile row
+    constexpr int kFit = (int)(sizeof(L.stages) / kRB) / C::WM * C::WM;
+    constexpr int kRowsPerPass = kFit < C::BM ? kFit : C::BM;
+    static_assert(kRowsPerPass >= C::WM && C::BM % kRowsPerPass == 0, "store passes");
+    constexpr int kPieces = kRB / 32;
+    constexpr int kSwz = (kPieces < 16 ? kPieces : 16) - 1;  // XOR mask on the 32-byte piece
+    static_assert((kPieces & (kPieces - 1)) == 0, "row length");
+    constexpr int kUnitsPerRow = kRB / 16;
+    constexpr int kUnits = kRowsPerPass * kUnitsPerRow;
+    static_assert(kUnits % C::kThreads == 0, "store loop");
+
+    uint8_t *buf = reinterpret_cast<uint8_t *>(&L.stages[0]);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int wm = wave / C::kWavesN;
     const int wn = wave % C::kWavesN;
+    const int wave_row0 = __builtin_amdgcn_readfirstlane(wm * C::WM);
 #pragma unroll
-    for (int i = 0; i < C::kTM; ++i) {
-        const int64_t row = row0 + wm * C::WM + i * 16 + (lane & 15);
-        if (row >= row_end) continue;
+    for (int pass = 0; pass < C::BM / kRowsPerPass; ++pass) {
+        const int r_lo = pass * kRowsPerPass;
+        __syncthreads();  // the stages (or the previous pass) are no longer read
+        if (wave_row0 >= r_lo && wave_row0 < r_lo + kRowsPerPass) {
 #pragma unroll
-        for (int j = 0; j < C::kTN; ++j) {
-            const int64_t col = n0 + wn * C::WN + j * 16 + 4 * (lane >> 4);
-            if (col >= N) continue;  // N is a multiple of 128: all four or none
-            const v4f v = acc[i][j];
-            if (OUT == kOutBF16) {
-                uint2 o;
-                o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-                o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(c) + row * ldc + col) = o;
-            } else {
-                *reinterpret_cast<float4 *>(static_cast<float *>(c) + row * ldc + col) =
-                    make_float4(v[0], v[1], v[2], v[3]);
+            for (int i = 0; i < C::kTM; ++i) {
+                const int r = wave_row0 - r_lo + 16 * i + (lane & 15);
+                const int swz = (r & kSwz) << 5;
+#pragma unroll
+                for (int j = 0; j < C::kTN; ++j) {
+                    const int cb = (wn * C::WN + 16 * j + 4 * (lane >> 4)) * kOB;
+                    uint8_t *dst = buf + r * kRB + (cb ^ swz);
+                    const v4f v = acc[i][j];
+                    if (OUT == kOutBF16) {
+                        uint2 o;
+                        o.x = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+                        o.y = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+                        *reinterpret_cast<uint2 *>(dst) = o;
+                    } else {
+                        *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int u = tid; u < kUnits; u += C::kThreads) {
+            const int r = u / kUnitsPerRow;
+            const int cb = (u % kUnitsPerRow) * 16;
+            const int64_t grow = row0 + r_lo + r;
+            const int64_t gcol = n0 + cb / kOB;
+            // N is a multiple of 128: a 16-byte piece is all in or all out
+            if (grow < row_end && gcol < N) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(buf + r * kRB +
+                                                                 (cb ^ ((r & kSwz) << 5)));
+                *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(c) + (grow * ldc + gcol) * kOB) =
+                    v;
             }
         }
     }
@@ -472,9 +515,10 @@ __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
     const int sw_slot = (int)(((n0 + wn * C::WN) >> 7) - (n0 >> 7));
     tile_mainloop<C>(op, p.K, p.G, kb0, kb1, sw_slot, lds, acc);
     if (OUT == kOutPartial)
-        tile_store<C, kOutF32>(acc, p.partial + (int64_t)ks * p.M * p.N, p.N, row0, p.M, n0, p.N);
+        tile_store<C, kOutF32>(acc, lds, p.partial + (int64_t)ks * p.M * p.N, p.N, row0, p.M, n0,
+                               p.N);
     else
-        tile_store<C, OUT>(acc, p.c, p.N, row0, p.M, n0, p.N);
+        tile_store<C, OUT>(acc, lds, p.c, p.N, row0, p.M, n0, p.N);
 }
 
 // Split-K reduction: C = sum over splits in fixed order 0..S-1, then the
@@ -558,7 +602,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p)
     const int wn = (threadIdx.x >> 6) % C::kWavesN;
     const int sw_slot = (int)(((n0 + wn * C::WN) >> 7) - (n0 >> 7));
     tile_mainloop<C>(op, p.K, p.G, 0, p.G, sw_slot, lds, acc);
-    tile_store<C, OUT>(acc, p.c, p.N, row0, row_end, n0, p.N);
+    tile_store<C, OUT>(acc, lds, p.c, p.N, row0, row_end, n0, p.N);
 }
 
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
