@@ -288,27 +288,40 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     const uint32_t lds_sc0 =
         lds_addr(reinterpret_cast<const uint8_t *>(&L.chunks.v[0][0][0][0]) + 1024 * wave);
 
-    auto issue = [&](int kb, int st) {
+    // Copy t of A fills tile rows [8 kWaves t, +8 kWaves); with two stages
+    // the copies of a block go in two halves: the rows of every wave's first
+    // kTM / 2 M tiles (with W and the scales), then the rest (see below).
+    auto a_copy_in_half = [&](int t, int half) {
+        return ((((8 * C::kWaves * t) % C::WM) < C::WM / 2) ? 0 : 1) == half;
+    };
+    auto issue_a = [&](const TileOperands &src, int kb, int st, int half) {
+        const uint32_t soff = (uint32_t)kb * 128u;
+        const uint32_t so = (uint32_t)(st * sizeof(S));
+#pragma unroll
+        for (int t = 0; t < C::kALoads; ++t)
+            if (half < 0 || a_copy_in_half(t, half))
+                copy16(src.a, wave_voff + t * rowstep, soff, lds_a0 + so + 1024 * C::kWaves * t);
+    };
+    // everything of block kb except (if a_half >= 0) the other half of A
+    auto issue = [&](const TileOperands &src, int kb, int st, int a_half) {
         if (kb == kb0 || (kb & (C::kScaleChunk - 1)) == 0) {
             const int c = kb / C::kScaleChunk;
             const uint32_t so = (uint32_t)((c & 1) * sizeof(L.chunks.v[0]));
 #pragma unroll
             for (int t = 0; t < C::kScaleLoads; ++t)
                 if (wave_u + C::kWaves * t < C::kScaleCopies)
-                    copy16(op.sa, sa_voff[t], (uint32_t)c * (4u * C::kScaleChunk),
+                    copy16(src.sa, sa_voff[t], (uint32_t)c * (4u * C::kScaleChunk),
                            lds_sc0 + so + 1024 * C::kWaves * t);
         }
+        issue_a(src, kb, st, a_half);
         const uint32_t soff = (uint32_t)kb * 128u;
         const uint32_t so = (uint32_t)(st * sizeof(S));
 #pragma unroll
-        for (int t = 0; t < C::kALoads; ++t)
-            copy16(op.a, wave_voff + t * rowstep, soff, lds_a0 + so + 1024 * C::kWaves * t);
-#pragma unroll
         for (int t = 0; t < C::kBLoads; ++t)
-            copy16(op.w, wave_voff + t * rowstep, soff, lds_b0 + so + 1024 * C::kWaves * t);
+            copy16(src.w, wave_voff + t * rowstep, soff, lds_b0 + so + 1024 * C::kWaves * t);
         // every wave fetches the (one or two) weight scales of the block to
         // the same LDS words; the duplicates carry identical values
-        copy4(op.sw, sw_voff, (uint32_t)kb * 4u, lds_sw0 + (uint32_t)st * sizeof(L.sw[0]));
+        copy4(src.sw, sw_voff, (uint32_t)kb * 4u, lds_sw0 + (uint32_t)st * sizeof(L.sw[0]));
     };
 
     // LDS byte offsets of this lane's two 16-byte operand chunks inside a
@@ -323,7 +336,8 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     // D[n][m]: lane L holds outputs n = 4 (L / 16) + e (e < 4), m = L % 16.
     // The activation scale is then one value per lane per M tile and the
     // weight scale one value per wave.
-    auto compute = [&](int s, int kb) {
+    auto compute = [&](int s, int kb, auto &&mid) {
+        constexpr bool kSplit = C::kStages == 2;
         const uint8_t *la = L.stages[s].a + a_base;
         const uint8_t *lb = L.stages[s].b + b_base;
         v8i wfr[C::kTN];
@@ -358,7 +372,14 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         int pi = -1, pj = 0;
 #pragma unroll
         for (int i = 0; i < C::kTM; ++i) {
-            const v8i af_next = afrag(i + 1 < C::kTM ? i + 1 : i);
+            if (kSplit && i == C::kTM / 2) {
+                mid();  // the second half of the block's A rows is in LDS from here
+                af = afrag(i);
+            }
+            // the next token fragment is read one row of tiles ahead, but not
+            // across the middle of a split block
+            const bool ahead = i + 1 < C::kTM && !(kSplit && i + 1 == C::kTM / 2);
+            const v8i af_next = afrag(ahead ? i + 1 : i);
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j) {
                 const v4f p = mfma_e4m3(wfr[j], af);
@@ -373,30 +394,61 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     };
 
     if constexpr (C::kStages == 2) {
-        issue(kb0, 0);
+        // Two stages, each block's copies in two halves so that the copy pipe
+        // never drains at a barrier.  Iteration kb: issue half 1 of block
+        // kb + 1 (W, scales, the A rows of the waves' first kTM / 2 M tiles)
+        // into the other stage (free: every wave finished block kb - 1 before
+        // the last barrier); compute those M tiles of block kb; wait for half
+        // 2 of block kb (issued in the middle of iteration kb - 1; only the
+        // kH1 newer copies may stay outstanding) and meet at a barrier; issue
+        // half 2 of block kb + 1; compute the other M tiles; wait for half 1
+        // of block kb + 1 (kH2 newer copies may stay outstanding) and meet at
+        // a barrier.  Each half gets one block of compute to land.
+        constexpr int kAHalf = C::kALoads / 2;
+        constexpr int kH1 = kAHalf + C::kBLoads + 1;  // per wave, without a scale chunk
+        constexpr int kH2 = C::kALoads - kAHalf;
+        static_assert((C::WM / 2) % (8 * C::kWaves) == 0 && C::kTM % 2 == 0, "split block");
+        // In the last iteration there is no next block: its copies are issued
+        // against empty buffers (every lane out of bounds: nothing is read,
+        // zeros land in the idle stage) so that the wait counts stay fixed
+        // and the loop body has no data-dependent branches.
+        TileOperands none = op;
+        none.a[2] = none.w[2] = none.sa[2] = none.sw[2] = 0;
+        issue(op, kb0, 0, -1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         for (int kb = kb0; kb < kb1; ++kb) {
             const int st = (kb - kb0) & 1;
-            if (kb + 1 < kb1) issue(kb + 1, st ^ 1);
-            compute(st, kb);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            const bool more = kb + 1 < kb1;
+            TileOperands next;
+            next.a = more ? op.a : none.a;
+            next.w = more ? op.w : none.w;
+            next.sa = more ? op.sa : none.sa;
+            next.sw = more ? op.sw : none.sw;
+            issue(next, kb + 1, st ^ 1, 0);
+            compute(st, kb, [&] {
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kH1) : "memory");
+                __syncthreads();
+                issue_a(next, kb + 1, st ^ 1, 1);
+            });
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kH2) : "memory");
             __syncthreads();
         }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
         constexpr int D = C::kStages - 2;
         for (int d = 0; d < D; ++d)
-            if (kb0 + d < kb1) issue(kb0 + d, d);
+            if (kb0 + d < kb1) issue(op, kb0 + d, d, -1);
         for (int kb = kb0; kb < kb1; ++kb) {
             const int i = kb - kb0;
             if (kb + D < kb1) {
-                issue(kb + D, (i + D) % C::kStages);
+                issue(op, kb + D, (i + D) % C::kStages, -1);
                 asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D * C::kCopiesPerBlock) : "memory");
             } else {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
             __syncthreads();
-            compute(i % C::kStages, kb);
+            compute(i % C::kStages, kb, [] {});
         }
     }
 }
