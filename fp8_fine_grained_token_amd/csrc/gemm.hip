@@ -98,14 +98,15 @@ struct TileCfg {
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns sit in one 128-block");
     static_assert(STAGES >= 2, "pipeline");
-    // a scale chunk buffer is reloaded kScaleChunk blocks after its last use
-    // was issued; with copies D = STAGES - 2 blocks ahead that use has ended
-    // on every wave once D <= kScaleChunk - 1
-    static_assert(STAGES - 2 <= kScaleChunk - 1, "scale chunk double buffer");
+    // a scale chunk buffer is reloaded for the block kScaleChunk blocks after
+    // its last user; with copies issued D <= STAGES - 1 blocks ahead, after a
+    // barrier that every wave passes only once it finished the block before,
+    // that user is done once D <= kScaleChunk
+    static_assert(STAGES - 1 <= kScaleChunk, "scale chunk double buffer");
     // copy instructions each wave issues per K block (A, W, weight scales);
     // a scale chunk adds kScaleLoads more every kScaleChunk blocks
     static constexpr int kCopiesPerBlock = kALoads + kBLoads + 1;
-    static_assert((STAGES - 2) * kCopiesPerBlock <= 63, "vmcnt range");
+    static_assert((STAGES - 2) * kCopiesPerBlock <= 63, "vmcnt range");  // wait count in the loop
 };
 
 // One LDS pipeline stage: the A (token) and W (weight) tiles of one K block.
@@ -231,15 +232,15 @@ __device__ __forceinline__ TileOperands tile_operands(const uint8_t *a, const fl
 // the current block from LDS (the weight fragments, then one token fragment
 // per 16-row tile, each followed by its MFMAs and promotion FMAs), then waits
 // for its copies and meets the other waves at one barrier, so the copies
-// overlap the whole MFMA phase.  With S >= 3 stages the copies run
-// D = S - 2 blocks ahead: an iteration issues block kb + D into the stage
-// last read in iteration kb - 2 (every wave has passed the barrier of
-// iteration kb - 1 since), waits until at most the copies of the D newer
-// blocks are outstanding, meets the others at a barrier and computes block
-// kb.  Every wave issues the same copies, so the wait count is uniform; the
-// activation-scale chunk of a block is issued before the block's operand
-// copies, so the wait also covers it (an extra chunk copy among the newer
-// ones only makes the wait stricter).
+// overlap the whole MFMA phase (in two halves, see below).  With S >= 3
+// stages the copies run D = S - 1 blocks ahead: an iteration waits until at
+// most the copies of the D - 1 newer blocks are outstanding, meets the
+// others at a barrier, issues block kb + D into the stage last read in
+// iteration kb - 1 and computes block kb.  Every wave issues the same
+// copies, so the wait count is uniform; the activation-scale chunk of a
+// block is issued before the block's operand copies, so the wait also
+// covers it (an extra chunk copy among the newer ones only makes the wait
+// stricter).
 //
 // Copy t of wave v fills LDS rows [8 (v + kWaves t), +8): lane L writes
 // physical chunk L % 8 of row L / 8 of that block, i.e. the row's logical
@@ -436,18 +437,21 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
-        constexpr int D = C::kStages - 2;
+        // S >= 3 stages: after the barrier of iteration kb every wave has
+        // finished block kb - 1, so its stage takes block kb + D, D = S - 1;
+        // before the barrier, only the copies of blocks kb + 1 .. kb + D - 1
+        // may still be outstanding.
+        constexpr int D = C::kStages - 1;
         for (int d = 0; d < D; ++d)
             if (kb0 + d < kb1) issue(op, kb0 + d, d, -1);
         for (int kb = kb0; kb < kb1; ++kb) {
             const int i = kb - kb0;
-            if (kb + D < kb1) {
-                issue(op, kb + D, (i + D) % C::kStages, -1);
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D * C::kCopiesPerBlock) : "memory");
-            } else {
+            if (kb + D - 1 < kb1)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"((D - 1) * C::kCopiesPerBlock) : "memory");
+            else
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            }
             __syncthreads();
+            if (kb + D < kb1) issue(op, kb + D, (i + D) % C::kStages, -1);
             compute(i % C::kStages, kb, [] {});
         }
     }
