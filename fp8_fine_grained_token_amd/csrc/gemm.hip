@@ -603,37 +603,51 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 // Grouped GEMM.  Logical tiles are ordered expert by expert; inside an
 // expert, N tile by N tile, and the expert's M tiles are consecutive, so the
 // M tiles that share one W tile run next to each other on one XCD.  The
-// offsets live on the device: thread 0 walks them (clamped to [0, T]; a
-// decreasing range is empty), counts the real tiles R, gives each XCD a
-// contiguous range of ceil(R / 8) of them (the grid is sized for the worst
-// case (ceil(T / BM) + E) * tiles_n, so sizing the ranges by the grid would
-// leave the last XCDs idle) and finds this tile's expert; surplus
-// workgroups exit.
+// offsets live on the device: thread 0 walks them, counts the real tiles R,
+// gives each XCD a contiguous range of ceil(R / 8) of them (the grid is
+// sized for the worst case (ceil(T / BM) + E) * tiles_n, so sizing the
+// ranges by the grid would leave the last XCDs idle) and finds this tile's
+// expert; surplus workgroups exit.  Expert e's rows are [lo_e, hi_e) with
+// lo_e = max(clamp(off[e]), hi_{e-1}) and hi_e = max(lo_e, clamp(off[e+1])),
+// clamp to [0, T]: the same as [off[e], off[e + 1]) for valid
+// (non-decreasing) offsets, and disjoint ranges within [0, T] for any
+// others, so the tile count never exceeds the worst case.
 template <class C, int OUT>
 __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p) {
     __shared__ TileLds<C> lds;
     __shared__ int64_t info[4];
     if (threadIdx.x == 0) {
         auto clamp_t = [&](int64_t v) { return v < 0 ? (int64_t)0 : (v > p.M ? p.M : v); };
-        auto m_tiles = [&](int e) {
-            const int64_t lo = clamp_t(p.offsets[e]), hi = clamp_t(p.offsets[e + 1]);
-            return hi > lo ? (hi - lo + C::BM - 1) / C::BM : (int64_t)0;
+        // rows [lo, hi) of expert e, given the previous expert's end `prev`
+        auto range = [&](int e, int64_t prev, int64_t &lo, int64_t &hi) {
+            lo = clamp_t(p.offsets[e]);
+            lo = lo > prev ? lo : prev;
+            hi = clamp_t(p.offsets[e + 1]);
+            hi = hi > lo ? hi : lo;
         };
         int64_t total = 0;
-        for (int e = 0; e < p.E; ++e) total += m_tiles(e) * p.tiles_n;
+        {
+            int64_t lo, hi = 0;
+            for (int e = 0; e < p.E; ++e) {
+                range(e, hi, lo, hi);
+                total += (hi - lo + C::BM - 1) / C::BM * p.tiles_n;
+            }
+        }
         const int64_t per = (total + kNumXcd - 1) / kNumXcd;
         const int64_t slot = blockIdx.x / kNumXcd;
         int64_t rem = (blockIdx.x % kNumXcd) * per + slot;
         int64_t e_hit = -1, r0 = 0, r1 = 0, tn = 0;
         if (slot < per && rem < total) {
+            int64_t lo, hi = 0;
             for (int e = 0; e < p.E; ++e) {
-                const int64_t mt = m_tiles(e);
+                range(e, hi, lo, hi);
+                const int64_t mt = (hi - lo + C::BM - 1) / C::BM;
                 const int64_t tiles = mt * p.tiles_n;
                 if (rem < tiles) {
                     e_hit = e;
                     tn = rem / mt;
-                    r0 = clamp_t(p.offsets[e]) + (rem - tn * mt) * C::BM;
-                    r1 = clamp_t(p.offsets[e + 1]);
+                    r0 = lo + (rem - tn * mt) * C::BM;
+                    r1 = hi;
                     break;
                 }
                 rem -= tiles;

@@ -120,8 +120,11 @@ fp8_status fp8_block_gemm(const void *a_e4m3, const float *a_scales,
  *   a_e4m3        [T][K] E4M3, rows sorted by expert; a_scales [T][K/128]
  *   w_e4m3        [E][N][K] E4M3; w_scales [E][N/128][K/128]
  *   group_offsets [E+1] int32 on the DEVICE: rows [off[e], off[e+1]) belong
- *                 to expert e.  Offsets are clamped to [0, T]; a decreasing
- *                 range is empty.  The host never reads them.
+ *                 to expert e for valid (non-decreasing) offsets.  Any others
+ *                 are made safe: offsets are clamped to [0, T] and expert e's
+ *                 range starts no earlier than expert e-1's ends (an empty
+ *                 range if that is past its end), so ranges never overlap.
+ *                 The host never reads them.
  *   c             [T][N] fp32 or bf16; rows outside every expert's range are
  *                 left untouched.
  * Each routed row r of expert e gets C[r] = block GEMM of (a[r], W[e]).

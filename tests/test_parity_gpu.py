@@ -245,11 +245,12 @@ def test_grouped_garbage_offsets_are_memory_safe():
     t.cuda.synchronize()
     ch = host(c)
     assert np.all(ch[:10] == 7.0)
+    # Clamped and made non-overlapping: expert 0 keeps [10, 60), expert 1 is
+    # empty, expert 2 starts where expert 0 ended: [60, 90), expert 3 gets
+    # [90, 100).
     R, _ = oracle.grouped_gemm(qa, sa, qw, sw, np.array([10, 60, 60, 90, 100], np.int32))
-    # rows [10, 60) belong to expert 0, [60, 90) to expert 2 (expert 1 empty),
-    # [90, 100) to expert 3; rows [40, 60) are also claimed by expert 2's
-    # clamped range [40, 90) and so are not compared.
-    check_gemm(c[10:40], R[10:40], "f32", "garbage offsets expert 0")
+    check_gemm(c[10:60], R[10:60], "f32", "garbage offsets expert 0")
+    check_gemm(c[60:90], R[60:90], "f32", "garbage offsets expert 2")
     check_gemm(c[90:100], R[90:100], "f32", "garbage offsets expert 3")
 
 
