@@ -194,6 +194,18 @@ __device__ __forceinline__ void copy16(const v4i &r, uint32_t voff, uint32_t sof
                  : "v"(voff), "s"(r), "s"(soff), "s"(lds)
                  : "memory", "m0");
 }
+// The same copy with the nontemporal cache policy, for the weight tiles:
+// streamed from HBM, plain copies of this pattern top out near 2.6 TB/s
+// while nontemporal ones reach ~6.5 TB/s (measured with a streaming probe);
+// the activation tiles, which neighbouring tiles re-read through L2, keep
+// the default policy.
+__device__ __forceinline__ void copy16_nt(const v4i &r, uint32_t voff, uint32_t soff,
+                                          uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen nt lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(soff), "s"(lds)
+                 : "memory", "m0");
+}
 __device__ __forceinline__ void copy4(const v4i &r, uint32_t voff, uint32_t soff, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
                  :
@@ -319,7 +331,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         const uint32_t so = (uint32_t)(st * sizeof(S));
 #pragma unroll
         for (int t = 0; t < C::kBLoads; ++t)
-            copy16(src.w, wave_voff + t * rowstep, soff, lds_b0 + so + 1024 * C::kWaves * t);
+            copy16_nt(src.w, wave_voff + t * rowstep, soff, lds_b0 + so + 1024 * C::kWaves * t);
         // every wave fetches the (one or two) weight scales of the block to
         // the same LDS words; the duplicates carry identical values
         copy4(src.sw, sw_voff, (uint32_t)kb * 4u, lds_sw0 + (uint32_t)st * sizeof(L.sw[0]));
