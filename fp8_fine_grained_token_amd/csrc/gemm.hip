@@ -69,6 +69,8 @@ struct GemmParams {
     int ksplit, kb_per_split;
     int E;
     int group_m;             // tile-order grouping height (in M tiles)
+    int tn1, tn2;            // two-kind plan: 256-wide and 192-wide N tiles
+    int64_t n_split;         // two-kind plan: first column of the 192-wide tiles
 };
 
 template <int BM_, int BN_, int WAVES_M, int WAVES_N, int STAGES>
@@ -96,7 +98,10 @@ struct TileCfg {
     static_assert(BM % 32 == 0, "scale loader");
     static_assert(((BM + BN) * 128) % 4096 == 0, "stage size");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
-    static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns sit in one 128-block");
+    // A wave's columns sit in one 128-column weight-scale block when WN
+    // divides 128 (tiles start at multiples of BN); otherwise each 16-column
+    // fragment looks up its own block.
+    static constexpr bool kWaveInOneBlock = WN <= 128 && 128 % WN == 0;
     static_assert(STAGES >= 2, "pipeline");
     // a scale chunk buffer is reloaded for the block kScaleChunk blocks after
     // its last user; with copies issued D <= STAGES - 1 blocks ahead, after a
@@ -259,7 +264,7 @@ __device__ __forceinline__ TileOperands tile_operands(const uint8_t *a, const fl
 // chunk (L % 8) ^ key(row).
 template <class C>
 __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K, int G, int kb0,
-                                              int kb1, int sw_first_block_of_wave,
+                                              int kb1, int col_off,
                                               TileLds<C> &L,
                                               v4f (&acc)[C::kTM][C::kTN]) {
     using S = Stage<C::BM, C::BN>;
@@ -360,12 +365,27 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             const uint4 hi = *reinterpret_cast<const uint4 *>(lb + j * 2048 + frag1);
             wfr[j] = make_v8i(lo, hi);
         }
-        const float swv = L.sw[s][sw_first_block_of_wave];
         const float *sa_lane =
             &L.chunks.v[(kb / C::kScaleChunk) & 1][(kb >> 2) & 1][wm * C::WM + lr][kb & 3];
+        // combined scale of M tile i and N fragment j: sa(i) * sw(j)
         float sc[C::kTM];
+        float swj[C::kTN];
+        if constexpr (C::kWaveInOneBlock) {
+            const float swv = L.sw[s][col_off >> 7];
 #pragma unroll
-        for (int i = 0; i < C::kTM; ++i) sc[i] = sa_lane[64 * i] * swv;
+            for (int i = 0; i < C::kTM; ++i) sc[i] = sa_lane[64 * i] * swv;
+        } else {
+#pragma unroll
+            for (int i = 0; i < C::kTM; ++i) sc[i] = sa_lane[64 * i];
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j) swj[j] = L.sw[s][(col_off + 16 * j) >> 7];
+        }
+        auto scale = [&](int i, int j) {
+            if constexpr (C::kWaveInOneBlock)
+                return sc[i];
+            else
+                return sc[i] * swj[j];
+        };
         auto afrag = [&](int i) {
             const uint4 lo = *reinterpret_cast<const uint4 *>(la + i * 2048 + frag0);
             const uint4 hi = *reinterpret_cast<const uint4 *>(la + i * 2048 + frag1);
@@ -375,10 +395,11 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         // the VALU FMAs never wait on the MFMA that produced their operand, and
         // the next A fragment is read from LDS one row of tiles ahead.
         auto promote = [&](int i, int j, const v4f &p) {
-            acc[i][j][0] = __builtin_fmaf(p[0], sc[i], acc[i][j][0]);
-            acc[i][j][1] = __builtin_fmaf(p[1], sc[i], acc[i][j][1]);
-            acc[i][j][2] = __builtin_fmaf(p[2], sc[i], acc[i][j][2]);
-            acc[i][j][3] = __builtin_fmaf(p[3], sc[i], acc[i][j][3]);
+            const float f = scale(i, j);
+            acc[i][j][0] = __builtin_fmaf(p[0], f, acc[i][j][0]);
+            acc[i][j][1] = __builtin_fmaf(p[1], f, acc[i][j][1]);
+            acc[i][j][2] = __builtin_fmaf(p[2], f, acc[i][j][2]);
+            acc[i][j][3] = __builtin_fmaf(p[3], f, acc[i][j][3]);
         };
         v8i af = afrag(0);
         v4f p_prev{};
@@ -478,8 +499,9 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 // every store instruction writes full 128-byte lines.  Rows that do not fit
 // in the stages at once (fp32 output of a 256 x 256 tile) go in passes of
 // whole wave rows.  Inside an LDS row, the 32-byte piece q of row r is kept
-// at piece q ^ (r % 16) (bounded by the row length), which spreads the 16
-// rows a wave writes at once over the banks.
+// at piece q ^ (r % 16) (bounded by the row length; rotated by r instead
+// for rows that are not a power of two long), which spreads the 16 rows a
+// wave writes at once over the banks.
 template <class C, int OUT>
 __device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], TileLds<C> &L,
                                            void *c, int64_t ldc, int64_t row0, int64_t row_end,
@@ -490,8 +512,16 @@ __device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], Til
     constexpr int kRowsPerPass = kFit < C::BM ? kFit : C::BM;
     static_assert(kRowsPerPass >= C::WM && C::BM % kRowsPerPass == 0, "store passes");
     constexpr int kPieces = kRB / 32;
+    static_assert(kRB % 32 == 0, "row length");
+    constexpr bool kPow2 = (kPieces & (kPieces - 1)) == 0;
     constexpr int kSwz = (kPieces < 16 ? kPieces : 16) - 1;  // XOR mask on the 32-byte piece
-    static_assert((kPieces & (kPieces - 1)) == 0, "row length");
+    // LDS byte offset of byte b of row r: the 32-byte piece b / 32 is XORed
+    // (power-of-two rows) or rotated (other rows) by the row index
+    auto lds_off = [](int r, int b) {
+        const int q = b >> 5;
+        const int qp = kPow2 ? (q ^ (r & kSwz)) : (q + r) % kPieces;
+        return r * kRB + (qp << 5) + (b & 31);
+    };
     constexpr int kUnitsPerRow = kRB / 16;
     constexpr int kUnits = kRowsPerPass * kUnitsPerRow;
     static_assert(kUnits % C::kThreads == 0, "store loop");
@@ -511,11 +541,10 @@ __device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], Til
 #pragma unroll
             for (int i = 0; i < C::kTM; ++i) {
                 const int r = wave_row0 - r_lo + 16 * i + (lane & 15);
-                const int swz = (r & kSwz) << 5;
 #pragma unroll
                 for (int j = 0; j < C::kTN; ++j) {
                     const int cb = (wn * C::WN + 16 * j + 4 * (lane >> 4)) * kOB;
-                    uint8_t *dst = buf + r * kRB + (cb ^ swz);
+                    uint8_t *dst = buf + lds_off(r, cb);
                     const v4f v = acc[i][j];
                     if (OUT == kOutBF16) {
                         uint2 o;
@@ -537,14 +566,27 @@ __device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], Til
             const int64_t gcol = n0 + cb / kOB;
             // N is a multiple of 128: a 16-byte piece is all in or all out
             if (grow < row_end && gcol < N) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(buf + r * kRB +
-                                                                 (cb ^ ((r & kSwz) << 5)));
+                const uint4 v = *reinterpret_cast<const uint4 *>(buf + lds_off(r, cb));
                 *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(c) + (grow * ldc + gcol) * kOB) =
                     v;
             }
         }
     }
 }
+
+// Tile shapes: 256 x 256 on 8 waves (wave tile 128 x 64, two LDS stages)
+// for GEMMs that fill the GPU; 128 x 128 on 4 waves (wave tile 64 x 64,
+// four stages: copies three K blocks ahead) for small ones, with split-K when
+// even those tiles cannot occupy the 256 CUs; 128 x 256 on 8 waves (wave
+// tile 64 x 64, three stages) for the grouped GEMM, whose experts' token
+// counts make 128-row granularity worth keeping.
+using BigTile = TileCfg<256, 256, 2, 4, 2>;
+// 256 x 192 on 8 waves (wave tile 128 x 48): covers part of the columns
+// when 256 x 256 tiles alone would leave a partly filled last round (see
+// plan_two_kind).
+using NarrowTile = TileCfg<256, 192, 2, 4, 2>;
+using SmallTile = TileCfg<128, 128, 2, 2, 4>;
+using MidTile = TileCfg<128, 256, 2, 4, 3>;
 
 // Logical tile index of this workgroup after the XCD remap (gridDim.x is a
 // multiple of 8; each XCD gets a contiguous range of logical tiles).
@@ -580,13 +622,71 @@ __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
     const TileOperands op =
         tile_operands<C>(p.a, p.sa, p.w, p.sw, row0, p.M - row0, n0, p.N - n0, p.K, p.G);
     const int wn = (threadIdx.x >> 6) % C::kWavesN;
-    const int sw_slot = (int)(((n0 + wn * C::WN) >> 7) - (n0 >> 7));
-    tile_mainloop<C>(op, p.K, p.G, kb0, kb1, sw_slot, lds, acc);
+    tile_mainloop<C>(op, p.K, p.G, kb0, kb1, (int)(n0 & 127) + wn * C::WN, lds, acc);
     if (OUT == kOutPartial)
         tile_store<C, kOutF32>(acc, lds, p.partial + (int64_t)ks * p.M * p.N, p.N, row0, p.M, n0,
                                p.N);
     else
         tile_store<C, OUT>(acc, lds, p.c, p.N, row0, p.M, n0, p.N);
+}
+
+// One 256-row tile of the dense GEMM at (row0, n0), full K.
+template <class C, int OUT>
+__device__ __forceinline__ void dense_tile(const GemmParams &p, TileLds<C> &lds, int64_t row0,
+                                           int64_t n0) {
+    v4f acc[C::kTM][C::kTN];
+    const TileOperands op =
+        tile_operands<C>(p.a, p.sa, p.w, p.sw, row0, p.M - row0, n0, p.N - n0, p.K, p.G);
+    const int wn = (threadIdx.x >> 6) % C::kWavesN;
+    tile_mainloop<C>(op, p.K, p.G, 0, p.G, (int)(n0 & 127) + wn * C::WN, lds, acc);
+    tile_store<C, OUT>(acc, lds, p.c, p.N, row0, p.M, n0, p.N);
+}
+
+// Grouped raster over a tiles_m x tiles_n grid (runs of group_m M tiles
+// sweep across N).
+__device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int group_m, int &tm,
+                                       int &tn) {
+    const int span = group_m * tiles_n;
+    const int grp = t / span;
+    const int first_m = grp * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int in = t - grp * span;
+    tm = first_m + in % gm;
+    tn = in / gm;
+}
+
+// Dense GEMM with two tile widths.  When 256 x 256 tiles alone would leave
+// the last round of workgroups partly filled, columns [0, n_split) are
+// covered by 256 x 256 tiles and [n_split, N) by 256 x 192 tiles, chosen so
+// that each kind fills whole rounds (e.g. 4096 x 7168: 256 of each, one of
+// each per CU instead of two 256 x 256 tiles on 192 CUs and one on the
+// rest).  Each XCD takes a contiguous share of each kind, the wide tiles
+// first; the LDS holds either layout.
+template <int OUT>
+__global__ __launch_bounds__(BigTile::kThreads) void dense_gemm_two_kind_kernel(GemmParams p) {
+    using CB = BigTile;
+    using CN = NarrowTile;
+    static_assert(CB::kThreads == CN::kThreads && CB::BM == CN::BM, "two-kind tiles");
+    __shared__ union DenseLds {
+        TileLds<CB> big;
+        TileLds<CN> narrow;
+    } lds;
+    const int t1 = p.tiles_m * p.tn1, t2 = p.tiles_m * p.tn2;
+    const int per1 = (t1 + kNumXcd - 1) / kNumXcd, per2 = (t2 + kNumXcd - 1) / kNumXcd;
+    const int xcd = blockIdx.x % kNumXcd;
+    const int slot = blockIdx.x / kNumXcd;
+    int tm, tn;
+    if (slot < per1) {
+        const int t = xcd * per1 + slot;
+        if (t >= t1) return;
+        raster(t, p.tiles_m, p.tn1, p.group_m, tm, tn);
+        dense_tile<CB, OUT>(p, lds.big, (int64_t)tm * CB::BM, (int64_t)tn * CB::BN);
+    } else {
+        const int t = xcd * per2 + (slot - per1);
+        if (slot - per1 >= per2 || t >= t2) return;
+        raster(t, p.tiles_m, p.tn2, p.group_m, tm, tn);
+        dense_tile<CN, OUT>(p, lds.narrow, (int64_t)tm * CN::BM, p.n_split + (int64_t)tn * CN::BN);
+    }
 }
 
 // Split-K reduction: C = sum over splits in fixed order 0..S-1, then the
@@ -682,34 +782,58 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p)
     const TileOperands op =
         tile_operands<C>(p.a, p.sa, w, sw, row0, row_end - row0, n0, p.N - n0, p.K, p.G);
     const int wn = (threadIdx.x >> 6) % C::kWavesN;
-    const int sw_slot = (int)(((n0 + wn * C::WN) >> 7) - (n0 >> 7));
-    tile_mainloop<C>(op, p.K, p.G, 0, p.G, sw_slot, lds, acc);
+    tile_mainloop<C>(op, p.K, p.G, 0, p.G, (int)(n0 & 127) + wn * C::WN, lds, acc);
     tile_store<C, OUT>(acc, lds, p.c, p.N, row0, row_end, n0, p.N);
 }
 
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
-// Tile shapes: 256 x 256 on 8 waves (wave tile 128 x 64, two LDS stages)
-// for GEMMs that fill the GPU; 128 x 128 on 4 waves (wave tile 64 x 64,
-// four stages: copies two K blocks ahead) for small ones, with split-K when
-// even those tiles cannot occupy the 256 CUs; 128 x 256 on 8 waves (wave
-// tile 64 x 64, three stages) for the grouped GEMM, whose experts' token
-// counts make 128-row granularity worth keeping.
-using BigTile = TileCfg<256, 256, 2, 4, 2>;
-using SmallTile = TileCfg<128, 128, 2, 2, 4>;
-using MidTile = TileCfg<128, 256, 2, 4, 3>;
 constexpr int kCUs = 256;
 
 struct Plan {
     bool big;
     int ksplit;
     int kb_per_split;
+    int tn1 = 0, tn2 = 0;  // two-kind plan (big only): 256-wide and 192-wide N tiles
 };
+
+// Two-kind plan for 256-row tiles: tn1 256-wide N tiles then tn2 192-wide
+// ones, used when both kinds fill whole rounds of the CUs and the estimated
+// time (a 256 x 192 tile costs ~0.85 of a 256 x 256 one: its copies are 7/8
+// and its MFMAs 3/4) beats whole-width tiles.  Returns false if none does.
+bool plan_two_kind(int64_t M, int64_t N, int &tn1, int &tn2) {
+    const int64_t tm = (M + 255) / 256;
+    const int64_t tn_big = (N + 255) / 256;
+    const double base = (double)((tm * tn_big + kCUs - 1) / kCUs);
+    double best = base;
+    bool found = false;
+    for (int64_t a = 0; a <= N / 256; ++a) {
+        const int64_t rest = N - 256 * a;
+        const int64_t b = (rest + 191) / 192;
+        if (b == 0 || (tm * a) % kCUs != 0 || (tm * b) % kCUs != 0) continue;
+        const double cost = (double)(tm * a / kCUs) + 0.85 * (double)(tm * b / kCUs);
+        if (cost < best - 1e-9) {
+            best = cost;
+            tn1 = (int)a;
+            tn2 = (int)b;
+            found = true;
+        }
+    }
+    return found;
+}
 
 Plan plan_dense(int64_t M, int64_t N, int64_t K) {
     const int G = (int)(K / 128);
     const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    if (big_tiles >= kCUs) return {true, 1, G};
+    if (big_tiles >= kCUs) {
+        Plan pl{true, 1, G};
+        int a, b;
+        if (plan_two_kind(M, N, a, b)) {
+            pl.tn1 = a;
+            pl.tn2 = b;
+        }
+        return pl;
+    }
     const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
     int s = 1;
     // Split K only when the output tiles cannot fill the CUs and each split
@@ -760,6 +884,22 @@ hipError_t launch_block_gemm(const void *a, const float *sa, const void *w, cons
     if (pl.ksplit > 1 && (workspace == nullptr || workspace_bytes < need)) pl = {false, 1, p.G};
     p.ksplit = pl.ksplit;
     p.kb_per_split = pl.kb_per_split;
+    if (pl.big && pl.tn2 > 0) {
+        p.tiles_m = (int)((M + 255) / 256);
+        p.tn1 = pl.tn1;
+        p.tn2 = pl.tn2;
+        p.n_split = (int64_t)pl.tn1 * BigTile::BN;
+        const int per1 = (p.tiles_m * p.tn1 + kNumXcd - 1) / kNumXcd;
+        const int per2 = (p.tiles_m * p.tn2 + kNumXcd - 1) / kNumXcd;
+        const int grid = kNumXcd * (per1 + per2);
+        if (bf16_out)
+            hipLaunchKernelGGL(dense_gemm_two_kind_kernel<kOutBF16>, dim3(grid),
+                               dim3(BigTile::kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL(dense_gemm_two_kind_kernel<kOutF32>, dim3(grid),
+                               dim3(BigTile::kThreads), 0, stream, p);
+        return hipGetLastError();
+    }
     if (pl.big)
         return bf16_out ? launch_dense<BigTile, kOutBF16>(p, stream)
                         : launch_dense<BigTile, kOutF32>(p, stream);
