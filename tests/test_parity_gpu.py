@@ -176,6 +176,38 @@ def test_gemm_big_tiles_ragged_edges(out):
     check_gemm(c[torch().from_numpy(rows).cuda()], R, out, f"big tiles ragged {out}")
 
 
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_192_wide_tiles_all_columns(out):
+    # 4096 x 6144 is planned as 32 x 16 tiles of 256 x 192 (two full rounds):
+    # tiles start at column offsets 0 or 64 inside a 128-column weight-scale
+    # block, so every way a wave's 48 columns can straddle two blocks occurs.
+    # Rows from every M tile, all columns.
+    M, N, K = 4096, 6144, 512
+    g = I.gemm_inputs(M, N, K, seed=78, outlier_frac=0.01, outlier_mult=20.0)
+    qa, sa, qw, sw = quantize(g)
+    c = run_gemm(qa, sa, qw, sw, out)
+    rows = np.unique(np.concatenate([np.arange(0, M, 127), [255, 256, 4095]]))
+    R = oracle.block_gemm(qa, sa, qw, sw, rows)
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, out, f"192-wide tiles {out}")
+
+
+def test_gemm_two_tile_widths_metamorphic_and_deterministic():
+    # 4096 x 7168 runs 256 tiles of 256 x 256 and 256 of 256 x 192: two runs
+    # are bitwise identical, and scaling the activation scales by 2^3 scales
+    # the FP32 result by exactly 2^3.
+    M, N, K = 4096, 7168, 256
+    g = I.gemm_inputs(M, N, K, seed=79)
+    qa, sa, qw, sw = quantize(g)
+    c0 = host(run_gemm(qa, sa, qw, sw, "f32"))
+    c1 = host(run_gemm(qa, sa, qw, sw, "f32"))
+    c2 = host(run_gemm(qa, sa * np.float32(8.0), qw, sw, "f32"))
+    assert np.array_equal(c0.view(np.uint32), c1.view(np.uint32))
+    assert np.array_equal(c2, c0 * np.float32(8.0))
+    rows = np.array([0, 255, 256, 2047, 4095])
+    R = oracle.block_gemm(qa, sa, qw, sw, rows)
+    check_gemm(torch().from_numpy(c0[rows]), R, "f32", "two tile widths")
+
+
 def test_gemm_power_of_two_metamorphic_and_deterministic():
     # Scaling the activation scales by 2^j scales an FP32 result by exactly
     # 2^j; two runs of the same call are bitwise identical.
