@@ -320,8 +320,16 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             if (half < 0 || a_copy_in_half(t, half))
                 copy16(src.a, wave_voff + t * rowstep, soff, lds_a0 + so + 1024 * C::kWaves * t);
     };
-    // everything of block kb except (if a_half >= 0) the other half of A
-    auto issue = [&](const TileOperands &src, int kb, int st, int a_half) {
+    auto issue_w = [&](const TileOperands &src, int kb, int st) {
+        const uint32_t soff = (uint32_t)kb * 128u;
+        const uint32_t so = (uint32_t)(st * sizeof(S));
+#pragma unroll
+        for (int t = 0; t < C::kBLoads; ++t)
+            copy16_nt(src.w, wave_voff + t * rowstep, soff, lds_b0 + so + 1024 * C::kWaves * t);
+    };
+    // block kb's scales, its A rows (all, or one half if a_half >= 0) and,
+    // if with_w, its W tile
+    auto issue = [&](const TileOperands &src, int kb, int st, int a_half, bool with_w) {
         if (kb == kb0 || (kb & (C::kScaleChunk - 1)) == 0) {
             const int c = kb / C::kScaleChunk;
             const uint32_t so = (uint32_t)((c & 1) * sizeof(L.chunks.v[0]));
@@ -332,11 +340,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
                            lds_sc0 + so + 1024 * C::kWaves * t);
         }
         issue_a(src, kb, st, a_half);
-        const uint32_t soff = (uint32_t)kb * 128u;
-        const uint32_t so = (uint32_t)(st * sizeof(S));
-#pragma unroll
-        for (int t = 0; t < C::kBLoads; ++t)
-            copy16_nt(src.w, wave_voff + t * rowstep, soff, lds_b0 + so + 1024 * C::kWaves * t);
+        if (with_w) issue_w(src, kb, st);
         // every wave fetches the (one or two) weight scales of the block to
         // the same LDS words; the duplicates carry identical values
         copy4(src.sw, sw_voff, (uint32_t)kb * 4u, lds_sw0 + (uint32_t)st * sizeof(L.sw[0]));
@@ -354,16 +358,22 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     // D[n][m]: lane L holds outputs n = 4 (L / 16) + e (e < 4), m = L % 16.
     // The activation scale is then one value per lane per M tile and the
     // weight scale one value per wave.
+    auto wfrag = [&](int s, int j) {
+        const uint8_t *lb = L.stages[s].b + b_base;
+        const uint4 lo = *reinterpret_cast<const uint4 *>(lb + j * 2048 + frag0);
+        const uint4 hi = *reinterpret_cast<const uint4 *>(lb + j * 2048 + frag1);
+        return make_v8i(lo, hi);
+    };
+    // Weight fragments of the block being computed.  With two stages they are
+    // already in registers when a block starts: the previous block reloads
+    // each one from the other stage right after its last MFMA on it.
+    v8i wfr[C::kTN];
     auto compute = [&](int s, int kb, auto &&mid) {
         constexpr bool kSplit = C::kStages == 2;
         const uint8_t *la = L.stages[s].a + a_base;
-        const uint8_t *lb = L.stages[s].b + b_base;
-        v8i wfr[C::kTN];
+        if constexpr (!kSplit) {
 #pragma unroll
-        for (int j = 0; j < C::kTN; ++j) {
-            const uint4 lo = *reinterpret_cast<const uint4 *>(lb + j * 2048 + frag0);
-            const uint4 hi = *reinterpret_cast<const uint4 *>(lb + j * 2048 + frag1);
-            wfr[j] = make_v8i(lo, hi);
+            for (int j = 0; j < C::kTN; ++j) wfr[j] = wfrag(s, j);
         }
         const float *sa_lane =
             &L.chunks.v[(kb / C::kScaleChunk) & 1][(kb >> 2) & 1][wm * C::WM + lr][kb & 3];
@@ -417,6 +427,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j) {
                 const v4f p = mfma_e4m3(wfr[j], af);
+                if (kSplit && i == C::kTM - 1) wfr[j] = wfrag(s ^ 1, j);  // next block's
                 if (pi >= 0) promote(pi, pj, p_prev);
                 p_prev = p;
                 pi = i;
@@ -428,44 +439,58 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     };
 
     if constexpr (C::kStages == 2) {
-        // Two stages, each block's copies in two halves so that the copy pipe
-        // never drains at a barrier.  Iteration kb: issue half 1 of block
-        // kb + 1 (W, scales, the A rows of the waves' first kTM / 2 M tiles)
-        // into the other stage (free: every wave finished block kb - 1 before
-        // the last barrier); compute those M tiles of block kb; wait for half
-        // 2 of block kb (issued in the middle of iteration kb - 1; only the
-        // kH1 newer copies may stay outstanding) and meet at a barrier; issue
-        // half 2 of block kb + 1; compute the other M tiles; wait for half 1
-        // of block kb + 1 (kH2 newer copies may stay outstanding) and meet at
-        // a barrier.  Each half gets one block of compute to land.
+        // Two stages, each block's copies in two groups so that the copy pipe
+        // never drains at a barrier:
+        //   G1(j): the scales and the A rows of every wave's first kTM / 2 M
+        //          tiles of block j, issued at the start of iteration j - 1;
+        //   G2(j): the other A rows of block j + 1 and the W tile of block
+        //          j + 2, issued in the middle of iteration j.
+        // Iteration kb: issue G1(kb + 1) into the other stage (free: every
+        // wave finished block kb - 1 before the last barrier); compute the
+        // first M tiles of block kb; wait for G2(kb - 1) (only the kG1 newer
+        // copies may stay outstanding) and meet at a barrier; issue G2(kb) (the
+        // W region of this stage is free: every wave holds block kb's W
+        // fragments in registers since before the last barrier); compute the
+        // other M tiles, reloading each W fragment for block kb + 1 (landed
+        // with G2(kb - 1)) right after its last MFMA in block kb; wait for
+        // G1(kb + 1) (kG2 newer copies may stay outstanding) and meet at a
+        // barrier.  Each group has one block of compute to land.
         constexpr int kAHalf = C::kALoads / 2;
-        constexpr int kH1 = kAHalf + C::kBLoads + 1;  // per wave, without a scale chunk
-        constexpr int kH2 = C::kALoads - kAHalf;
+        constexpr int kG1 = kAHalf + 1;  // per wave, without a scale chunk
+        constexpr int kG2 = C::kALoads - kAHalf + C::kBLoads;
         static_assert((C::WM / 2) % (8 * C::kWaves) == 0 && C::kTM % 2 == 0, "split block");
-        // In the last iteration there is no next block: its copies are issued
-        // against empty buffers (every lane out of bounds: nothing is read,
-        // zeros land in the idle stage) so that the wait counts stay fixed
-        // and the loop body has no data-dependent branches.
+        // Blocks past the end are copied from empty buffers (every lane out of
+        // bounds: nothing is read, zeros land in regions no block uses) so
+        // that the wait counts stay fixed and the loop body has no
+        // data-dependent branches.
         TileOperands none = op;
         none.a[2] = none.w[2] = none.sa[2] = none.sw[2] = 0;
-        issue(op, kb0, 0, -1);
+        auto src_for = [&](int kb) {
+            const bool in = kb < kb1;
+            TileOperands t;
+            t.a = in ? op.a : none.a;
+            t.w = in ? op.w : none.w;
+            t.sa = in ? op.sa : none.sa;
+            t.sw = in ? op.sw : none.sw;
+            return t;
+        };
+        issue(op, kb0, 0, -1, true);
+        issue_w(src_for(kb0 + 1), kb0 + 1, 1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j) wfr[j] = wfrag(0, j);
         for (int kb = kb0; kb < kb1; ++kb) {
             const int st = (kb - kb0) & 1;
-            const bool more = kb + 1 < kb1;
-            TileOperands next;
-            next.a = more ? op.a : none.a;
-            next.w = more ? op.w : none.w;
-            next.sa = more ? op.sa : none.sa;
-            next.sw = more ? op.sw : none.sw;
-            issue(next, kb + 1, st ^ 1, 0);
+            const TileOperands next = src_for(kb + 1);
+            issue(next, kb + 1, st ^ 1, 0, false);
             compute(st, kb, [&] {
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kH1) : "memory");
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kG1) : "memory");
                 __syncthreads();
                 issue_a(next, kb + 1, st ^ 1, 1);
+                issue_w(src_for(kb + 2), kb + 2, st);
             });
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kH2) : "memory");
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kG2) : "memory");
             __syncthreads();
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -476,7 +501,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         // may still be outstanding.
         constexpr int D = C::kStages - 1;
         for (int d = 0; d < D; ++d)
-            if (kb0 + d < kb1) issue(op, kb0 + d, d, -1);
+            if (kb0 + d < kb1) issue(op, kb0 + d, d, -1, true);
         for (int kb = kb0; kb < kb1; ++kb) {
             const int i = kb - kb0;
             if (kb + D - 1 < kb1)
@@ -484,7 +509,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             else
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            if (kb + D < kb1) issue(op, kb + D, (i + D) % C::kStages, -1);
+            if (kb + D < kb1) issue(op, kb + D, (i + D) % C::kStages, -1, true);
             compute(i % C::kStages, kb, [] {});
         }
     }
