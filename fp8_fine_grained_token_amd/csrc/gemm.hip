@@ -329,7 +329,9 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     };
     // block kb's scales, its A rows (all, or one half if a_half >= 0) and,
     // if with_w, its W tile
-    auto issue = [&](const TileOperands &src, int kb, int st, int a_half, bool with_w) {
+    // block kb's scales: its activation-scale chunk if one starts there, and
+    // its weight scales
+    auto issue_scales = [&](const TileOperands &src, int kb, int st) {
         if (kb == kb0 || (kb & (C::kScaleChunk - 1)) == 0) {
             const int c = kb / C::kScaleChunk;
             const uint32_t so = (uint32_t)((c & 1) * sizeof(L.chunks.v[0]));
@@ -339,11 +341,15 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
                     copy16(src.sa, sa_voff[t], (uint32_t)c * (4u * C::kScaleChunk),
                            lds_sc0 + so + 1024 * C::kWaves * t);
         }
-        issue_a(src, kb, st, a_half);
-        if (with_w) issue_w(src, kb, st);
         // every wave fetches the (one or two) weight scales of the block to
         // the same LDS words; the duplicates carry identical values
         copy4(src.sw, sw_voff, (uint32_t)kb * 4u, lds_sw0 + (uint32_t)st * sizeof(L.sw[0]));
+    };
+    // all of block kb
+    auto issue = [&](const TileOperands &src, int kb, int st) {
+        issue_scales(src, kb, st);
+        issue_a(src, kb, st, -1);
+        issue_w(src, kb, st);
     };
 
     // LDS byte offsets of this lane's two 16-byte operand chunks inside a
@@ -364,22 +370,11 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         const uint4 hi = *reinterpret_cast<const uint4 *>(lb + j * 2048 + frag1);
         return make_v8i(lo, hi);
     };
-    // Weight fragments of the block being computed.  With two stages they are
-    // already in registers when a block starts: the previous block reloads
-    // each one from the other stage right after its last MFMA on it.
-    v8i wfr[C::kTN];
-    auto compute = [&](int s, int kb, auto &&mid) {
-        constexpr bool kSplit = C::kStages == 2;
-        const uint8_t *la = L.stages[s].a + a_base;
-        if constexpr (!kSplit) {
-#pragma unroll
-            for (int j = 0; j < C::kTN; ++j) wfr[j] = wfrag(s, j);
-        }
+    // Scales of block kb (stage s): sc[i] = sa(i) * sw for waves inside one
+    // weight-scale block, else sc[i] = sa(i) and swj[j] = sw(fragment j).
+    auto load_scales = [&](int s, int kb, float (&sc)[C::kTM], float (&swj)[C::kTN]) {
         const float *sa_lane =
             &L.chunks.v[(kb / C::kScaleChunk) & 1][(kb >> 2) & 1][wm * C::WM + lr][kb & 3];
-        // combined scale of M tile i and N fragment j: sa(i) * sw(j)
-        float sc[C::kTM];
-        float swj[C::kTN];
         if constexpr (C::kWaveInOneBlock) {
             const float swv = L.sw[s][col_off >> 7];
 #pragma unroll
@@ -390,6 +385,23 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j) swj[j] = L.sw[s][(col_off + 16 * j) >> 7];
         }
+    };
+    // Weight fragments and scales of the block being computed.  With two
+    // stages they are already in registers when a block starts: the previous
+    // block reloads each W fragment from the other stage right after its last
+    // MFMA on it, and reads the next block's scales during its last row.
+    v8i wfr[C::kTN];
+    float sc[C::kTM], swj[C::kTN];
+    auto compute = [&](int s, int kb, auto &&mid) {
+        constexpr bool kSplit = C::kStages == 2;
+        const uint8_t *la = L.stages[s].a + a_base;
+        if constexpr (!kSplit) {
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j) wfr[j] = wfrag(s, j);
+        }
+        if constexpr (!kSplit) load_scales(s, kb, sc, swj);
+        float sc_next[C::kTM], swj_next[C::kTN];
+        // combined scale of M tile i and N fragment j: sa(i) * sw(j)
         auto scale = [&](int i, int j) {
             if constexpr (C::kWaveInOneBlock)
                 return sc[i];
@@ -424,6 +436,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             // across the middle of a split block
             const bool ahead = i + 1 < C::kTM && !(kSplit && i + 1 == C::kTM / 2);
             const v8i af_next = afrag(ahead ? i + 1 : i);
+            if (kSplit && i == C::kTM - 1) load_scales(s ^ 1, kb + 1, sc_next, swj_next);
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j) {
                 const v4f p = mfma_e4m3(wfr[j], af);
@@ -436,15 +449,21 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             af = af_next;
         }
         promote(pi, pj, p_prev);
+        if constexpr (kSplit) {
+#pragma unroll
+            for (int i = 0; i < C::kTM; ++i) sc[i] = sc_next[i];
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j) swj[j] = swj_next[j];
+        }
     };
 
     if constexpr (C::kStages == 2) {
         // Two stages, each block's copies in two groups so that the copy pipe
         // never drains at a barrier:
-        //   G1(j): the scales and the A rows of every wave's first kTM / 2 M
-        //          tiles of block j, issued at the start of iteration j - 1;
-        //   G2(j): the other A rows of block j + 1 and the W tile of block
-        //          j + 2, issued in the middle of iteration j.
+        //   G1(j): the A rows of every wave's first kTM / 2 M tiles of block
+        //          j, issued at the start of iteration j - 1;
+        //   G2(j): the other A rows of block j + 1, and the W tile and the
+        //          scales of block j + 2, issued in the middle of iteration j.
         // Iteration kb: issue G1(kb + 1) into the other stage (free: every
         // wave finished block kb - 1 before the last barrier); compute the
         // first M tiles of block kb; wait for G2(kb - 1) (only the kG1 newer
@@ -452,12 +471,13 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         // W region of this stage is free: every wave holds block kb's W
         // fragments in registers since before the last barrier); compute the
         // other M tiles, reloading each W fragment for block kb + 1 (landed
-        // with G2(kb - 1)) right after its last MFMA in block kb; wait for
+        // with G2(kb - 1)) right after its last MFMA in block kb and reading
+        // block kb + 1's scales (also in G2(kb - 1)) in the last row; wait for
         // G1(kb + 1) (kG2 newer copies may stay outstanding) and meet at a
         // barrier.  Each group has one block of compute to land.
         constexpr int kAHalf = C::kALoads / 2;
-        constexpr int kG1 = kAHalf + 1;  // per wave, without a scale chunk
-        constexpr int kG2 = C::kALoads - kAHalf + C::kBLoads;
+        constexpr int kG1 = kAHalf;
+        constexpr int kG2 = C::kALoads - kAHalf + C::kBLoads + 1;  // without a scale chunk
         static_assert((C::WM / 2) % (8 * C::kWaves) == 0 && C::kTM % 2 == 0, "split block");
         // Blocks past the end are copied from empty buffers (every lane out of
         // bounds: nothing is read, zeros land in regions no block uses) so
@@ -474,21 +494,25 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             t.sw = in ? op.sw : none.sw;
             return t;
         };
-        issue(op, kb0, 0, -1, true);
+        issue(op, kb0, 0);
         issue_w(src_for(kb0 + 1), kb0 + 1, 1);
+        issue_scales(src_for(kb0 + 1), kb0 + 1, 1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) wfr[j] = wfrag(0, j);
+        load_scales(0, kb0, sc, swj);
         for (int kb = kb0; kb < kb1; ++kb) {
             const int st = (kb - kb0) & 1;
             const TileOperands next = src_for(kb + 1);
-            issue(next, kb + 1, st ^ 1, 0, false);
+            issue_a(next, kb + 1, st ^ 1, 0);
             compute(st, kb, [&] {
                 asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kG1) : "memory");
                 __syncthreads();
                 issue_a(next, kb + 1, st ^ 1, 1);
-                issue_w(src_for(kb + 2), kb + 2, st);
+                const TileOperands next2 = src_for(kb + 2);
+                issue_w(next2, kb + 2, st);
+                issue_scales(next2, kb + 2, st);
             });
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kG2) : "memory");
             __syncthreads();
@@ -501,7 +525,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         // may still be outstanding.
         constexpr int D = C::kStages - 1;
         for (int d = 0; d < D; ++d)
-            if (kb0 + d < kb1) issue(op, kb0 + d, d, -1, true);
+            if (kb0 + d < kb1) issue(op, kb0 + d, d);
         for (int kb = kb0; kb < kb1; ++kb) {
             const int i = kb - kb0;
             if (kb + D - 1 < kb1)
@@ -509,7 +533,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             else
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            if (kb + D < kb1) issue(op, kb + D, (i + D) % C::kStages, -1, true);
+            if (kb + D < kb1) issue(op, kb + D, (i + D) % C::kStages);
             compute(i % C::kStages, kb, [] {});
         }
     }
