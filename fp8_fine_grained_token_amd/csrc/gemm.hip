@@ -392,7 +392,14 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     // MFMA on it, and reads the next block's scales during its last row.
     v8i wfr[C::kTN];
     float sc[C::kTM], swj[C::kTN];
-    auto compute = [&](int s, int kb, auto &&mid) {
+    v8i af_carry;  // two stages: the next block's first token fragment
+    auto afrag_at = [&](int s, int i) {
+        const uint8_t *la = L.stages[s].a + a_base;
+        const uint4 lo = *reinterpret_cast<const uint4 *>(la + i * 2048 + frag0);
+        const uint4 hi = *reinterpret_cast<const uint4 *>(la + i * 2048 + frag1);
+        return make_v8i(lo, hi);
+    };
+    auto compute = [&](int s, int kb, auto &&mid, auto &&end) {
         constexpr bool kSplit = C::kStages == 2;
         const uint8_t *la = L.stages[s].a + a_base;
         if constexpr (!kSplit) {
@@ -423,19 +430,28 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             acc[i][j][2] = __builtin_fmaf(p[2], f, acc[i][j][2]);
             acc[i][j][3] = __builtin_fmaf(p[3], f, acc[i][j][3]);
         };
-        v8i af = afrag(0);
+        v8i af;
+        if constexpr (kSplit)
+            af = af_carry;
+        else
+            af = afrag(0);
         v4f p_prev{};
         int pi = -1, pj = 0;
 #pragma unroll
         for (int i = 0; i < C::kTM; ++i) {
-            if (kSplit && i == C::kTM / 2) {
-                mid();  // the second half of the block's A rows is in LDS from here
-                af = afrag(i);
-            }
-            // the next token fragment is read one row of tiles ahead, but not
-            // across the middle of a split block
-            const bool ahead = i + 1 < C::kTM && !(kSplit && i + 1 == C::kTM / 2);
-            const v8i af_next = afrag(ahead ? i + 1 : i);
+            // With two stages the barriers come one row early: the row's token
+            // fragment is already in registers, and the next one (first of
+            // the second half, or the next block's first) is read while the
+            // row's MFMAs run.
+            if (kSplit && i == C::kTM / 2 - 1) mid();  // second half of A in LDS from here
+            if (kSplit && i == C::kTM - 1) end();      // next block's first half in LDS
+            v8i af_next;
+            if (i + 1 < C::kTM)
+                af_next = afrag(i + 1);
+            else if (kSplit)
+                af_next = afrag_at(s ^ 1, 0);
+            else
+                af_next = af;
             if (kSplit && i == C::kTM - 1) load_scales(s ^ 1, kb + 1, sc_next, swj_next);
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j) {
@@ -450,6 +466,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         }
         promote(pi, pj, p_prev);
         if constexpr (kSplit) {
+            af_carry = af;
 #pragma unroll
             for (int i = 0; i < C::kTM; ++i) sc[i] = sc_next[i];
 #pragma unroll
@@ -460,21 +477,23 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     if constexpr (C::kStages == 2) {
         // Two stages, each block's copies in two groups so that the copy pipe
         // never drains at a barrier:
-        //   G1(j): the A rows of every wave's first kTM / 2 M tiles of block
-        //          j, issued at the start of iteration j - 1;
+        //   G1(j): the A rows of every wave's first kTM / 2 M tiles of block j;
         //   G2(j): the other A rows of block j + 1, and the W tile and the
-        //          scales of block j + 2, issued in the middle of iteration j.
-        // Iteration kb: issue G1(kb + 1) into the other stage (free: every
-        // wave finished block kb - 1 before the last barrier); compute the
-        // first M tiles of block kb; wait for G2(kb - 1) (only the kG1 newer
-        // copies may stay outstanding) and meet at a barrier; issue G2(kb) (the
-        // W region of this stage is free: every wave holds block kb's W
-        // fragments in registers since before the last barrier); compute the
-        // other M tiles, reloading each W fragment for block kb + 1 (landed
-        // with G2(kb - 1)) right after its last MFMA in block kb and reading
-        // block kb + 1's scales (also in G2(kb - 1)) in the last row; wait for
-        // G1(kb + 1) (kG2 newer copies may stay outstanding) and meet at a
-        // barrier.  Each group has one block of compute to land.
+        //          scales of block j + 2.
+        // Block kb (stage st) runs as: rows 0 .. kTM/2 - 2; wait for G2(kb - 1)
+        // (only the kG1 newer copies may stay outstanding), barrier, issue
+        // G2(kb); rows kTM/2 - 1 .. kTM - 2; wait for G1(kb + 1) (kG2 newer
+        // copies may stay outstanding), barrier, issue G1(kb + 2); row kTM - 1.
+        // Each barrier comes one row before the data it guards is needed, so
+        // the next token fragment is read while that row's MFMAs run.  In the
+        // last row each W fragment of block kb + 1 (landed with G2(kb - 1)) is
+        // reloaded right after its last MFMA in block kb, and block kb + 1's
+        // scales and first token fragment are read.  Reuse is safe: G2(kb)
+        // overwrites the other stage's second-half A rows (block kb - 1 was
+        // finished before the last barrier) and this stage's W tile and
+        // scales (read into registers during block kb - 1's last row); G1(kb
+        // + 2) overwrites this stage's first-half A rows (rows 0 .. kTM/2 - 1
+        // of block kb are done).  Each group has one block of compute to land.
         constexpr int kAHalf = C::kALoads / 2;
         constexpr int kG1 = kAHalf;
         constexpr int kG2 = C::kALoads - kAHalf + C::kBLoads + 1;  // without a scale chunk
@@ -499,23 +518,28 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         issue_scales(src_for(kb0 + 1), kb0 + 1, 1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+        issue_a(src_for(kb0 + 1), kb0 + 1, 1, 0);  // G1(kb0 + 1)
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) wfr[j] = wfrag(0, j);
         load_scales(0, kb0, sc, swj);
+        af_carry = afrag_at(0, 0);
         for (int kb = kb0; kb < kb1; ++kb) {
             const int st = (kb - kb0) & 1;
-            const TileOperands next = src_for(kb + 1);
-            issue_a(next, kb + 1, st ^ 1, 0);
-            compute(st, kb, [&] {
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kG1) : "memory");
-                __syncthreads();
-                issue_a(next, kb + 1, st ^ 1, 1);
-                const TileOperands next2 = src_for(kb + 2);
-                issue_w(next2, kb + 2, st);
-                issue_scales(next2, kb + 2, st);
-            });
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kG2) : "memory");
-            __syncthreads();
+            compute(
+                st, kb,
+                [&] {
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kG1) : "memory");
+                    __syncthreads();
+                    issue_a(src_for(kb + 1), kb + 1, st ^ 1, 1);
+                    const TileOperands next2 = src_for(kb + 2);
+                    issue_w(next2, kb + 2, st);
+                    issue_scales(next2, kb + 2, st);
+                },
+                [&] {
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kG2) : "memory");
+                    __syncthreads();
+                    issue_a(src_for(kb + 2), kb + 2, st, 0);  // G1(kb + 2)
+                });
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
@@ -534,7 +558,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             if (kb + D < kb1) issue(op, kb + D, (i + D) % C::kStages);
-            compute(i % C::kStages, kb, [] {});
+            compute(i % C::kStages, kb, [] {}, [] {});
         }
     }
 }
