@@ -252,14 +252,13 @@ def main():
     torch.cuda.synchronize()
 
     gemm_t = Timer(torch, args.steps)
-    quant_t = Timer(torch, args.steps)
 
+    # Only the GEMM (the roofline kernel) is bracketed by events inside the
+    # timed steps: every event record is a command between two kernels.  The
+    # quantizer's own time is measured in `parts`.
     def step(timed):
-        if timed:
-            quant_t.start()
         F.fp8_quant_act_1x128(X, qa, sa)
         if timed:
-            quant_t.stop()
             gemm_t.start()
         F.fp8_block_gemm(qa, sa, qw, sw, out_dtype="bf16", c=C)
         if timed:
@@ -289,12 +288,11 @@ def main():
                                "channels x100) + fp8_block_gemm M=4096 N=7168 K=7168 bf16 out",
                    "M": M, "N": N, "K": K, "weights": "128x128-quantized once before timing",
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "dense_gemm_kernel", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": "dense_gemm_two_kind_kernel", "achieved": round(achieved, 2),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                      "traffic": traffic_from_counters(),
-                     "gemm_us": round(gemm_ms * 1e3, 2),
-                     "act_quant_us_in_step": round(quant_t.mean_ms() * 1e3, 2)},
+                     "gemm_us": round(gemm_ms * 1e3, 2)},
     }
     if args.copy_calib:
         result["copy_calibration"] = copy_calibration(torch)
