@@ -191,6 +191,20 @@ def test_gemm_192_wide_tiles_all_columns(out):
     check_gemm(c[torch().from_numpy(rows).cuda()], R, out, f"192-wide tiles {out}")
 
 
+@pytest.mark.parametrize("shape", [(4096, 4096, 128), (4096, 4096, 256), (4096, 7168, 128)])
+def test_gemm_big_tiles_one_or_two_k_blocks(shape):
+    # The two-stage pipeline with one or two K blocks: the copies of blocks
+    # past the end come from empty buffers.  4096 x 4096 runs 256 tiles of
+    # 256 x 256, 4096 x 7168 the two tile widths.
+    M, N, K = shape
+    g = I.gemm_inputs(M, N, K, seed=80 + K)
+    qa, sa, qw, sw = quantize(g)
+    c = run_gemm(qa, sa, qw, sw, "f32")
+    rows = np.array([0, 17, 255, 256, 1000, 2047, 2048, 4095])
+    R = oracle.block_gemm(qa, sa, qw, sw, rows)
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, "f32", f"big tiles {M}x{N}x{K}")
+
+
 def test_gemm_two_tile_widths_metamorphic_and_deterministic():
     # 4096 x 7168 runs 256 tiles of 256 x 256 and 256 of 256 x 192: two runs
     # are bitwise identical, and scaling the activation scales by 2^3 scales
