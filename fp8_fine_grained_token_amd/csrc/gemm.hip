@@ -40,6 +40,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kNumXcd = 8;
 
@@ -575,7 +576,11 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 // at piece q ^ (r % 16) (bounded by the row length; rotated by r instead
 // for rows that are not a power of two long), which spreads the 16 rows a
 // wave writes at once over the banks.
-template <class C, int OUT>
+//
+// Final outputs, written once and not read again here, use nontemporal
+// stores; split-K partials (kStream false), read back by the reduction
+// right after, keep the default cache policy.
+template <class C, int OUT, bool kStream = true>
 __device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], TileLds<C> &L,
                                            void *c, int64_t ldc, int64_t row0, int64_t row_end,
                                            int64_t n0, int64_t N) {
@@ -640,8 +645,13 @@ __device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], Til
             // N is a multiple of 128: a 16-byte piece is all in or all out
             if (grow < row_end && gcol < N) {
                 const uint4 v = *reinterpret_cast<const uint4 *>(buf + lds_off(r, cb));
-                *reinterpret_cast<uint4 *>(static_cast<uint8_t *>(c) + (grow * ldc + gcol) * kOB) =
-                    v;
+                u32x4 *dst = reinterpret_cast<u32x4 *>(static_cast<uint8_t *>(c) +
+                                                       (grow * ldc + gcol) * kOB);
+                const u32x4 w = {v.x, v.y, v.z, v.w};
+                if (kStream)
+                    __builtin_nontemporal_store(w, dst);
+                else
+                    *dst = w;
             }
         }
     }
@@ -697,8 +707,8 @@ __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
     const int wn = (threadIdx.x >> 6) % C::kWavesN;
     tile_mainloop<C>(op, p.K, p.G, kb0, kb1, (int)(n0 & 127) + wn * C::WN, lds, acc);
     if (OUT == kOutPartial)
-        tile_store<C, kOutF32>(acc, lds, p.partial + (int64_t)ks * p.M * p.N, p.N, row0, p.M, n0,
-                               p.N);
+        tile_store<C, kOutF32, false>(acc, lds, p.partial + (int64_t)ks * p.M * p.N, p.N, row0,
+                                      p.M, n0, p.N);
     else
         tile_store<C, OUT>(acc, lds, p.c, p.N, row0, p.M, n0, p.N);
 }
