@@ -20,8 +20,11 @@ Printed as one JSON line, with:
   * cpu_baseline: the CPU oracle timed on this host on a bounded sample of
     the same step (first 256 tokens).
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+Usage: python bench.py [--gpus 1] [--steps 500] [--warmup 300]
        [--no-parts] [--no-cpu-baseline] [--copy-calib]
+The default warmup (~70 ms of steps) lets the GPU reach its sustained clock
+before timing; with a few warmup steps the timed region starts while the
+clock is still ramping up after input generation, and reads ~20% slow.
 """
 from __future__ import annotations
 
@@ -221,8 +224,8 @@ def cpu_baseline(I, X_bits, w_bits):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-parts", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")

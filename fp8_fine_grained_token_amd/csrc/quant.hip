@@ -103,7 +103,8 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_flat_kernel(
         o.z = w2;
         o.w = w3;
         if (in) {
-            __builtin_nontemporal_store(o, q + c);
+            // default cache policy: the GEMM that follows reads q back
+            q[c] = o;
             if ((threadIdx.x & 7) == 0) scales[c >> 3] = s;
         }
     }
