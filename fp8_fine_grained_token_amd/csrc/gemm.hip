@@ -16,10 +16,11 @@
 //
 // Structure of one workgroup tile (BM x BN, K stepped 128 at a time):
 //   - A (BM x 128 bytes) and W (BN x 128 bytes) tiles plus the weight
-//     scales of the K block are staged in LDS by direct global->LDS copies:
-//     the next block's copies are in flight while the MFMAs of the current
-//     one run; one barrier per K block.  The tile's activation scales are
-//     fetched eight K blocks at a time into a separate double buffer.
+//     scales of the K block are staged in LDS by direct global->LDS copies
+//     (weights with the nontemporal cache policy), issued one or more blocks
+//     ahead of the MFMAs that use them (see tile_mainloop).  The tile's
+//     activation scales are fetched eight K blocks at a time into a separate
+//     double buffer.
 //   - LDS rows are 128 bytes; 16-byte chunk j of row r is stored at chunk
 //     j ^ key(r), so the MFMA operand reads (16 rows x 32 bytes per lane
 //     group) are bank-conflict free.
@@ -28,6 +29,7 @@
 //   - blockIdx is remapped so that each XCD (hardware dispatches consecutive
 //     workgroups round-robin over the 8 XCDs, each with its own L2) works on
 //     a contiguous, compact range of output tiles.
+//   - The output tile leaves through LDS in whole 128-byte lines.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -245,13 +247,14 @@ __device__ __forceinline__ TileOperands tile_operands(const uint8_t *a, const fl
 // Runs K blocks [kb0, kb1) of one BM x BN tile and leaves the FP32
 // accumulators in acc.
 //
-// Pipeline over kStages LDS stages.  With two stages, an iteration issues the
-// direct global->LDS copies of the next K block into the other stage, runs
-// the current block from LDS (the weight fragments, then one token fragment
-// per 16-row tile, each followed by its MFMAs and promotion FMAs), then waits
-// for its copies and meets the other waves at one barrier, so the copies
-// overlap the whole MFMA phase (in two halves, see below).  With S >= 3
-// stages the copies run D = S - 1 blocks ahead: an iteration waits until at
+// Pipeline over kStages LDS stages.  A block is computed row of 16-row tiles
+// by row: each row's token fragment, then its MFMAs with the weight
+// fragments, each followed by the promotion FMAs of the previous MFMA.  With
+// two stages the copies of a block go in two groups issued half a block
+// apart, with a barrier before each group's data is used, and the next
+// block's weight fragments and scales are read during the current block's
+// last row (details at the loop below).  With S >= 3 stages the copies run
+// D = S - 1 blocks ahead: an iteration waits until at
 // most the copies of the D - 1 newer blocks are outstanding, meets the
 // others at a barrier, issues block kb + D into the stage last read in
 // iteration kb - 1 and computes block kb.  Every wave issues the same
@@ -308,8 +311,8 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         lds_addr(reinterpret_cast<const uint8_t *>(&L.chunks.v[0][0][0][0]) + 1024 * wave);
 
     // Copy t of A fills tile rows [8 kWaves t, +8 kWaves); with two stages
-    // the copies of a block go in two halves: the rows of every wave's first
-    // kTM / 2 M tiles (with W and the scales), then the rest (see below).
+    // a block's A rows go in two halves: the rows of every wave's first
+    // kTM / 2 M tiles, then the rest (see below).
     auto a_copy_in_half = [&](int t, int half) {
         return ((((8 * C::kWaves * t) % C::WM) < C::WM / 2) ? 0 : 1) == half;
     };
@@ -328,8 +331,6 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         for (int t = 0; t < C::kBLoads; ++t)
             copy16_nt(src.w, wave_voff + t * rowstep, soff, lds_b0 + so + 1024 * C::kWaves * t);
     };
-    // block kb's scales, its A rows (all, or one half if a_half >= 0) and,
-    // if with_w, its W tile
     // block kb's scales: its activation-scale chunk if one starts there, and
     // its weight scales
     auto issue_scales = [&](const TileOperands &src, int kb, int st) {
@@ -364,7 +365,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     // fragment as its B operand, so it produces the transposed 16x16 tile
     // D[n][m]: lane L holds outputs n = 4 (L / 16) + e (e < 4), m = L % 16.
     // The activation scale is then one value per lane per M tile and the
-    // weight scale one value per wave.
+    // weight scale one value per wave (or per fragment, see kWaveInOneBlock).
     auto wfrag = [&](int s, int j) {
         const uint8_t *lb = L.stages[s].b + b_base;
         const uint4 lo = *reinterpret_cast<const uint4 *>(lb + j * 2048 + frag0);
