@@ -659,9 +659,11 @@ __device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], Til
 }
 
 // Tile shapes: 256 x 256 on 8 waves (wave tile 128 x 64, two LDS stages)
-// for GEMMs that fill the GPU; 128 x 128 on 4 waves (wave tile 64 x 64,
+// for GEMMs that fill the GPU; 128 x 64 on 4 waves (wave tile 64 x 32,
 // four stages: copies three K blocks ahead) for small ones, with split-K when
-// even those tiles cannot occupy the 256 CUs; 128 x 256 on 8 waves (wave
+// even those tiles cannot occupy the 256 CUs (narrower tiles need half the
+// splits, so half the partial sums, than 128 x 128 ones for the same
+// occupancy); 128 x 256 on 8 waves (wave
 // tile 64 x 64, three stages) for the grouped GEMM, whose experts' token
 // counts make 128-row granularity worth keeping.
 using BigTile = TileCfg<256, 256, 2, 4, 2>;
@@ -669,7 +671,7 @@ using BigTile = TileCfg<256, 256, 2, 4, 2>;
 // when 256 x 256 tiles alone would leave a partly filled last round (see
 // plan_two_kind).
 using NarrowTile = TileCfg<256, 192, 2, 4, 2>;
-using SmallTile = TileCfg<128, 128, 2, 2, 4>;
+using SmallTile = TileCfg<128, 64, 2, 2, 4>;
 using MidTile = TileCfg<128, 256, 2, 4, 3>;
 
 // Logical tile index of this workgroup after the XCD remap (gridDim.x is a
@@ -775,16 +777,26 @@ __global__ __launch_bounds__(BigTile::kThreads) void dense_gemm_two_kind_kernel(
 
 // Split-K reduction: C = sum over splits in fixed order 0..S-1, then the
 // output conversion.  Four elements per thread (M*N is a multiple of 128).
+// The partials are loaded eight splits at a time before any is added, so
+// their latencies overlap instead of adding up (indexes past S - 1 re-read
+// split S - 1 and are not added).
 template <int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ partial,
                                                             void *__restrict__ c, int64_t MN,
                                                             int S) {
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= MN) return;
-    float4 s = *reinterpret_cast<const float4 *>(partial + i);
-    for (int k = 1; k < S; ++k) {
-        const float4 v = *reinterpret_cast<const float4 *>(partial + (int64_t)k * MN + i);
-        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    auto load = [&](int k) { return *reinterpret_cast<const float4 *>(partial + (int64_t)k * MN + i); };
+    float4 s = load(0);
+    for (int k0 = 1; k0 < S; k0 += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = load(k0 + j < S ? k0 + j : S - 1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (k0 + j < S) {
+                s.x += v[j].x; s.y += v[j].y; s.z += v[j].z; s.w += v[j].w;
+            }
     }
     if (OUT == kOutBF16) {
         uint2 o;
@@ -918,7 +930,7 @@ Plan plan_dense(int64_t M, int64_t N, int64_t K) {
         }
         return pl;
     }
-    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t tiles = ((M + SmallTile::BM - 1) / SmallTile::BM) * ((N + SmallTile::BN - 1) / SmallTile::BN);
     int s = 1;
     // Split K only when the output tiles cannot fill the CUs and each split
     // keeps at least 4 K blocks.
