@@ -811,7 +811,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 // Grouped GEMM.  Logical tiles are ordered expert by expert; inside an
 // expert, N tile by N tile, and the expert's M tiles are consecutive, so the
 // M tiles that share one W tile run next to each other on one XCD.  The
-// offsets live on the device: thread 0 walks them, counts the real tiles R,
+// offsets live on the device: the first wave scans them (64 experts per
+// step), counts the real tiles R,
 // gives each XCD a contiguous range of ceil(R / 8) of them (the grid is
 // sized for the worst case (ceil(T / BM) + E) * tiles_n, so sizing the
 // ranges by the grid would leave the last XCDs idle) and finds this tile's
@@ -824,47 +825,88 @@ template <class C, int OUT>
 __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p) {
     __shared__ TileLds<C> lds;
     __shared__ int64_t info[4];
-    if (threadIdx.x == 0) {
-        auto clamp_t = [&](int64_t v) { return v < 0 ? (int64_t)0 : (v > p.M ? p.M : v); };
-        // rows [lo, hi) of expert e, given the previous expert's end `prev`
-        auto range = [&](int e, int64_t prev, int64_t &lo, int64_t &hi) {
-            lo = clamp_t(p.offsets[e]);
-            lo = lo > prev ? lo : prev;
-            hi = clamp_t(p.offsets[e + 1]);
-            hi = hi > lo ? hi : lo;
+    if (threadIdx.x < 64) {
+        // Wave 0 finds this workgroup's tile.  Expert e's rows are
+        // [PM(e), PM(e + 1)) with PM(i) = max_{j <= i} clamp(off[j]): the
+        // ranges above unrolled (hi_e is the running maximum of the clamped
+        // offsets up to off[e + 1], and lo_e the one up to off[e]).  Lane l
+        // of a chunk handles expert e0 + l: a prefix maximum across the
+        // lanes gives PM, a prefix sum the tile counts before each expert.
+        const int lane = threadIdx.x;
+        const int T = (int)p.M;
+        const int E = p.E;
+        auto clamped = [&](int i) {
+            const int v = p.offsets[i];
+            return v < 0 ? 0 : (v > T ? T : v);
         };
-        int64_t total = 0;
+        struct Chunk {
+            int lo, hi, incl, own;  // expert rows [lo, hi); tiles up to and of this expert
+        };
+        auto chunk = [&](int e0, int carry_hi) {
+            const int e = e0 + lane;
+            Chunk c;
+            c.hi = e < E ? clamped(e + 1) : 0;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int t = __shfl_up(c.hi, d);
+                if (lane >= d) c.hi = t > c.hi ? t : c.hi;
+            }
+            c.hi = carry_hi > c.hi ? carry_hi : c.hi;
+            c.lo = __shfl_up(c.hi, 1);
+            if (lane == 0) c.lo = carry_hi;
+            c.own = e < E ? (c.hi - c.lo + C::BM - 1) / C::BM * p.tiles_n : 0;
+            c.incl = c.own;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int t = __shfl_up(c.incl, d);
+                if (lane >= d) c.incl += t;
+            }
+            return c;
+        };
+        const int pm0 = E > 0 ? clamped(0) : 0;
+        Chunk first{};
+        int total = 0;
         {
-            int64_t lo, hi = 0;
-            for (int e = 0; e < p.E; ++e) {
-                range(e, hi, lo, hi);
-                total += (hi - lo + C::BM - 1) / C::BM * p.tiles_n;
+            int carry = pm0;
+            for (int e0 = 0; e0 < E; e0 += 64) {
+                const Chunk c = chunk(e0, carry);
+                if (e0 == 0) first = c;
+                total += __shfl(c.incl, 63);
+                carry = __shfl(c.hi, 63);
             }
         }
-        const int64_t per = (total + kNumXcd - 1) / kNumXcd;
-        const int64_t slot = blockIdx.x / kNumXcd;
-        int64_t rem = (blockIdx.x % kNumXcd) * per + slot;
+        const int per = (total + kNumXcd - 1) / kNumXcd;
+        const int slot = (int)blockIdx.x / kNumXcd;
+        const int rem = ((int)blockIdx.x % kNumXcd) * per + slot;
         int64_t e_hit = -1, r0 = 0, r1 = 0, tn = 0;
         if (slot < per && rem < total) {
-            int64_t lo, hi = 0;
-            for (int e = 0; e < p.E; ++e) {
-                range(e, hi, lo, hi);
-                const int64_t mt = (hi - lo + C::BM - 1) / C::BM;
-                const int64_t tiles = mt * p.tiles_n;
-                if (rem < tiles) {
-                    e_hit = e;
-                    tn = rem / mt;
-                    r0 = lo + (rem - tn * mt) * C::BM;
+            int carry = pm0, base = 0;
+            for (int e0 = 0; e0 < E; e0 += 64) {
+                const Chunk c = e0 == 0 ? first : chunk(e0, carry);
+                const int r = rem - base;
+                const unsigned long long hit =
+                    __ballot(c.own > 0 && r >= c.incl - c.own && r < c.incl);
+                if (hit) {
+                    const int h = __builtin_ctzll(hit);
+                    const int lo = __shfl(c.lo, h), hi = __shfl(c.hi, h);
+                    const int local = r - (__shfl(c.incl, h) - __shfl(c.own, h));
+                    const int mt = (hi - lo + C::BM - 1) / C::BM;
+                    e_hit = e0 + h;
+                    tn = local / mt;
+                    r0 = lo + (int64_t)(local - tn * mt) * C::BM;
                     r1 = hi;
                     break;
                 }
-                rem -= tiles;
+                base += __shfl(c.incl, 63);
+                carry = __shfl(c.hi, 63);
             }
         }
-        info[0] = e_hit;
-        info[1] = r0;
-        info[2] = r1;
-        info[3] = tn;
+        if (lane == 0) {
+            info[0] = e_hit;
+            info[1] = r0;
+            info[2] = r1;
+            info[3] = tn;
+        }
     }
     __syncthreads();
     const int64_t e = info[0];
