@@ -194,13 +194,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // orders every LDS read after all outstanding LDS-DMA copies it knows of,
 // which would serialize the next block's copy with this block's MFMAs.
 // These instructions have no register results; the data they write is read
-// only after the explicit "s_waitcnt vmcnt(0)" and barrier that end each
-// main-loop iteration.
+// only after an explicit "s_waitcnt vmcnt" that covers the copy and a
+// barrier (see tile_mainloop).
+//
+// M0 is reserved to the compiler, so each copy saves it in a scratch SGPR,
+// sets the LDS address, issues the load (which takes M0 at issue: copies
+// back to back with different addresses land where they should) and puts
+// the old value back.
 __device__ __forceinline__ void copy16(const v4i &r, uint32_t voff, uint32_t soff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-                 :
-                 : "v"(voff), "s"(r), "s"(soff), "s"(lds)
-                 : "memory", "m0");
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(r), "s"(soff), "s"(lds)
+        : "memory");
 }
 // The same copy with the nontemporal cache policy, for the weight tiles:
 // streamed from HBM, plain copies of this pattern top out near 2.6 TB/s
@@ -209,16 +217,22 @@ __device__ __forceinline__ void copy16(const v4i &r, uint32_t voff, uint32_t sof
 // the default policy.
 __device__ __forceinline__ void copy16_nt(const v4i &r, uint32_t voff, uint32_t soff,
                                           uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen nt lds"
-                 :
-                 : "v"(voff), "s"(r), "s"(soff), "s"(lds)
-                 : "memory", "m0");
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen nt lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(r), "s"(soff), "s"(lds)
+        : "memory");
 }
 __device__ __forceinline__ void copy4(const v4i &r, uint32_t voff, uint32_t soff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dword %0, %1, %2 offen lds"
-                 :
-                 : "v"(voff), "s"(r), "s"(soff), "s"(lds)
-                 : "memory", "m0");
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\t"
+        "buffer_load_dword %1, %2, %3 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(r), "s"(soff), "s"(lds)
+        : "memory");
 }
 
 // Per-tile operand view for the main loop.  Rows [row0, row0 + rows) of A

@@ -147,6 +147,25 @@ def test_gemm_decode_workload_with_and_without_workspace():
     check_gemm(c3, R, "f32", "decode split-K f32")
 
 
+@pytest.mark.parametrize("M,N,K,splits", [(128, 128, 8192, 16), (100, 256, 2688, 4)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_gemm_split_k_many_and_uneven_splits(M, N, K, splits, out):
+    """Split-K with more than eight splits (the reduction gathers partials
+    eight at a time) and with a last split shorter than the others (21 K
+    blocks over 4 splits of 6); the workspace size shows the split count."""
+    g = I.gemm_inputs(M, N, K, seed=M + N + K, outlier_frac=0.01, outlier_mult=20.0)
+    qa, sa, qw, sw = quantize(g)
+    R = oracle.block_gemm(qa, sa, qw, sw)
+    t = torch()
+    nbytes = B.fp8_gemm_workspace_bytes(M, N, K, out)
+    assert nbytes == splits * M * N * 4, f"{M}x{N}x{K}: workspace {nbytes} B"
+    ws = t.empty(nbytes, dtype=t.uint8, device="cuda")
+    c1 = run_gemm(qa, sa, qw, sw, out, workspace=ws)
+    c2 = run_gemm(qa, sa, qw, sw, out, workspace=ws)
+    check_gemm(c1, R, out, f"split-K x{splits} {M}x{N}x{K} {out}")
+    assert t.equal(c1, c2), "split-K result changed between identical calls"
+
+
 def test_gemm_dense_workload_sampled_rows():
     g = I.config_dense(seed=0)
     qa, sa, qw, sw = quantize(g)
