@@ -16,7 +16,8 @@ Printed as one JSON line, with:
   * parts: each kernel on its own workload with the caches flushed before
     every launch (act quantizer GB/s vs HBM, beside a plain device copy of
     the same byte count; dense / decode / grouped GEMM TFLOP/s vs MFMA and
-    GB/s vs HBM);
+    GB/s vs HBM), and the power-of-two-scale variants (quantizer, dense and
+    grouped GEMM on the block-scaled MFMA) on the same workloads;
   * cpu_baseline: the CPU oracle timed on this host on a bounded sample of
     the same step (first 256 tokens).
 
@@ -106,7 +107,7 @@ def to_dev_bf16(torch, bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def measure_parts(torch, F, I, X, qa, sa, qw, sw, C, iters=20):
+def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
     """Each kernel on its own workload.  Before every launch a 512 MB buffer
     is read (twice the 256 MB Infinity Cache), so operands come from HBM; a
     read leaves no dirty lines whose write-back would land in the timed
@@ -146,6 +147,18 @@ def measure_parts(torch, F, I, X, qa, sa, qw, sw, C, iters=20):
     fl = 2 * M * N * K
     parts["dense_gemm_4096x7168x7168"] = {
         "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
+
+    # power-of-two scales: quantizer and dense GEMM on the same workload
+    pa, psa = F.fp8_quant_act_1x128_pow2(X)
+    pw, psw = F.fp8_quant_weight_128x128_pow2(Wb)
+    ms = timed(lambda: F.fp8_quant_act_1x128_pow2(X, pa, psa), iters)
+    b = quant_bytes(M, K)
+    parts["pow2_act_quant_4096x7168"] = {
+        "us": ms * 1e3, "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+    ms = timed(lambda: F.fp8_block_gemm_pow2(pa, psa, pw, psw, out_dtype="bf16", c=C), iters)
+    parts["pow2_dense_gemm_4096x7168x7168"] = {
+        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
+    del pa, psa, pw, psw
 
     # decode GEMM, 256 x 2048 x 7168 (split-K with workspace)
     gd = I.config_decode(seed=0)
@@ -188,6 +201,22 @@ def measure_parts(torch, F, I, X, qa, sa, qw, sw, C, iters=20):
         "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
         "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
         "counts": [int(c) for c in gi.counts]}
+    del gq, gsa, gw, gsw
+
+    # the same grouped workload with power-of-two scales
+    ga = to_dev_bf16(torch, gi.a_bf16)
+    gq, gsa = F.fp8_quant_act_1x128_pow2(ga)
+    del ga
+    gwb = to_dev_bf16(torch, gi.w_bf16.reshape(gi.E * gi.N, gi.K))
+    gw, gsw = F.fp8_quant_weight_128x128_pow2(gwb)
+    del gwb
+    gw = gw.view(gi.E, gi.N, gi.K)
+    gsw = gsw.view(gi.E, gi.N // 128, gi.K // 128)
+    ms = timed(lambda: F.fp8_block_grouped_gemm_pow2(gq, gsa, gw, gsw, off, out_dtype="bf16",
+                                                     c=gc), iters)
+    parts["pow2_grouped_gemm_e32_t8192_n4096_k7168"] = {
+        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
+        "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
     del gq, gsa, gw, gsw, gc, flush
     torch.cuda.empty_cache()
     return parts
@@ -301,7 +330,7 @@ def main():
         result["copy_calibration"] = copy_calibration(torch)
     if not args.no_parts:
         log("bench: per-kernel parts ...")
-        result["parts"] = measure_parts(torch, F, I, X, qa, sa, qw, sw, C)
+        result["parts"] = measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C)
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline ...")
         result["cpu_baseline"] = cpu_baseline(I, X_bits, w_bits)

@@ -9,9 +9,10 @@ Two layers:
   * ``lib()`` returns the ctypes handle with typed signatures of the C
     functions (raw device pointers, sizes, stream handle);
   * ``fp8_quant_act_1x128``, ``fp8_quant_weight_128x128``,
-    ``fp8_block_gemm`` and ``fp8_block_grouped_gemm`` take torch tensors on
-    the GPU, allocate outputs when not given, call the C function on
-    ``torch.cuda.current_stream()`` and raise ``Fp8Error`` on a nonzero
+    ``fp8_block_gemm`` and ``fp8_block_grouped_gemm`` (and their ``_pow2``
+    forms, power-of-two scales for the block-scaled matrix core) take torch
+    tensors on the GPU, allocate outputs when not given, call the C function
+    on ``torch.cuda.current_stream()`` and raise ``Fp8Error`` on a nonzero
     status.
 """
 from __future__ import annotations
@@ -45,6 +46,12 @@ _SIGNATURES = {
                                 _I64, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "fp8_gemm_workspace_bytes": ([_I64, _I64, _I64, ctypes.c_int], ctypes.c_size_t),
     "fp8_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "fp8_quant_act_1x128_pow2": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "fp8_quant_weight_128x128_pow2": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "fp8_block_gemm_pow2": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P,
+                        ctypes.c_size_t, _P], ctypes.c_int),
+    "fp8_block_grouped_gemm_pow2": ([_P, _P, _P, _P, _P, _I64, _I64, _P, ctypes.c_int,
+                                _I64, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
 }
 
 _lock = threading.Lock()
@@ -120,8 +127,7 @@ def _out_code(out_dtype):
     raise ValueError(f"unsupported out_dtype {out_dtype}")
 
 
-def fp8_quant_act_1x128(x, q=None, scales=None, stream=None):
-    """x: bf16 [M][K] -> (q uint8 [M][K] E4M3, scales fp32 [M][ceil(K/128)])."""
+def _quant_act(fn, x, q, scales, stream):
     torch = _torch()
     M, K = x.shape
     G = (K + 127) // 128
@@ -129,14 +135,22 @@ def fp8_quant_act_1x128(x, q=None, scales=None, stream=None):
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((M, G), dtype=torch.float32, device=x.device)
-    _check(lib().fp8_quant_act_1x128(_dev(x, "x", torch.bfloat16), M, K, _dev(q, "q", torch.uint8),
-                                     _dev(scales, "scales", torch.float32),
-                                     _stream_handle(stream)), "fp8_quant_act_1x128")
+    _check(getattr(lib(), fn)(_dev(x, "x", torch.bfloat16), M, K, _dev(q, "q", torch.uint8),
+                              _dev(scales, "scales", torch.float32), _stream_handle(stream)), fn)
     return q, scales
 
 
-def fp8_quant_weight_128x128(w, q=None, scales=None, stream=None):
-    """w: bf16 [N][K] -> (q uint8 [N][K], scales fp32 [ceil(N/128)][ceil(K/128)])."""
+def fp8_quant_act_1x128(x, q=None, scales=None, stream=None):
+    """x: bf16 [M][K] -> (q uint8 [M][K] E4M3, scales fp32 [M][ceil(K/128)])."""
+    return _quant_act("fp8_quant_act_1x128", x, q, scales, stream)
+
+
+def fp8_quant_act_1x128_pow2(x, q=None, scales=None, stream=None):
+    """As fp8_quant_act_1x128 with power-of-two scales."""
+    return _quant_act("fp8_quant_act_1x128_pow2", x, q, scales, stream)
+
+
+def _quant_weight(fn, w, q, scales, stream):
     torch = _torch()
     N, K = w.shape
     if q is None:
@@ -144,11 +158,19 @@ def fp8_quant_weight_128x128(w, q=None, scales=None, stream=None):
     if scales is None:
         scales = torch.empty(((N + 127) // 128, (K + 127) // 128), dtype=torch.float32,
                              device=w.device)
-    _check(lib().fp8_quant_weight_128x128(_dev(w, "w", torch.bfloat16), N, K,
-                                          _dev(q, "q", torch.uint8),
-                                          _dev(scales, "scales", torch.float32),
-                                          _stream_handle(stream)), "fp8_quant_weight_128x128")
+    _check(getattr(lib(), fn)(_dev(w, "w", torch.bfloat16), N, K, _dev(q, "q", torch.uint8),
+                              _dev(scales, "scales", torch.float32), _stream_handle(stream)), fn)
     return q, scales
+
+
+def fp8_quant_weight_128x128(w, q=None, scales=None, stream=None):
+    """w: bf16 [N][K] -> (q uint8 [N][K], scales fp32 [ceil(N/128)][ceil(K/128)])."""
+    return _quant_weight("fp8_quant_weight_128x128", w, q, scales, stream)
+
+
+def fp8_quant_weight_128x128_pow2(w, q=None, scales=None, stream=None):
+    """As fp8_quant_weight_128x128 with power-of-two scales."""
+    return _quant_weight("fp8_quant_weight_128x128_pow2", w, q, scales, stream)
 
 
 def fp8_gemm_workspace_bytes(M: int, N: int, K: int, out_dtype="bf16") -> int:
@@ -163,9 +185,7 @@ def _workspace_args(workspace):
     return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
 
 
-def fp8_block_gemm(a, sa, w, sw, out_dtype="bf16", c=None, workspace=None, stream=None):
-    """C[M][N] = block-scaled product of a [M][K] E4M3 (scales [M][K/128]) and
-    w [N][K] E4M3 (scales [N/128][K/128]); bf16 or fp32 output."""
+def _block_gemm(fn, a, sa, w, sw, out_dtype, c, workspace, stream):
     torch = _torch()
     M, K = a.shape
     N = w.shape[0]
@@ -173,17 +193,25 @@ def fp8_block_gemm(a, sa, w, sw, out_dtype="bf16", c=None, workspace=None, strea
     if c is None:
         c = torch.empty((M, N), dtype=tdt, device=a.device)
     wp, wb = _workspace_args(workspace)
-    _check(lib().fp8_block_gemm(_dev(a, "a", torch.uint8), _dev(sa, "sa", torch.float32),
-                                _dev(w, "w", torch.uint8), _dev(sw, "sw", torch.float32),
-                                _dev(c, "c", tdt), code, M, N, K, wp, wb,
-                                _stream_handle(stream)), "fp8_block_gemm")
+    _check(getattr(lib(), fn)(_dev(a, "a", torch.uint8), _dev(sa, "sa", torch.float32),
+                              _dev(w, "w", torch.uint8), _dev(sw, "sw", torch.float32),
+                              _dev(c, "c", tdt), code, M, N, K, wp, wb, _stream_handle(stream)),
+           fn)
     return c
 
 
-def fp8_block_grouped_gemm(a, sa, w, sw, group_offsets, out_dtype="bf16", c=None,
-                           workspace=None, stream=None):
-    """Grouped GEMM over expert-sorted rows: a [T][K], w [E][N][K],
-    sw [E][N/128][K/128], group_offsets int32 [E+1] on the GPU."""
+def fp8_block_gemm(a, sa, w, sw, out_dtype="bf16", c=None, workspace=None, stream=None):
+    """C[M][N] = block-scaled product of a [M][K] E4M3 (scales [M][K/128]) and
+    w [N][K] E4M3 (scales [N/128][K/128]); bf16 or fp32 output."""
+    return _block_gemm("fp8_block_gemm", a, sa, w, sw, out_dtype, c, workspace, stream)
+
+
+def fp8_block_gemm_pow2(a, sa, w, sw, out_dtype="bf16", c=None, workspace=None, stream=None):
+    """As fp8_block_gemm, for power-of-two scales (the block-scaled MFMA)."""
+    return _block_gemm("fp8_block_gemm_pow2", a, sa, w, sw, out_dtype, c, workspace, stream)
+
+
+def _grouped_gemm(fn, a, sa, w, sw, group_offsets, out_dtype, c, workspace, stream):
     torch = _torch()
     T, K = a.shape
     E, N, _ = w.shape
@@ -191,9 +219,23 @@ def fp8_block_grouped_gemm(a, sa, w, sw, group_offsets, out_dtype="bf16", c=None
     if c is None:
         c = torch.empty((T, N), dtype=tdt, device=a.device)
     wp, wb = _workspace_args(workspace)
-    _check(lib().fp8_block_grouped_gemm(_dev(a, "a", torch.uint8), _dev(sa, "sa", torch.float32),
-                                        _dev(w, "w", torch.uint8), _dev(sw, "sw", torch.float32),
-                                        _dev(group_offsets, "group_offsets", torch.int32), E, T,
-                                        _dev(c, "c", tdt), code, N, K, wp, wb,
-                                        _stream_handle(stream)), "fp8_block_grouped_gemm")
+    _check(getattr(lib(), fn)(_dev(a, "a", torch.uint8), _dev(sa, "sa", torch.float32),
+                              _dev(w, "w", torch.uint8), _dev(sw, "sw", torch.float32),
+                              _dev(group_offsets, "group_offsets", torch.int32), E, T,
+                              _dev(c, "c", tdt), code, N, K, wp, wb, _stream_handle(stream)), fn)
     return c
+
+
+def fp8_block_grouped_gemm(a, sa, w, sw, group_offsets, out_dtype="bf16", c=None,
+                           workspace=None, stream=None):
+    """Grouped GEMM over expert-sorted rows: a [T][K], w [E][N][K],
+    sw [E][N/128][K/128], group_offsets int32 [E+1] on the GPU."""
+    return _grouped_gemm("fp8_block_grouped_gemm", a, sa, w, sw, group_offsets, out_dtype, c,
+                         workspace, stream)
+
+
+def fp8_block_grouped_gemm_pow2(a, sa, w, sw, group_offsets, out_dtype="bf16", c=None,
+                                workspace=None, stream=None):
+    """As fp8_block_grouped_gemm, for power-of-two scales."""
+    return _grouped_gemm("fp8_block_grouped_gemm_pow2", a, sa, w, sw, group_offsets, out_dtype,
+                         c, workspace, stream)

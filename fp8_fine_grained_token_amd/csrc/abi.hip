@@ -46,45 +46,41 @@ fp8_status check_gemm_common(const void *a, const float *sa, const void *w, cons
     return FP8_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-fp8_status fp8_quant_act_1x128(const void *x_bf16, int64_t M, int64_t K, void *q_e4m3,
-                               float *scales, void *hip_stream) {
+fp8_status quant_act(const void *x_bf16, int64_t M, int64_t K, void *q_e4m3, float *scales,
+                     bool pow2, void *hip_stream) {
     fp8_status st = check_quant(x_bf16, M, K, q_e4m3, scales);
     if (st != FP8_OK || M == 0 || K == 0) return st;
     if (!aligned(x_bf16, 2) || !aligned(scales, 4)) return FP8_ERR_ALIGN;
-    return from_hip(fp8blk::launch_quant_act_1x128(x_bf16, M, K, q_e4m3, scales,
+    return from_hip(fp8blk::launch_quant_act_1x128(x_bf16, M, K, q_e4m3, scales, pow2,
                                                    as_stream(hip_stream)));
 }
 
-fp8_status fp8_quant_weight_128x128(const void *w_bf16, int64_t N, int64_t K, void *q_e4m3,
-                                    float *scales, void *hip_stream) {
+fp8_status quant_weight(const void *w_bf16, int64_t N, int64_t K, void *q_e4m3, float *scales,
+                        bool pow2, void *hip_stream) {
     fp8_status st = check_quant(w_bf16, N, K, q_e4m3, scales);
     if (st != FP8_OK || N == 0 || K == 0) return st;
     if (!aligned(w_bf16, 2) || !aligned(scales, 4)) return FP8_ERR_ALIGN;
-    return from_hip(fp8blk::launch_quant_weight_128x128(w_bf16, N, K, q_e4m3, scales,
+    return from_hip(fp8blk::launch_quant_weight_128x128(w_bf16, N, K, q_e4m3, scales, pow2,
                                                         as_stream(hip_stream)));
 }
 
-fp8_status fp8_block_gemm(const void *a_e4m3, const float *a_scales, const void *w_e4m3,
-                          const float *w_scales, void *c, int out_dtype, int64_t M, int64_t N,
-                          int64_t K, void *workspace, size_t workspace_bytes, void *hip_stream) {
+fp8_status block_gemm(const void *a_e4m3, const float *a_scales, const void *w_e4m3,
+                      const float *w_scales, void *c, int out_dtype, int64_t M, int64_t N,
+                      int64_t K, void *workspace, size_t workspace_bytes, bool pow2,
+                      void *hip_stream) {
     fp8_status st = check_gemm_common(a_e4m3, a_scales, w_e4m3, w_scales, c, out_dtype, M, N, K,
                                       workspace, workspace_bytes);
     if (st != FP8_OK || M == 0 || N == 0) return st;
     if (K == 0) return FP8_ERR_SHAPE;
     return from_hip(fp8blk::launch_block_gemm(a_e4m3, a_scales, w_e4m3, w_scales, c,
                                               out_dtype == FP8_OUT_BF16, M, N, K, workspace,
-                                              workspace_bytes, as_stream(hip_stream)));
+                                              workspace_bytes, pow2, as_stream(hip_stream)));
 }
 
-fp8_status fp8_block_grouped_gemm(const void *a_e4m3, const float *a_scales,
-                                  const void *w_e4m3, const float *w_scales,
-                                  const int32_t *group_offsets, int64_t E, int64_t T, void *c,
-                                  int out_dtype, int64_t N, int64_t K, void *workspace,
-                                  size_t workspace_bytes, void *hip_stream) {
+fp8_status grouped_gemm(const void *a_e4m3, const float *a_scales, const void *w_e4m3,
+                        const float *w_scales, const int32_t *group_offsets, int64_t E,
+                        int64_t T, void *c, int out_dtype, int64_t N, int64_t K, void *workspace,
+                        size_t workspace_bytes, bool pow2, void *hip_stream) {
     fp8_status st = check_gemm_common(a_e4m3, a_scales, w_e4m3, w_scales, c, out_dtype, T, N, K,
                                       workspace, workspace_bytes);
     if (st != FP8_OK) return st;
@@ -96,8 +92,66 @@ fp8_status fp8_block_grouped_gemm(const void *a_e4m3, const float *a_scales,
     if (!group_offsets) return FP8_ERR_NULL;
     if (!aligned(group_offsets, 4)) return FP8_ERR_ALIGN;
     return from_hip(fp8blk::launch_grouped_gemm(a_e4m3, a_scales, w_e4m3, w_scales, group_offsets,
-                                                E, T, c, out_dtype == FP8_OUT_BF16, N, K,
+                                                E, T, c, out_dtype == FP8_OUT_BF16, N, K, pow2,
                                                 as_stream(hip_stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8_status fp8_quant_act_1x128(const void *x_bf16, int64_t M, int64_t K, void *q_e4m3,
+                               float *scales, void *hip_stream) {
+    return quant_act(x_bf16, M, K, q_e4m3, scales, false, hip_stream);
+}
+
+fp8_status fp8_quant_weight_128x128(const void *w_bf16, int64_t N, int64_t K, void *q_e4m3,
+                                    float *scales, void *hip_stream) {
+    return quant_weight(w_bf16, N, K, q_e4m3, scales, false, hip_stream);
+}
+
+fp8_status fp8_quant_act_1x128_pow2(const void *x_bf16, int64_t M, int64_t K, void *q_e4m3,
+                                    float *scales, void *hip_stream) {
+    return quant_act(x_bf16, M, K, q_e4m3, scales, true, hip_stream);
+}
+
+fp8_status fp8_quant_weight_128x128_pow2(const void *w_bf16, int64_t N, int64_t K,
+                                         void *q_e4m3, float *scales, void *hip_stream) {
+    return quant_weight(w_bf16, N, K, q_e4m3, scales, true, hip_stream);
+}
+
+fp8_status fp8_block_gemm(const void *a_e4m3, const float *a_scales, const void *w_e4m3,
+                          const float *w_scales, void *c, int out_dtype, int64_t M, int64_t N,
+                          int64_t K, void *workspace, size_t workspace_bytes, void *hip_stream) {
+    return block_gemm(a_e4m3, a_scales, w_e4m3, w_scales, c, out_dtype, M, N, K, workspace,
+                      workspace_bytes, false, hip_stream);
+}
+
+fp8_status fp8_block_gemm_pow2(const void *a_e4m3, const float *a_scales, const void *w_e4m3,
+                               const float *w_scales, void *c, int out_dtype, int64_t M,
+                               int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                               void *hip_stream) {
+    return block_gemm(a_e4m3, a_scales, w_e4m3, w_scales, c, out_dtype, M, N, K, workspace,
+                      workspace_bytes, true, hip_stream);
+}
+
+fp8_status fp8_block_grouped_gemm(const void *a_e4m3, const float *a_scales,
+                                  const void *w_e4m3, const float *w_scales,
+                                  const int32_t *group_offsets, int64_t E, int64_t T, void *c,
+                                  int out_dtype, int64_t N, int64_t K, void *workspace,
+                                  size_t workspace_bytes, void *hip_stream) {
+    return grouped_gemm(a_e4m3, a_scales, w_e4m3, w_scales, group_offsets, E, T, c, out_dtype,
+                        N, K, workspace, workspace_bytes, false, hip_stream);
+}
+
+fp8_status fp8_block_grouped_gemm_pow2(const void *a_e4m3, const float *a_scales,
+                                       const void *w_e4m3, const float *w_scales,
+                                       const int32_t *group_offsets, int64_t E, int64_t T,
+                                       void *c, int out_dtype, int64_t N, int64_t K,
+                                       void *workspace, size_t workspace_bytes,
+                                       void *hip_stream) {
+    return grouped_gemm(a_e4m3, a_scales, w_e4m3, w_scales, group_offsets, E, T, c, out_dtype,
+                        N, K, workspace, workspace_bytes, true, hip_stream);
 }
 
 size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int out_dtype) {

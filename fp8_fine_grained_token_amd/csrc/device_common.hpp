@@ -38,6 +38,20 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Power-of-two scale (the block-scaled-MFMA variant): the smallest 2^E with
+// 448 * 2^E >= amax, and at least 2^-126 (so every scale is a normal fp32
+// whose exponent field is its E8M0 code).  With amax = (1 + f) 2^(e - 127)
+// (e the exponent field) and 448 = 1.75 * 2^8, 448 * 2^E >= amax holds from
+// E = e - 135 on when 1 + f <= 1.75, else from e - 134.  Zero or subnormal
+// amax gives the floor.
+__device__ __forceinline__ float scale_pow2(float amax) {
+    const uint32_t b = __float_as_uint(amax);
+    const int e = (int)(b >> 23);  // amax >= 0
+    int E = e - 135 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    E = (e == 0 || E < -126) ? -126 : E;
+    return __uint_as_float((uint32_t)(E + 127) << 23);
+}
+
 // Per-group quotient context.  The quantized value is E4M3_RNE(fl32(x / s)).
 // For amax >= 2^-60 the correctly rounded quotient is obtained from the
 // correctly rounded reciprocal r = fl32(1/s) with one FMA correction
@@ -47,14 +61,24 @@ __device__ __forceinline__ float wave_max(float v) {
 // s) falls back to the IEEE divide.  The sign is taken from x so that -0
 // and tiny negatives keep it.
 // An all-zero group (amax = 0, so s = 0) encodes every element as +0.
+// With power-of-two scales (pow2) r = 1/s is exact, so the FMA quotient is
+// the correctly rounded one for every amax; an all-zero group keeps the
+// floor scale 2^-126 and also encodes as +0.
 struct QuotientCtx {
     float s, r;
     bool fast, zero;
-    __device__ __forceinline__ explicit QuotientCtx(float amax) {
-        s = amax / kE4M3Max;
-        zero = !(s > 0.0f);
-        fast = amax >= 0x1p-60f;
-        r = fast ? 1.0f / s : 0.0f;
+    __device__ __forceinline__ explicit QuotientCtx(float amax, bool pow2 = false) {
+        if (pow2) {
+            s = scale_pow2(amax);
+            zero = !(amax > 0.0f);
+            fast = true;
+            r = 1.0f / s;
+        } else {
+            s = amax / kE4M3Max;
+            zero = !(s > 0.0f);
+            fast = amax >= 0x1p-60f;
+            r = fast ? 1.0f / s : 0.0f;
+        }
     }
     __device__ __forceinline__ float operator()(float x) const {
         float y;

@@ -54,6 +54,21 @@ __device__ __forceinline__ v4f mfma_e4m3(const v8i &a, const v8i &b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// The block-scaled form for power-of-two scales: c + 2^(ca - 127) 2^(cb -
+// 127) (a . b), with E8M0 codes ca, cb in byte 0 of the scale operands.
+// Each lane's code applies to the operand row it holds (and its 32-deep K
+// quarter); here every lane holding a row passes that row's code.
+__device__ __forceinline__ v4f mfma_e4m3_scaled(const v8i &a, const v8i &b, const v4f &c,
+                                                int ca, int cb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ca, 0, cb);
+}
+
+// E8M0 code of a power-of-two fp32 scale (its exponent field), carried in
+// a float register's bits.
+__device__ __forceinline__ float e8m0_code(float s) {
+    return __uint_as_float(__float_as_uint(s) >> 23);
+}
+
 enum OutKind { kOutF32 = 0, kOutBF16 = 1, kOutPartial = 2 };
 
 struct GemmParams {
@@ -280,7 +295,11 @@ __device__ __forceinline__ TileOperands tile_operands(const uint8_t *a, const fl
 // Copy t of wave v fills LDS rows [8 (v + kWaves t), +8): lane L writes
 // physical chunk L % 8 of row L / 8 of that block, i.e. the row's logical
 // chunk (L % 8) ^ key(row).
-template <class C>
+//
+// kPow2: the scales are powers of two.  Each MFMA then takes their E8M0 codes
+// and accumulates into the FP32 accumulators itself (acc + sa sw P_kb in one
+// instruction), so there is no promotion FMA.
+template <class C, bool kPow2 = false>
 __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K, int G, int kb0,
                                               int kb1, int col_off,
                                               TileLds<C> &L,
@@ -387,11 +406,17 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         return make_v8i(lo, hi);
     };
     // Scales of block kb (stage s): sc[i] = sa(i) * sw for waves inside one
-    // weight-scale block, else sc[i] = sa(i) and swj[j] = sw(fragment j).
+    // weight-scale block, else sc[i] = sa(i) and swj[j] = sw(fragment j);
+    // with power-of-two scales, sc[i] and swj[j] hold the E8M0 codes.
     auto load_scales = [&](int s, int kb, float (&sc)[C::kTM], float (&swj)[C::kTN]) {
         const float *sa_lane =
             &L.chunks.v[(kb / C::kScaleChunk) & 1][(kb >> 2) & 1][wm * C::WM + lr][kb & 3];
-        if constexpr (C::kWaveInOneBlock) {
+        if constexpr (kPow2) {
+#pragma unroll
+            for (int i = 0; i < C::kTM; ++i) sc[i] = e8m0_code(sa_lane[64 * i]);
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j) swj[j] = e8m0_code(L.sw[s][(col_off + 16 * j) >> 7]);
+        } else if constexpr (C::kWaveInOneBlock) {
             const float swv = L.sw[s][col_off >> 7];
 #pragma unroll
             for (int i = 0; i < C::kTM; ++i) sc[i] = sa_lane[64 * i] * swv;
@@ -471,16 +496,22 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             if (kSplit && i == C::kTM - 1) load_scales(s ^ 1, kb + 1, sc_next, swj_next);
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j) {
-                const v4f p = mfma_e4m3(wfr[j], af);
-                if (kSplit && i == C::kTM - 1) wfr[j] = wfrag(s ^ 1, j);  // next block's
-                if (pi >= 0) promote(pi, pj, p_prev);
-                p_prev = p;
-                pi = i;
-                pj = j;
+                if constexpr (kPow2) {
+                    acc[i][j] = mfma_e4m3_scaled(wfr[j], af, acc[i][j], __float_as_int(swj[j]),
+                                                 __float_as_int(sc[i]));
+                    if (kSplit && i == C::kTM - 1) wfr[j] = wfrag(s ^ 1, j);  // next block's
+                } else {
+                    const v4f p = mfma_e4m3(wfr[j], af);
+                    if (kSplit && i == C::kTM - 1) wfr[j] = wfrag(s ^ 1, j);  // next block's
+                    if (pi >= 0) promote(pi, pj, p_prev);
+                    p_prev = p;
+                    pi = i;
+                    pj = j;
+                }
             }
             af = af_next;
         }
-        promote(pi, pj, p_prev);
+        if constexpr (!kPow2) promote(pi, pj, p_prev);
         if constexpr (kSplit) {
             af_carry = af;
 #pragma unroll
@@ -695,7 +726,7 @@ __device__ __forceinline__ int xcd_logical_tile() {
     return (blockIdx.x % kNumXcd) * per + blockIdx.x / kNumXcd;
 }
 
-template <class C, int OUT>
+template <class C, int OUT, bool kPow2>
 __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
     __shared__ TileLds<C> lds;
     const int logical = xcd_logical_tile();
@@ -722,7 +753,7 @@ __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
     const TileOperands op =
         tile_operands<C>(p.a, p.sa, p.w, p.sw, row0, p.M - row0, n0, p.N - n0, p.K, p.G);
     const int wn = (threadIdx.x >> 6) % C::kWavesN;
-    tile_mainloop<C>(op, p.K, p.G, kb0, kb1, (int)(n0 & 127) + wn * C::WN, lds, acc);
+    tile_mainloop<C, kPow2>(op, p.K, p.G, kb0, kb1, (int)(n0 & 127) + wn * C::WN, lds, acc);
     if (OUT == kOutPartial)
         tile_store<C, kOutF32, false>(acc, lds, p.partial + (int64_t)ks * p.M * p.N, p.N, row0,
                                       p.M, n0, p.N);
@@ -731,14 +762,14 @@ __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
 }
 
 // One 256-row tile of the dense GEMM at (row0, n0), full K.
-template <class C, int OUT>
+template <class C, int OUT, bool kPow2>
 __device__ __forceinline__ void dense_tile(const GemmParams &p, TileLds<C> &lds, int64_t row0,
                                            int64_t n0) {
     v4f acc[C::kTM][C::kTN];
     const TileOperands op =
         tile_operands<C>(p.a, p.sa, p.w, p.sw, row0, p.M - row0, n0, p.N - n0, p.K, p.G);
     const int wn = (threadIdx.x >> 6) % C::kWavesN;
-    tile_mainloop<C>(op, p.K, p.G, 0, p.G, (int)(n0 & 127) + wn * C::WN, lds, acc);
+    tile_mainloop<C, kPow2>(op, p.K, p.G, 0, p.G, (int)(n0 & 127) + wn * C::WN, lds, acc);
     tile_store<C, OUT>(acc, lds, p.c, p.N, row0, p.M, n0, p.N);
 }
 
@@ -762,7 +793,7 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int grou
 // each per CU instead of two 256 x 256 tiles on 192 CUs and one on the
 // rest).  Each XCD takes a contiguous share of each kind, the wide tiles
 // first; the LDS holds either layout.
-template <int OUT>
+template <int OUT, bool kPow2>
 __global__ __launch_bounds__(BigTile::kThreads) void dense_gemm_two_kind_kernel(GemmParams p) {
     using CB = BigTile;
     using CN = NarrowTile;
@@ -780,12 +811,13 @@ __global__ __launch_bounds__(BigTile::kThreads) void dense_gemm_two_kind_kernel(
         const int t = xcd * per1 + slot;
         if (t >= t1) return;
         raster(t, p.tiles_m, p.tn1, p.group_m, tm, tn);
-        dense_tile<CB, OUT>(p, lds.big, (int64_t)tm * CB::BM, (int64_t)tn * CB::BN);
+        dense_tile<CB, OUT, kPow2>(p, lds.big, (int64_t)tm * CB::BM, (int64_t)tn * CB::BN);
     } else {
         const int t = xcd * per2 + (slot - per1);
         if (slot - per1 >= per2 || t >= t2) return;
         raster(t, p.tiles_m, p.tn2, p.group_m, tm, tn);
-        dense_tile<CN, OUT>(p, lds.narrow, (int64_t)tm * CN::BM, p.n_split + (int64_t)tn * CN::BN);
+        dense_tile<CN, OUT, kPow2>(p, lds.narrow, (int64_t)tm * CN::BM,
+                                   p.n_split + (int64_t)tn * CN::BN);
     }
 }
 
@@ -835,7 +867,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
 // clamp to [0, T]: the same as [off[e], off[e + 1]) for valid
 // (non-decreasing) offsets, and disjoint ranges within [0, T] for any
 // others, so the tile count never exceeds the worst case.
-template <class C, int OUT>
+template <class C, int OUT, bool kPow2>
 __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p) {
     __shared__ TileLds<C> lds;
     __shared__ int64_t info[4];
@@ -934,7 +966,7 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p)
     const TileOperands op =
         tile_operands<C>(p.a, p.sa, w, sw, row0, row_end - row0, n0, p.N - n0, p.K, p.G);
     const int wn = (threadIdx.x >> 6) % C::kWavesN;
-    tile_mainloop<C>(op, p.K, p.G, 0, p.G, (int)(n0 & 127) + wn * C::WN, lds, acc);
+    tile_mainloop<C, kPow2>(op, p.K, p.G, 0, p.G, (int)(n0 & 127) + wn * C::WN, lds, acc);
     tile_store<C, OUT>(acc, lds, p.c, p.N, row0, row_end, n0, p.N);
 }
 
@@ -996,15 +1028,44 @@ Plan plan_dense(int64_t M, int64_t N, int64_t K) {
     return {false, s, per};
 }
 
-template <class C, int OUT>
+template <class C, int OUT, bool kPow2>
 hipError_t launch_dense(const GemmParams &p0, hipStream_t stream) {
     GemmParams p = p0;
     p.tiles_m = (int)((p.M + C::BM - 1) / C::BM);
     p.tiles_n = (int)((p.N + C::BN - 1) / C::BN);
     p.ntiles = p.tiles_m * p.tiles_n * p.ksplit;
     const int grid = round_up(p.ntiles, kNumXcd);
-    hipLaunchKernelGGL((dense_gemm_kernel<C, OUT>), dim3(grid), dim3(C::kThreads), 0, stream, p);
+    hipLaunchKernelGGL((dense_gemm_kernel<C, OUT, kPow2>), dim3(grid), dim3(C::kThreads), 0,
+                       stream, p);
     return hipGetLastError();
+}
+
+// Launches the planned dense GEMM for one output type and scale mode.
+template <int OUT, bool kPow2>
+hipError_t block_gemm(GemmParams p, const Plan &pl, void *c, hipStream_t stream) {
+    if (pl.big && pl.tn2 > 0) {
+        p.tiles_m = (int)((p.M + 255) / 256);
+        p.tn1 = pl.tn1;
+        p.tn2 = pl.tn2;
+        p.n_split = (int64_t)pl.tn1 * BigTile::BN;
+        const int per1 = (p.tiles_m * p.tn1 + kNumXcd - 1) / kNumXcd;
+        const int per2 = (p.tiles_m * p.tn2 + kNumXcd - 1) / kNumXcd;
+        const int grid = kNumXcd * (per1 + per2);
+        hipLaunchKernelGGL((dense_gemm_two_kind_kernel<OUT, kPow2>), dim3(grid),
+                           dim3(BigTile::kThreads), 0, stream, p);
+        return hipGetLastError();
+    }
+    if (pl.big) return launch_dense<BigTile, OUT, kPow2>(p, stream);
+    if (p.ksplit > 1) {
+        hipError_t e = launch_dense<SmallTile, kOutPartial, kPow2>(p, stream);
+        if (e != hipSuccess) return e;
+        const int64_t MN = p.M * p.N;
+        const int64_t blocks = (MN / 4 + 255) / 256;
+        hipLaunchKernelGGL(splitk_reduce_kernel<OUT>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           p.partial, c, MN, p.ksplit);
+        return hipGetLastError();
+    }
+    return launch_dense<SmallTile, OUT, kPow2>(p, stream);
 }
 
 }  // namespace
@@ -1018,7 +1079,8 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_block_gemm(const void *a, const float *sa, const void *w, const float *sw,
                              void *c, bool bf16_out, int64_t M, int64_t N, int64_t K,
-                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                             void *workspace, size_t workspace_bytes, bool pow2,
+                             hipStream_t stream) {
     GemmParams p{};
     p.a = static_cast<const uint8_t *>(a);
     p.sa = sa;
@@ -1036,46 +1098,18 @@ hipError_t launch_block_gemm(const void *a, const float *sa, const void *w, cons
     if (pl.ksplit > 1 && (workspace == nullptr || workspace_bytes < need)) pl = {false, 1, p.G};
     p.ksplit = pl.ksplit;
     p.kb_per_split = pl.kb_per_split;
-    if (pl.big && pl.tn2 > 0) {
-        p.tiles_m = (int)((M + 255) / 256);
-        p.tn1 = pl.tn1;
-        p.tn2 = pl.tn2;
-        p.n_split = (int64_t)pl.tn1 * BigTile::BN;
-        const int per1 = (p.tiles_m * p.tn1 + kNumXcd - 1) / kNumXcd;
-        const int per2 = (p.tiles_m * p.tn2 + kNumXcd - 1) / kNumXcd;
-        const int grid = kNumXcd * (per1 + per2);
-        if (bf16_out)
-            hipLaunchKernelGGL(dense_gemm_two_kind_kernel<kOutBF16>, dim3(grid),
-                               dim3(BigTile::kThreads), 0, stream, p);
-        else
-            hipLaunchKernelGGL(dense_gemm_two_kind_kernel<kOutF32>, dim3(grid),
-                               dim3(BigTile::kThreads), 0, stream, p);
-        return hipGetLastError();
-    }
-    if (pl.big)
-        return bf16_out ? launch_dense<BigTile, kOutBF16>(p, stream)
-                        : launch_dense<BigTile, kOutF32>(p, stream);
-    if (p.ksplit > 1) {
-        p.partial = static_cast<float *>(workspace);
-        hipError_t e = launch_dense<SmallTile, kOutPartial>(p, stream);
-        if (e != hipSuccess) return e;
-        const int64_t MN = M * N;
-        const int64_t blocks = (MN / 4 + 255) / 256;
-        if (bf16_out)
-            hipLaunchKernelGGL(splitk_reduce_kernel<kOutBF16>, dim3((unsigned)blocks), dim3(256), 0,
-                               stream, p.partial, c, MN, p.ksplit);
-        else
-            hipLaunchKernelGGL(splitk_reduce_kernel<kOutF32>, dim3((unsigned)blocks), dim3(256), 0,
-                               stream, p.partial, c, MN, p.ksplit);
-        return hipGetLastError();
-    }
-    return bf16_out ? launch_dense<SmallTile, kOutBF16>(p, stream)
-                    : launch_dense<SmallTile, kOutF32>(p, stream);
+    p.partial = static_cast<float *>(workspace);
+    if (pow2)
+        return bf16_out ? block_gemm<kOutBF16, true>(p, pl, c, stream)
+                        : block_gemm<kOutF32, true>(p, pl, c, stream);
+    return bf16_out ? block_gemm<kOutBF16, false>(p, pl, c, stream)
+                    : block_gemm<kOutF32, false>(p, pl, c, stream);
 }
 
 hipError_t launch_grouped_gemm(const void *a, const float *sa, const void *w, const float *sw,
                                const int32_t *offsets, int64_t E, int64_t T, void *c,
-                               bool bf16_out, int64_t N, int64_t K, hipStream_t stream) {
+                               bool bf16_out, int64_t N, int64_t K, bool pow2,
+                               hipStream_t stream) {
     using C = MidTile;
     GemmParams p{};
     p.a = static_cast<const uint8_t *>(a);
@@ -1095,13 +1129,22 @@ hipError_t launch_grouped_gemm(const void *a, const float *sa, const void *w, co
     p.ntiles = p.tiles_m * p.tiles_n;
     p.ksplit = 1;
     p.kb_per_split = p.G;
-    const int grid = round_up(p.ntiles, kNumXcd);
-    if (bf16_out)
-        hipLaunchKernelGGL((grouped_gemm_kernel<C, kOutBF16>), dim3(grid), dim3(C::kThreads), 0,
-                           stream, p);
-    else
-        hipLaunchKernelGGL((grouped_gemm_kernel<C, kOutF32>), dim3(grid), dim3(C::kThreads), 0,
-                           stream, p);
+    const dim3 grid(round_up(p.ntiles, kNumXcd));
+    if (pow2) {
+        if (bf16_out)
+            hipLaunchKernelGGL((grouped_gemm_kernel<C, kOutBF16, true>), grid, dim3(C::kThreads),
+                               0, stream, p);
+        else
+            hipLaunchKernelGGL((grouped_gemm_kernel<C, kOutF32, true>), grid, dim3(C::kThreads),
+                               0, stream, p);
+    } else {
+        if (bf16_out)
+            hipLaunchKernelGGL((grouped_gemm_kernel<C, kOutBF16, false>), grid, dim3(C::kThreads),
+                               0, stream, p);
+        else
+            hipLaunchKernelGGL((grouped_gemm_kernel<C, kOutF32, false>), grid, dim3(C::kThreads),
+                               0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -38,8 +38,11 @@ constexpr int kQuantThreads = 256;
 // One unit per thread: more, shorter workgroups keep more of the stream in
 // flight than two or four units per thread (measured ~5% faster on
 // 4096 x 7168).
+// kPow2: power-of-two scales (scale_pow2); the reciprocal is then exact and
+// the fast path serves every group with amax > 0.
 constexpr int kFlatUnroll = 1;  // 16-element units per thread per block
 
+template <bool kPow2>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_flat_kernel(
     const u32x4 *__restrict__ x, u32x4 *__restrict__ q, float *__restrict__ scales,
     int64_t n_units) {
@@ -77,13 +80,13 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_flat_kernel(
         const float amax = row8_max(m);
         float y[16];
         float s;
-        if (__all(!in || amax >= 0x1p-60f)) {
-            s = scale_fast(amax);
+        if (__all(!in || (kPow2 ? amax > 0.0f : amax >= 0x1p-60f))) {
+            s = kPow2 ? scale_pow2(amax) : scale_fast(amax);
             const float r = 1.0f / s;
 #pragma unroll
             for (int i = 0; i < 16; ++i) y[i] = quot_fast(f[i], s, r);
         } else {
-            const QuotientCtx qc(amax);
+            const QuotientCtx qc(amax, kPow2);
             s = qc.s;
 #pragma unroll
             for (int i = 0; i < 16; ++i) y[i] = qc(f[i]);
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_flat_kernel(
 // General path: any K and alignment.  One DPP row per group (m, g); lane j
 // covers channels [128 g + 8 j, +8) clipped to K.  kVec: K % 8 == 0 with x
 // 16-byte and q 8-byte aligned, so every in-range chunk is a full vector.
-template <bool kVec>
+template <bool kVec, bool kPow2>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_general_kernel(
     const uint16_t *__restrict__ x, uint8_t *__restrict__ q, float *__restrict__ scales,
     int64_t M, int64_t K, int64_t G) {
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_general_kernel(
             f[i] = i < n ? __uint_as_float((uint32_t)x[off + i] << 16) : 0.0f;
     }
     const float amax = row16_max(absmax8(f));
-    const QuotientCtx qc(amax);
+    const QuotientCtx qc(amax, kPow2);
     const uint2 out = quant8(f, qc);
     if (kVec && n == 8) {
         *reinterpret_cast<uint2 *>(q + off) = out;
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_general_kernel(
 // covers chunk c = t + 256 i (i < 8): block row c / 16, channels 8 (c % 16)
 // .. +8.  Block maximum: per-thread, per-wave DPP/shuffle, then across the
 // four waves through LDS.  Offline work (weights are quantized once).
-template <bool kVec>
+template <bool kVec, bool kPow2>
 __global__ __launch_bounds__(kQuantThreads) void quant_weight_kernel(
     const uint16_t *__restrict__ w, uint8_t *__restrict__ q, float *__restrict__ scales,
     int64_t N, int64_t K, int64_t G) {
@@ -184,7 +187,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_weight_kernel(
     if ((threadIdx.x & 63) == 0) wave_amax[threadIdx.x >> 6] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(wave_amax[0], wave_amax[1]), fmaxf(wave_amax[2], wave_amax[3]));
-    const QuotientCtx qc(amax);
+    const QuotientCtx qc(amax, kPow2);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const uint2 out = quant8(f[i], qc);
@@ -200,50 +203,64 @@ __global__ __launch_bounds__(kQuantThreads) void quant_weight_kernel(
 
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-}  // namespace
-
-hipError_t launch_quant_act_1x128(const void *x, int64_t M, int64_t K, void *q, float *scales,
-                                  hipStream_t stream) {
+template <bool kPow2>
+hipError_t quant_act(const void *x, int64_t M, int64_t K, void *q, float *scales,
+                     hipStream_t stream) {
     const int64_t G = (K + kGroup - 1) / kGroup;
     const bool vec = (K % 8 == 0) && aligned(x, 16) && aligned(q, 8);
     if (K % kGroup == 0 && aligned(x, 16) && aligned(q, 16)) {
         const int64_t n_units = M * K / 16;
         const int64_t per_block = (int64_t)kQuantThreads * kFlatUnroll;
         const int64_t blocks = (n_units + per_block - 1) / per_block;
-        hipLaunchKernelGGL(quant_act_flat_kernel, dim3((unsigned)blocks), dim3(kQuantThreads), 0,
-                           stream, static_cast<const u32x4 *>(x), static_cast<u32x4 *>(q), scales,
-                           n_units);
+        hipLaunchKernelGGL(quant_act_flat_kernel<kPow2>, dim3((unsigned)blocks),
+                           dim3(kQuantThreads), 0, stream, static_cast<const u32x4 *>(x),
+                           static_cast<u32x4 *>(q), scales, n_units);
     } else {
         const int64_t groups = M * G;
         const int64_t per_block = kQuantThreads / 16;
         const int64_t blocks = (groups + per_block - 1) / per_block;
         if (vec)
-            hipLaunchKernelGGL(quant_act_general_kernel<true>, dim3((unsigned)blocks),
+            hipLaunchKernelGGL((quant_act_general_kernel<true, kPow2>), dim3((unsigned)blocks),
                                dim3(kQuantThreads), 0, stream, static_cast<const uint16_t *>(x),
                                static_cast<uint8_t *>(q), scales, M, K, G);
         else
-            hipLaunchKernelGGL(quant_act_general_kernel<false>, dim3((unsigned)blocks),
+            hipLaunchKernelGGL((quant_act_general_kernel<false, kPow2>), dim3((unsigned)blocks),
                                dim3(kQuantThreads), 0, stream, static_cast<const uint16_t *>(x),
                                static_cast<uint8_t *>(q), scales, M, K, G);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_quant_weight_128x128(const void *w, int64_t N, int64_t K, void *q,
-                                       float *scales, hipStream_t stream) {
+template <bool kPow2>
+hipError_t quant_weight(const void *w, int64_t N, int64_t K, void *q, float *scales,
+                        hipStream_t stream) {
     const int64_t G = (K + kGroup - 1) / kGroup;
     const int64_t NB = (N + kGroup - 1) / kGroup;
     const bool vec = (K % 8 == 0) && aligned(w, 16) && aligned(q, 8);
     const dim3 grid((unsigned)(NB * G));
     if (vec)
-        hipLaunchKernelGGL(quant_weight_kernel<true>, grid, dim3(kQuantThreads), 0, stream,
-                           static_cast<const uint16_t *>(w), static_cast<uint8_t *>(q), scales, N,
-                           K, G);
+        hipLaunchKernelGGL((quant_weight_kernel<true, kPow2>), grid, dim3(kQuantThreads), 0,
+                           stream, static_cast<const uint16_t *>(w), static_cast<uint8_t *>(q),
+                           scales, N, K, G);
     else
-        hipLaunchKernelGGL(quant_weight_kernel<false>, grid, dim3(kQuantThreads), 0, stream,
-                           static_cast<const uint16_t *>(w), static_cast<uint8_t *>(q), scales, N,
-                           K, G);
+        hipLaunchKernelGGL((quant_weight_kernel<false, kPow2>), grid, dim3(kQuantThreads), 0,
+                           stream, static_cast<const uint16_t *>(w), static_cast<uint8_t *>(q),
+                           scales, N, K, G);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_act_1x128(const void *x, int64_t M, int64_t K, void *q, float *scales,
+                                  bool pow2, hipStream_t stream) {
+    return pow2 ? quant_act<true>(x, M, K, q, scales, stream)
+                : quant_act<false>(x, M, K, q, scales, stream);
+}
+
+hipError_t launch_quant_weight_128x128(const void *w, int64_t N, int64_t K, void *q,
+                                       float *scales, bool pow2, hipStream_t stream) {
+    return pow2 ? quant_weight<true>(w, N, K, q, scales, stream)
+                : quant_weight<false>(w, N, K, q, scales, stream);
 }
 
 }  // namespace fp8blk

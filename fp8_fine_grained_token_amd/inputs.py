@@ -74,6 +74,19 @@ def weights(rng: np.random.Generator, shape, sigma: float = 0.02) -> np.ndarray:
     return normal_bf16(rng, shape, sigma)
 
 
+def every_amax_groups(seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """One 128-element bf16 group per positive finite bf16 value A (32,639
+    groups): A itself, then 127 random magnitudes <= A, random signs.
+    Returns (bits [32639][128], A as float32)."""
+    amax_bits = np.arange(1, 0x7F80, dtype=np.uint32).astype(np.uint16)
+    rng = np.random.default_rng(seed)
+    amax = bf16_bits_to_f32(amax_bits)
+    rest = f32_to_bf16_bits(amax[:, None] * rng.random((amax.size, 127), dtype=np.float32))
+    rest = np.minimum(rest, amax_bits[:, None])
+    sign = (rng.random((amax.size, 128)) < 0.5).astype(np.uint16) << np.uint16(15)
+    return np.concatenate([amax_bits[:, None], rest], axis=1) | sign, amax
+
+
 def zipf_counts(rng: np.random.Generator, T: int, E: int, s: float = 1.1,
                 cap: int | None = None) -> np.ndarray:
     """Tokens per expert: Multinomial(T, p_e ~ (e+1)^-s), expert 0 hottest.

@@ -138,6 +138,52 @@ fp8_status fp8_block_grouped_gemm(const void *a_e4m3, const float *a_scales,
                                   int64_t K, void *workspace,
                                   size_t workspace_bytes, void *hip_stream);
 
+/*
+ * Power-of-two-scale variants for the block-scaled matrix core (page
+ * "kailasan.com recruit 147436", passage recommending that matrix units take
+ * the per-group scaling factors and do the group-scaled MMA themselves; on
+ * gfx950 V_MFMA_SCALE_F32_16X16X128_F8F6F4 takes one E8M0 power-of-two
+ * scale per operand row and 32-deep K quarter).  The pages fix no rule for
+ * power-of-two scales; the one used here: s = the smallest power of two
+ * with 448 s >= amax, and at least 2^-126, so every scale is a normal fp32
+ * power of two whose exponent field is its E8M0 code; code = E4M3
+ * round-to-nearest-even of x / s (exact division); an all-zero group stores
+ * s = 2^-126 and zero bytes.  Layouts, sizes and errors are those of
+ * fp8_quant_act_1x128 / fp8_quant_weight_128x128.
+ */
+fp8_status fp8_quant_act_1x128_pow2(const void *x_bf16, int64_t M, int64_t K,
+                                    void *q_e4m3, float *scales,
+                                    void *hip_stream);
+fp8_status fp8_quant_weight_128x128_pow2(const void *w_bf16, int64_t N,
+                                         int64_t K, void *q_e4m3,
+                                         float *scales, void *hip_stream);
+
+/*
+ * fp8_block_gemm / fp8_block_grouped_gemm with every scale a power of two
+ * (as the _pow2 quantizers write them).  The same C is computed, but each
+ * K block's product is scaled and added into the FP32 accumulators by the
+ * matrix core itself (one block-scaled MFMA per 16x16 tile and K block), so
+ * there is no separate promotion step.  Only the scales' exponent fields
+ * are used: a scale with nonzero mantissa bits, or outside [2^-126, 2^127],
+ * gives a result computed with its exponent alone (not checked).  Arguments,
+ * layouts, workspace and errors are those of the plain entry points.
+ */
+fp8_status fp8_block_gemm_pow2(const void *a_e4m3, const float *a_scales,
+                               const void *w_e4m3, const float *w_scales,
+                               void *c, int out_dtype, int64_t M, int64_t N,
+                               int64_t K, void *workspace,
+                               size_t workspace_bytes, void *hip_stream);
+fp8_status fp8_block_grouped_gemm_pow2(const void *a_e4m3,
+                                       const float *a_scales,
+                                       const void *w_e4m3,
+                                       const float *w_scales,
+                                       const int32_t *group_offsets,
+                                       int64_t E, int64_t T, void *c,
+                                       int out_dtype, int64_t N, int64_t K,
+                                       void *workspace,
+                                       size_t workspace_bytes,
+                                       void *hip_stream);
+
 /* Workspace bytes that let fp8_block_gemm use its split-K path for this
  * shape (0 when the shape does not use it). */
 size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int out_dtype);

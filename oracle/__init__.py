@@ -64,6 +64,10 @@ def _load():
         lib.orc_quant_act_1x128.restype = None
         lib.orc_quant_weight_128x128.argtypes = [P, I64, I64, P, P]
         lib.orc_quant_weight_128x128.restype = None
+        lib.orc_quant_act_1x128_pow2.argtypes = [P, I64, I64, P, P]
+        lib.orc_quant_act_1x128_pow2.restype = None
+        lib.orc_quant_weight_128x128_pow2.argtypes = [P, I64, I64, P, P]
+        lib.orc_quant_weight_128x128_pow2.restype = None
         lib.orc_block_gemm_rows.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P]
         lib.orc_block_gemm_rows.restype = None
         lib.orc_grouped_gemm_rows.argtypes = [P, P, P, P, P, I64, I64, I64, I64,
@@ -124,6 +128,27 @@ def quant_weight_128x128(w_bf16: np.ndarray):
     q = np.empty((N, K), dtype=np.uint8)
     s = np.empty(((N + 127) // 128, (K + 127) // 128), dtype=np.float32)
     _load().orc_quant_weight_128x128(_ptr(w), N, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quant_act_1x128_pow2(x_bf16: np.ndarray):
+    """As quant_act_1x128 with power-of-two scales (oracle.c, pow2 reading)."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    G = (K + 127) // 128
+    q = np.empty((M, K), dtype=np.uint8)
+    s = np.empty((M, G), dtype=np.float32)
+    _load().orc_quant_act_1x128_pow2(_ptr(x), M, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quant_weight_128x128_pow2(w_bf16: np.ndarray):
+    """As quant_weight_128x128 with power-of-two scales."""
+    w = _c(w_bf16, np.uint16)
+    N, K = w.shape
+    q = np.empty((N, K), dtype=np.uint8)
+    s = np.empty(((N + 127) // 128, (K + 127) // 128), dtype=np.float32)
+    _load().orc_quant_weight_128x128_pow2(_ptr(w), N, K, _ptr(q), _ptr(s))
     return q, s
 
 

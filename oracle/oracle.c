@@ -30,6 +30,16 @@
  * group gives s = 0 and zero bytes, and the GEMM reference is the exact sum of
  * dequantized products evaluated in binary64.
  *
+ * Power-of-two variant (the *_pow2 quantizers), after [kailasan 147436],
+ * passage recommending that matrix units take the scaling factors and do
+ * the group-scaled MMA themselves (block-scaled matrix instructions take
+ * power-of-two scales).  The pages give no rule for such scales; the reading
+ * used: s = the smallest power of two with 448 s >= amax, but at least
+ * 2^-126 (so s is a normal binary32); then the same quotient and rounding as
+ * above (x / s is exact); an all-zero group keeps s = 2^-126 and gets zero
+ * bytes.  The GEMM reference needs no variant: it takes the scales as
+ * inputs.
+ *
  * Parity pins: every function here is pinned by tests that do not reuse this
  * code (format facts and an independent library cast for the E4M3 codec,
  * closed forms, invariants and exact-rational brute force for the rest).
@@ -128,11 +138,13 @@ void orc_e4m3_encode_array(const float *y, int64_t n, uint8_t *out) {
 
 /* Quantize the elements x[r*ld + c] for r < rows, c < cols as ONE group:
  *   amax = max |x|            (exact, order-free)
- *   s    = fl32(amax / 448)   (binary32 divide, RNE, gradual underflow)
- *   q    = E4M3_RNE(fl32(x / s)), or all 0x00 with s = +0 when amax == 0.
+ *   s    = fl32(amax / 448)   (binary32 divide, RNE, gradual underflow),
+ *          or with pow2 the smallest power of two >= amax / 448 and >= 2^-126
+ *   q    = E4M3_RNE(fl32(x / s)), or all 0x00 when amax == 0 (with s = +0,
+ *          or 2^-126 with pow2).
  * The bytes go to q[r*ld + c]; the scale is returned. */
 static float orc_quant_group(const uint16_t *x, int64_t ld, int64_t rows,
-                             int64_t cols, uint8_t *q) {
+                             int64_t cols, int pow2, uint8_t *q) {
     int64_t r, c;
     float amax = 0.0f, s;
     for (r = 0; r < rows; ++r)
@@ -140,11 +152,19 @@ static float orc_quant_group(const uint16_t *x, int64_t ld, int64_t rows,
             float v = fabsf(orc_bf16_to_float(x[r * ld + c]));
             if (v > amax) amax = v;
         }
-    s = amax / ORC_FP8_MAX;
-    if (s == 0.0f) {
+    if (pow2) {
+        /* Start at the floor 2^-126 and double until 448 s reaches amax;
+         * every step is exact in binary64. */
+        double sd = ldexp(1.0, -126);
+        while (448.0 * sd < (double)amax) sd *= 2.0;
+        s = (float)sd; /* a power of two in binary32's normal range: exact */
+    } else {
+        s = amax / ORC_FP8_MAX;
+    }
+    if (amax == 0.0f) {
         for (r = 0; r < rows; ++r)
             for (c = 0; c < cols; ++c) q[r * ld + c] = 0x00;
-        return 0.0f;
+        return s;
     }
     for (r = 0; r < rows; ++r)
         for (c = 0; c < cols; ++c) {
@@ -159,8 +179,8 @@ static float orc_quant_group(const uint16_t *x, int64_t ld, int64_t rows,
 /* 1x128 activation tiles [dssusan 93378, Figure 7 (a)]: x is bf16 [M][K]
  * row-major, q is E4M3 [M][K], scales is fp32 [M][ceil(K/128)] row-major;
  * the last group of a row holds the K % 128 remaining channels. */
-void orc_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q,
-                         float *scales) {
+static void orc_quant_act(const uint16_t *x, int64_t M, int64_t K, int pow2,
+                          uint8_t *q, float *scales) {
     int64_t G = (K + ORC_GROUP - 1) / ORC_GROUP;
     int64_t m;
     orc_init_table();
@@ -171,7 +191,7 @@ void orc_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q,
             int64_t k0 = g * ORC_GROUP;
             int64_t w = (K - k0 < ORC_GROUP) ? K - k0 : ORC_GROUP;
             scales[m * G + g] =
-                orc_quant_group(x + m * K + k0, K, 1, w, q + m * K + k0);
+                orc_quant_group(x + m * K + k0, K, 1, w, pow2, q + m * K + k0);
         }
     }
 }
@@ -179,8 +199,8 @@ void orc_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q,
 /* 128x128 weight blocks [dssusan 93378, Figure 7 (a)]: w is bf16 [N][K]
  * (output channel n, input channel k), q is E4M3 [N][K], scales is fp32
  * [ceil(N/128)][ceil(K/128)]; edge blocks hold what remains. */
-void orc_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K,
-                              uint8_t *q, float *scales) {
+static void orc_quant_weight(const uint16_t *w, int64_t N, int64_t K, int pow2,
+                             uint8_t *q, float *scales) {
     int64_t NB = (N + ORC_GROUP - 1) / ORC_GROUP;
     int64_t G = (K + ORC_GROUP - 1) / ORC_GROUP;
     int64_t blk;
@@ -192,8 +212,29 @@ void orc_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K,
         int64_t h = (N - n0 < ORC_GROUP) ? N - n0 : ORC_GROUP;
         int64_t wd = (K - k0 < ORC_GROUP) ? K - k0 : ORC_GROUP;
         scales[nb * G + g] =
-            orc_quant_group(w + n0 * K + k0, K, h, wd, q + n0 * K + k0);
+            orc_quant_group(w + n0 * K + k0, K, h, wd, pow2, q + n0 * K + k0);
     }
+}
+
+void orc_quant_act_1x128(const uint16_t *x, int64_t M, int64_t K, uint8_t *q,
+                         float *scales) {
+    orc_quant_act(x, M, K, 0, q, scales);
+}
+
+void orc_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K,
+                              uint8_t *q, float *scales) {
+    orc_quant_weight(w, N, K, 0, q, scales);
+}
+
+/* Power-of-two-scale variants (same layouts). */
+void orc_quant_act_1x128_pow2(const uint16_t *x, int64_t M, int64_t K,
+                              uint8_t *q, float *scales) {
+    orc_quant_act(x, M, K, 1, q, scales);
+}
+
+void orc_quant_weight_128x128_pow2(const uint16_t *w, int64_t N, int64_t K,
+                                   uint8_t *q, float *scales) {
+    orc_quant_weight(w, N, K, 1, q, scales);
 }
 
 /* ---- GEMM reference ----------------------------------------------------- */

@@ -29,9 +29,11 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == sorted([
-        "fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_block_gemm",
-        "fp8_block_grouped_gemm", "fp8_gemm_workspace_bytes", "fp8_status_string"])
+    method = ["fp8_quant_act_1x128", "fp8_quant_weight_128x128", "fp8_block_gemm",
+              "fp8_block_grouped_gemm"]
+    assert declared_functions() == sorted(
+        method + [m + "_pow2" for m in method]
+        + ["fp8_gemm_workspace_bytes", "fp8_status_string"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -49,19 +51,26 @@ def test_status_strings():
     assert B.status_string(99) == "unknown fp8_status"
 
 
+SUFFIXES = ["", "_pow2"]
+
+
 def gemm(lib, a=A16, sa=A16, w=A16, sw=A16, c=A16, dt=B.FP8_OUT_BF16, M=128, N=256, K=512,
-         ws=NUL, wsb=0):
-    return lib.fp8_block_gemm(a, sa, w, sw, c, dt, M, N, K, ws, wsb, NUL)
+         ws=NUL, wsb=0, suffix=""):
+    fn = getattr(lib, "fp8_block_gemm" + suffix)
+    return fn(a, sa, w, sw, c, dt, M, N, K, ws, wsb, NUL)
 
 
 def grouped(lib, a=A16, sa=A16, w=A16, sw=A16, off=A16, E=4, T=128, c=A16,
-            dt=B.FP8_OUT_BF16, N=256, K=512, ws=NUL, wsb=0):
-    return lib.fp8_block_grouped_gemm(a, sa, w, sw, off, E, T, c, dt, N, K, ws, wsb, NUL)
+            dt=B.FP8_OUT_BF16, N=256, K=512, ws=NUL, wsb=0, suffix=""):
+    fn = getattr(lib, "fp8_block_grouped_gemm" + suffix)
+    return fn(a, sa, w, sw, off, E, T, c, dt, N, K, ws, wsb, NUL)
 
 
-def test_quantizer_argument_errors():
+@pytest.mark.parametrize("suffix", SUFFIXES)
+def test_quantizer_argument_errors(suffix):
     lib = B.lib()
-    for fn in (lib.fp8_quant_act_1x128, lib.fp8_quant_weight_128x128):
+    for fn in (getattr(lib, "fp8_quant_act_1x128" + suffix),
+               getattr(lib, "fp8_quant_weight_128x128" + suffix)):
         assert fn(NUL, 4, 128, NUL, NUL, NUL) == B.FP8_ERR_NULL
         assert fn(A16, 4, 128, NUL, A16, NUL) == B.FP8_ERR_NULL
         assert fn(A16, -1, 128, A16, A16, NUL) == B.FP8_ERR_SHAPE
@@ -76,42 +85,50 @@ def test_quantizer_argument_errors():
         assert fn(A16, 4, 128, A16, ctypes.c_void_p(0x10002), NUL) == B.FP8_ERR_ALIGN
 
 
-def test_gemm_argument_errors():
+@pytest.mark.parametrize("suffix", SUFFIXES)
+def test_gemm_argument_errors(suffix):
     lib = B.lib()
-    assert gemm(lib, K=500) == B.FP8_ERR_SHAPE
-    assert gemm(lib, N=200) == B.FP8_ERR_SHAPE
-    assert gemm(lib, M=-1) == B.FP8_ERR_SHAPE
-    assert gemm(lib, dt=7) == B.FP8_ERR_DTYPE
-    assert gemm(lib, a=NUL) == B.FP8_ERR_NULL
-    assert gemm(lib, sw=NUL) == B.FP8_ERR_NULL
-    assert gemm(lib, c=NUL) == B.FP8_ERR_NULL
-    assert gemm(lib, a=A8) == B.FP8_ERR_ALIGN
-    assert gemm(lib, w=A8) == B.FP8_ERR_ALIGN
-    assert gemm(lib, c=A8) == B.FP8_ERR_ALIGN
-    assert gemm(lib, sa=ctypes.c_void_p(0x10002)) == B.FP8_ERR_ALIGN
-    assert gemm(lib, ws=A16, wsb=0) == B.FP8_ERR_WORKSPACE
-    assert gemm(lib, ws=NUL, wsb=1024) == B.FP8_ERR_WORKSPACE
-    assert gemm(lib, ws=ctypes.c_void_p(0x10010), wsb=1024) == B.FP8_ERR_WORKSPACE
-    assert gemm(lib, K=0) == B.FP8_ERR_SHAPE
+
+    def gemm_(*a, **k):
+        return gemm(*a, suffix=suffix, **k)
+    assert gemm_(lib, K=500) == B.FP8_ERR_SHAPE
+    assert gemm_(lib, N=200) == B.FP8_ERR_SHAPE
+    assert gemm_(lib, M=-1) == B.FP8_ERR_SHAPE
+    assert gemm_(lib, dt=7) == B.FP8_ERR_DTYPE
+    assert gemm_(lib, a=NUL) == B.FP8_ERR_NULL
+    assert gemm_(lib, sw=NUL) == B.FP8_ERR_NULL
+    assert gemm_(lib, c=NUL) == B.FP8_ERR_NULL
+    assert gemm_(lib, a=A8) == B.FP8_ERR_ALIGN
+    assert gemm_(lib, w=A8) == B.FP8_ERR_ALIGN
+    assert gemm_(lib, c=A8) == B.FP8_ERR_ALIGN
+    assert gemm_(lib, sa=ctypes.c_void_p(0x10002)) == B.FP8_ERR_ALIGN
+    assert gemm_(lib, ws=A16, wsb=0) == B.FP8_ERR_WORKSPACE
+    assert gemm_(lib, ws=NUL, wsb=1024) == B.FP8_ERR_WORKSPACE
+    assert gemm_(lib, ws=ctypes.c_void_p(0x10010), wsb=1024) == B.FP8_ERR_WORKSPACE
+    assert gemm_(lib, K=0) == B.FP8_ERR_SHAPE
     # M = 0 is a no-op
-    assert gemm(lib, a=NUL, sa=NUL, c=NUL, M=0) == B.FP8_OK
+    assert gemm_(lib, a=NUL, sa=NUL, c=NUL, M=0) == B.FP8_OK
     # dtype is checked before the empty-problem shortcut
-    assert gemm(lib, M=0, dt=3) == B.FP8_ERR_DTYPE
+    assert gemm_(lib, M=0, dt=3) == B.FP8_ERR_DTYPE
 
 
-def test_grouped_argument_errors():
+@pytest.mark.parametrize("suffix", SUFFIXES)
+def test_grouped_argument_errors(suffix):
     lib = B.lib()
-    assert grouped(lib, off=NUL) == B.FP8_ERR_NULL
-    assert grouped(lib, E=0) == B.FP8_ERR_SHAPE
-    assert grouped(lib, E=-2) == B.FP8_ERR_SHAPE
-    assert grouped(lib, K=384 + 1) == B.FP8_ERR_SHAPE
-    assert grouped(lib, N=100) == B.FP8_ERR_SHAPE
-    assert grouped(lib, dt=2) == B.FP8_ERR_DTYPE
-    assert grouped(lib, off=ctypes.c_void_p(0x10002)) == B.FP8_ERR_ALIGN
-    assert grouped(lib, c=A8) == B.FP8_ERR_ALIGN
-    assert grouped(lib, ws=A16, wsb=0) == B.FP8_ERR_WORKSPACE
+
+    def grouped_(*a, **k):
+        return grouped(*a, suffix=suffix, **k)
+    assert grouped_(lib, off=NUL) == B.FP8_ERR_NULL
+    assert grouped_(lib, E=0) == B.FP8_ERR_SHAPE
+    assert grouped_(lib, E=-2) == B.FP8_ERR_SHAPE
+    assert grouped_(lib, K=384 + 1) == B.FP8_ERR_SHAPE
+    assert grouped_(lib, N=100) == B.FP8_ERR_SHAPE
+    assert grouped_(lib, dt=2) == B.FP8_ERR_DTYPE
+    assert grouped_(lib, off=ctypes.c_void_p(0x10002)) == B.FP8_ERR_ALIGN
+    assert grouped_(lib, c=A8) == B.FP8_ERR_ALIGN
+    assert grouped_(lib, ws=A16, wsb=0) == B.FP8_ERR_WORKSPACE
     # T = 0 is a no-op (E = 0 allowed then)
-    assert grouped(lib, T=0, E=0, a=NUL, sa=NUL, off=NUL, c=NUL) == B.FP8_OK
+    assert grouped_(lib, T=0, E=0, a=NUL, sa=NUL, off=NUL, c=NUL) == B.FP8_OK
 
 
 def test_workspace_query():

@@ -1,0 +1,223 @@
+"""GPU parity of the power-of-two-scale path (the block-scaled MFMA).
+
+Page "kailasan.com recruit 147436", passage recommending that matrix units
+take the per-group scaling factors and do the group-scaled MMA themselves.
+The _pow2 quantizers must match the oracle's power-of-two quantizers byte
+for byte and bit for bit; the _pow2 GEMMs, fed with those bytes and scales,
+must match the oracle's binary64 block GEMM (which takes the scales as
+inputs) within the same tolerances as the plain GEMMs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fp8_fine_grained_token_amd import binding as B
+from fp8_fine_grained_token_amd import inputs as I
+
+from .gpu_util import check_gemm, dev, dev_bf16, host, log, rel_fro, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = torch()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    yield
+    t.cuda.synchronize()
+
+
+def assert_quant_equal(qg, sg, qo, so, what):
+    nbad = int((qg != qo).sum())
+    sbad = int((sg.view(np.uint32) != so.view(np.uint32)).sum())
+    log(f"  {what}: byte mismatches={nbad} scale mismatches={sbad}")
+    if nbad:
+        idx = np.argwhere(qg != qo)[:5]
+        log("  first mismatches (row, col, gpu, oracle):",
+            [(int(i), int(j), int(qg[i, j]), int(qo[i, j])) for i, j in idx])
+    if sbad:
+        idx = np.argwhere(sg.view(np.uint32) != so.view(np.uint32))[:5]
+        log("  first scale mismatches (index, gpu, oracle):",
+            [(tuple(int(v) for v in i), float(sg[tuple(i)]), float(so[tuple(i)])) for i in idx])
+    assert nbad == 0 and sbad == 0
+
+
+def quant_act_gpu(bits):
+    q, s = B.fp8_quant_act_1x128_pow2(dev_bf16(bits))
+    return host(q), host(s)
+
+
+# ---- quantizers ---------------------------------------------------------------
+
+@pytest.mark.parametrize("M,K", [(1, 128), (3, 300), (17, 7168), (64, 1000), (5, 1001),
+                                 (33, 8), (2, 130)])
+def test_pow2_quant_act_shapes(M, K):
+    x, _ = I.activations(np.random.default_rng(M * 11 + K), M, K, 0.01, 50.0)
+    qo, so = oracle.quant_act_1x128_pow2(x)
+    qg, sg = quant_act_gpu(x)
+    assert_quant_equal(qg, sg, qo, so, f"pow2 act {M}x{K}")
+
+
+def test_pow2_quant_act_every_bf16_amax():
+    # One group per positive finite bf16 amax: every exponent, the floor
+    # 2^-126 and the significand test at 1.75 (amax = 448 * 2^k exactly and
+    # just above it) all occur.
+    x, _ = I.every_amax_groups(31)
+    qo, so = oracle.quant_act_1x128_pow2(x)
+    qg, sg = quant_act_gpu(x)
+    assert_quant_equal(qg, sg, qo, so, f"pow2 act, {x.shape[0]} amax values")
+
+
+def test_pow2_quant_act_workload_and_zero_groups():
+    x, _ = I.config_quant(seed=3)
+    x = x.copy()
+    x[5, :128] = 0            # +0 group
+    x[6, 256:384] = 0x8000    # -0 group: zero bytes, floor scale
+    log("  oracle quantizing 4096x7168 (pow2) ...")
+    qo, so = oracle.quant_act_1x128_pow2(x)
+    qg, sg = quant_act_gpu(x)
+    assert_quant_equal(qg, sg, qo, so, "pow2 act 4096x7168")
+    assert sg[5, 0] == np.float32(2.0 ** -126) and np.all(qg[6, 256:384] == 0)
+
+
+@pytest.mark.parametrize("N,K", [(256, 512), (200, 130), (128, 7168), (2048, 7168), (3, 5)])
+def test_pow2_quant_weight_shapes(N, K):
+    w = I.weights(np.random.default_rng(N * 3 + K), (N, K))
+    qo, so = oracle.quant_weight_128x128_pow2(w)
+    q, s = B.fp8_quant_weight_128x128_pow2(dev_bf16(w))
+    assert_quant_equal(host(q), host(s), qo, so, f"pow2 weight {N}x{K}")
+
+
+# ---- dense GEMM -----------------------------------------------------------------
+
+def quantize(g):
+    qa, sa = oracle.quant_act_1x128_pow2(g.a_bf16)
+    qw, sw = oracle.quant_weight_128x128_pow2(g.w_bf16)
+    return qa, sa, qw, sw
+
+
+def run_gemm(qa, sa, qw, sw, out, workspace=None):
+    return B.fp8_block_gemm_pow2(dev(qa), dev(sa), dev(qw), dev(sw), out_dtype=out,
+                                 workspace=workspace)
+
+
+def test_pow2_gemm_tiny_fp32_out():
+    g = I.config_tiny(seed=0)
+    qa, sa, qw, sw = quantize(g)
+    R = oracle.block_gemm(qa, sa, qw, sw)
+    check_gemm(run_gemm(qa, sa, qw, sw, "f32"), R, "f32", "pow2 tiny 128x256x512 f32")
+
+
+@pytest.mark.parametrize("M", [1, 17, 129, 300])
+@pytest.mark.parametrize("N,K", [(128, 128), (384, 640)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_pow2_gemm_ragged(M, N, K, out):
+    g = I.gemm_inputs(M, N, K, seed=M * 1000 + N + K + 1, outlier_frac=0.01, outlier_mult=20.0)
+    qa, sa, qw, sw = quantize(g)
+    R = oracle.block_gemm(qa, sa, qw, sw)
+    check_gemm(run_gemm(qa, sa, qw, sw, out), R, out, f"pow2 {M}x{N}x{K} {out}")
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 2048, 7168), (128, 128, 8192)])
+def test_pow2_gemm_split_k(M, N, K):
+    g = I.gemm_inputs(M, N, K, seed=M + N + K, outlier_frac=0.001, outlier_mult=100.0)
+    qa, sa, qw, sw = quantize(g)
+    log(f"  oracle GEMM {M}x{N}x{K} ...")
+    R = oracle.block_gemm(qa, sa, qw, sw)
+    t = torch()
+    nbytes = B.fp8_gemm_workspace_bytes(M, N, K, "bf16")
+    assert nbytes > 0
+    ws = t.empty(nbytes, dtype=t.uint8, device="cuda")
+    for out in ("f32", "bf16"):
+        check_gemm(run_gemm(qa, sa, qw, sw, out, workspace=ws), R, out,
+                   f"pow2 split-K {M}x{N}x{K} {out}")
+    check_gemm(run_gemm(qa, sa, qw, sw, "bf16"), R, "bf16", f"pow2 {M}x{N}x{K} no workspace")
+
+
+@pytest.mark.parametrize("M,N,K", [(4000, 7040, 384), (4096, 6144, 512), (4096, 7168, 256)])
+def test_pow2_gemm_large_tiles(M, N, K):
+    # 256 x 256 tiles with ragged edges, 256 x 192 tiles (waves straddling
+    # weight-scale blocks), and the two tile widths together.
+    g = I.gemm_inputs(M, N, K, seed=M + N + K + 2, outlier_frac=0.01, outlier_mult=20.0)
+    qa, sa, qw, sw = quantize(g)
+    c = run_gemm(qa, sa, qw, sw, "f32")
+    rows = np.unique(np.concatenate([np.arange(0, M, 113), [255, 256, M - 1]]))
+    R = oracle.block_gemm(qa, sa, qw, sw, rows)
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, "f32", f"pow2 {M}x{N}x{K}")
+
+
+def test_pow2_gemm_dense_workload_sampled_rows_and_plain_path():
+    # The prefill workload: sampled rows against the oracle, and the whole
+    # output against the plain (FMA-promoting) GEMM on the same bytes and
+    # scales; the two differ only in where the FP32 roundings fall.
+    g = I.config_dense(seed=0)
+    qa, sa, qw, sw = quantize(g)
+    c = host(run_gemm(qa, sa, qw, sw, "f32"))
+    c_plain = host(B.fp8_block_gemm(dev(qa), dev(sa), dev(qw), dev(sw), out_dtype="f32"))
+    rf = rel_fro(c, c_plain.astype(np.float64))
+    log(f"  pow2 vs plain GEMM, 4096x7168x7168 f32: rel_fro={rf:.3e}")
+    assert rf <= 1e-5
+    rows = np.array([0, 1, 255, 256, 2047, 2048, 4094, 4095])
+    log("  oracle GEMM on 8 sampled rows of 4096x7168x7168 ...")
+    R = oracle.block_gemm(qa, sa, qw, sw, rows)
+    check_gemm(torch().from_numpy(c[rows]), R, "f32", "pow2 dense sampled rows")
+
+
+def test_pow2_gemm_metamorphic_and_deterministic():
+    # Multiplying the activation scales by 2^3 keeps them powers of two and
+    # multiplies an FP32 result by exactly 8; repeated calls are bitwise equal.
+    g = I.gemm_inputs(4096, 7168, 256, seed=81)
+    qa, sa, qw, sw = quantize(g)
+    c0 = host(run_gemm(qa, sa, qw, sw, "f32"))
+    c1 = host(run_gemm(qa, sa, qw, sw, "f32"))
+    c2 = host(run_gemm(qa, sa * np.float32(8.0), qw, sw, "f32"))
+    assert np.array_equal(c0.view(np.uint32), c1.view(np.uint32))
+    assert np.array_equal(c2, c0 * np.float32(8.0))
+
+
+# ---- grouped GEMM -----------------------------------------------------------------
+
+def quantize_grouped(gi):
+    qa, sa = oracle.quant_act_1x128_pow2(gi.a_bf16)
+    E, N, K = gi.w_bf16.shape
+    qw, sw = oracle.quant_weight_128x128_pow2(gi.w_bf16.reshape(E * N, K))
+    return qa, sa, qw.reshape(E, N, K), sw.reshape(E, N // 128, K // 128)
+
+
+@pytest.mark.parametrize("counts,T", [([20, 0, 33, 1, 10], 70), ([129, 127, 1, 0, 256], 513)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_pow2_grouped_edge_cases(counts, T, out):
+    E = len(counts)
+    gi = I.grouped_inputs(E, T, 256, 384, seed=sum(counts) + E + 1, counts=counts)
+    qa, sa, qw, sw = quantize_grouped(gi)
+    R, _ = oracle.grouped_gemm(qa, sa, qw, sw, gi.offsets)
+    t = torch()
+    dt = t.float32 if out == "f32" else t.bfloat16
+    c = t.full((T, 256), 7.0, dtype=dt, device="cuda")
+    B.fp8_block_grouped_gemm_pow2(dev(qa), dev(sa), dev(qw), dev(sw),
+                                  dev(gi.offsets.astype(np.int32)), out_dtype=out, c=c)
+    routed = int(gi.offsets[-1])
+    assert np.all(host(c)[routed:] == 7.0), "unrouted rows were written"
+    check_gemm(c[:routed], R[:routed], out, f"pow2 grouped {counts} {out}")
+
+
+def test_pow2_grouped_workload_sampled_rows():
+    gi = I.config_grouped(seed=0)
+    log("  quantizing grouped workload with the oracle (pow2) ...")
+    qa, sa, qw, sw = quantize_grouped(gi)
+    c = B.fp8_block_grouped_gemm_pow2(dev(qa), dev(sa), dev(qw), dev(sw),
+                                      dev(gi.offsets.astype(np.int32)), out_dtype="bf16")
+    off = gi.offsets
+    rng = np.random.default_rng(3)
+    rows = []
+    for e in range(gi.E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            rows += [lo, hi - 1] + list(rng.integers(lo, hi, size=1))
+    rows = np.unique(np.array(rows))
+    log(f"  oracle grouped GEMM on {rows.size} sampled rows ...")
+    R, found = oracle.grouped_gemm(qa, sa, qw, sw, off, rows)
+    assert found.all()
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, "bf16", "pow2 grouped workload rows")
