@@ -70,6 +70,10 @@ def _load():
         lib.orc_quant_weight_128x128_pow2.restype = None
         lib.orc_block_gemm_rows.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P]
         lib.orc_block_gemm_rows.restype = None
+        lib.orc_rowscaled_gemm_rows.argtypes = [P, P, P, P, I64, I64, I64, P, I64, P]
+        lib.orc_rowscaled_gemm_rows.restype = None
+        lib.orc_quant_act_128x1_t.argtypes = [P, I64, I64, P, P]
+        lib.orc_quant_act_128x1_t.restype = None
         lib.orc_grouped_gemm_rows.argtypes = [P, P, P, P, P, I64, I64, I64, I64,
                                               P, I64, P, P]
         lib.orc_grouped_gemm_rows.restype = None
@@ -169,6 +173,47 @@ def block_gemm(qa, sa, qw, sw, rows=None) -> np.ndarray:
     R = np.empty((rows.size, N), dtype=np.float64)
     _load().orc_block_gemm_rows(_ptr(qa), _ptr(sa), _ptr(qw), _ptr(sw), M, N, K,
                                 _ptr(rows), rows.size, _ptr(R))
+    return R
+
+
+def quant_act_128x1_t(x_bf16: np.ndarray):
+    """128x1 tiles (128 tokens of one channel) of bf16 bits [M][K], written
+    transposed: (q_t u8 [K][M], scales_t f32 [K][ceil(M/128)])."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    q = np.empty((K, M), dtype=np.uint8)
+    s = np.empty((K, (M + 127) // 128), dtype=np.float32)
+    _load().orc_quant_act_128x1_t(_ptr(x), M, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def transpose_weight(qw: np.ndarray, sw: np.ndarray):
+    """Weights quantized in 128x128 blocks, transposed: q [N][K] -> [K][N],
+    scales [N/128][K/128] -> [K/128][N/128] (a block's scale is the same
+    whichever way the block is read)."""
+    return np.ascontiguousarray(_c(qw, np.uint8).T), np.ascontiguousarray(_c(sw, np.float32).T)
+
+
+def rowscaled_gemm(qa, sa, qb, sb, rows=None) -> np.ndarray:
+    """Binary64 reference of the GEMM with one scale row per row of both
+    operands: R[r][n] = sum_k (qa[m][k] sa[m][k/128]) (qb[n][k] sb[n][k/128])
+    for m = rows[r] (all rows when None)."""
+    qa = _c(qa, np.uint8)
+    sa = _c(sa, np.float32)
+    qb = _c(qb, np.uint8)
+    sb = _c(sb, np.float32)
+    M, K = qa.shape
+    N = qb.shape[0]
+    if sb.shape != (N, (K + 127) // 128):
+        raise ValueError("sb must be [N][ceil(K/128)]")
+    if rows is None:
+        rows = np.arange(M, dtype=np.int64)
+    rows = _c(np.asarray(rows, dtype=np.int64), np.int64)
+    if rows.size and (rows.min() < 0 or rows.max() >= M):
+        raise IndexError("row index out of range")
+    R = np.empty((rows.size, N), dtype=np.float64)
+    _load().orc_rowscaled_gemm_rows(_ptr(qa), _ptr(sa), _ptr(qb), _ptr(sb), M, N, K,
+                                    _ptr(rows), rows.size, _ptr(R))
     return R
 
 

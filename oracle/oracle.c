@@ -40,6 +40,16 @@
  * bytes.  The GEMM reference needs no variant: it takes the scales as
  * inputs.
  *
+ * Backward GEMMs [dssusan 93378, passages on FP8 in Fprop, Dgrad and Wgrad
+ * (E4M3 on every tensor; Wgrad lets activations be kept in FP8) and on
+ * per-group scaling along the inner dimension]; the grouping along the
+ * transposed axis is a reading.  Dgrad (dX = dY W) keeps the forward
+ * groupings: dY in 1x128 tiles along its inner dimension N, W in its
+ * 128x128 blocks, used transposed.  Wgrad (dW = dY^T X) sums over tokens, so
+ * both operands are grouped in 128x1 tiles (128 tokens of one channel),
+ * stored transposed with the token axis contiguous; its reference is the
+ * GEMM with one scale per row on both operands.
+ *
  * Parity pins: every function here is pinned by tests that do not reuse this
  * code (format facts and an independent library cast for the E4M3 codec,
  * closed forms, invariants and exact-rational brute force for the rest).
@@ -237,6 +247,34 @@ void orc_quant_weight_128x128_pow2(const uint16_t *w, int64_t N, int64_t K,
     orc_quant_weight(w, N, K, 1, q, scales);
 }
 
+/* 128x1 tiles, written transposed [backward reading above]: group (mb, k)
+ * holds x[m][k] for m in [128 mb, min(128 mb + 128, M)), quantized as one
+ * group (amax / 448 scale, as orc_quant_group).  q_t is E4M3 [K][M] with
+ * q_t[k][m] the code of x[m][k]; scales_t is fp32 [K][ceil(M/128)]. */
+void orc_quant_act_128x1_t(const uint16_t *x, int64_t M, int64_t K,
+                           uint8_t *q_t, float *scales_t) {
+    int64_t GM = (M + ORC_GROUP - 1) / ORC_GROUP;
+    int64_t k;
+    uint8_t *q = (uint8_t *)malloc((size_t)(M * K > 0 ? M * K : 1));
+    orc_init_table();
+#pragma omp parallel for schedule(static)
+    for (k = 0; k < K; ++k) {
+        int64_t mb;
+        for (mb = 0; mb < GM; ++mb) {
+            int64_t m0 = mb * ORC_GROUP;
+            int64_t h = (M - m0 < ORC_GROUP) ? M - m0 : ORC_GROUP;
+            scales_t[k * GM + mb] =
+                orc_quant_group(x + m0 * K + k, K, h, 1, 0, q + m0 * K + k);
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (k = 0; k < K; ++k) {
+        int64_t m;
+        for (m = 0; m < M; ++m) q_t[k * M + m] = q[m * K + k];
+    }
+    free(q);
+}
+
 /* ---- GEMM reference ----------------------------------------------------- */
 
 /* Dequantized operand element: the E4M3 value times its group's scale.
@@ -252,16 +290,18 @@ static double orc_deq(uint8_t code, float scale) {
  * summed in ascending k in binary64.  qa_row / sa_row are one activation row
  * and its ceil(K/128) scales; qw is [N][K], sw is [ceil(N/128)][ceil(K/128)].
  */
+/* w_rows_per_scale: 128 when sw holds one scale row per 128 W rows (128x128
+ * blocks), 1 when every W row has its own scales (1x128 tiles, Wgrad). */
 static void orc_gemm_row(const uint8_t *qa_row, const float *sa_row,
                          const uint8_t *qw, const float *sw, int64_t N,
-                         int64_t K, double *R) {
+                         int64_t K, int64_t w_rows_per_scale, double *R) {
     int64_t G = (K + ORC_GROUP - 1) / ORC_GROUP;
     int64_t n, k;
     double *a_deq = (double *)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
     for (k = 0; k < K; ++k) a_deq[k] = orc_deq(qa_row[k], sa_row[k / ORC_GROUP]);
     for (n = 0; n < N; ++n) {
         const uint8_t *wrow = qw + n * K;
-        const float *swrow = sw + (n / ORC_GROUP) * G;
+        const float *swrow = sw + (n / w_rows_per_scale) * G;
         double acc = 0.0;
         for (k = 0; k < K; ++k)
             acc += a_deq[k] * orc_deq(wrow[k], swrow[k / ORC_GROUP]);
@@ -283,7 +323,24 @@ void orc_block_gemm_rows(const uint8_t *qa, const float *sa, const uint8_t *qw,
 #pragma omp parallel for schedule(dynamic, 1)
     for (r = 0; r < nrows; ++r) {
         int64_t m = rows[r];
-        orc_gemm_row(qa + m * K, sa + m * G, qw, sw, N, K, R + r * N);
+        orc_gemm_row(qa + m * K, sa + m * G, qw, sw, N, K, ORC_GROUP, R + r * N);
+    }
+}
+
+/* GEMM with one scale row per row of both operands (Wgrad on 128x1-grouped
+ * operands stored transposed): R[r][n] = sum_k (qa[m][k] sa[m][k/128])
+ * (qb[n][k] sb[n][k/128]) for m = rows[r]; qb is [N][K], sb [N][ceil(K/128)]. */
+void orc_rowscaled_gemm_rows(const uint8_t *qa, const float *sa,
+                             const uint8_t *qb, const float *sb, int64_t M,
+                             int64_t N, int64_t K, const int64_t *rows,
+                             int64_t nrows, double *R) {
+    int64_t G = (K + ORC_GROUP - 1) / ORC_GROUP;
+    int64_t r;
+    (void)M;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < nrows; ++r) {
+        int64_t m = rows[r];
+        orc_gemm_row(qa + m * K, sa + m * G, qb, sb, N, K, 1, R + r * N);
     }
 }
 
@@ -310,7 +367,7 @@ void orc_grouped_gemm_rows(const uint8_t *qa, const float *sa,
         found[r] = hit >= 0;
         if (hit < 0) continue;
         orc_gemm_row(qa + t * K, sa + t * G, qw + hit * N * K,
-                     sw + hit * NB * G, N, K, R + r * N);
+                     sw + hit * NB * G, N, K, ORC_GROUP, R + r * N);
     }
 }
 
