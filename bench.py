@@ -16,8 +16,11 @@ Printed as one JSON line, with:
   * parts: each kernel on its own workload with the caches flushed before
     every launch (act quantizer GB/s vs HBM, beside a plain device copy of
     the same byte count; dense / decode / grouped GEMM TFLOP/s vs MFMA and
-    GB/s vs HBM), and the power-of-two-scale variants (quantizer, dense and
-    grouped GEMM on the block-scaled MFMA) on the same workloads;
+    GB/s vs HBM), the power-of-two-scale variants (quantizer, dense and
+    grouped GEMM on the block-scaled MFMA) on the same workloads, and the
+    backward pass of the same linear layer (the 128x1 transposed quantizer
+    on dY and X, Dgrad on the transposed weights, Wgrad over the 4096
+    tokens);
   * cpu_baseline: the CPU oracle timed on this host on a bounded sample of
     the same step (first 256 tokens).
 
@@ -112,6 +115,7 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
     is read (twice the 256 MB Infinity Cache), so operands come from HBM; a
     read leaves no dirty lines whose write-back would land in the timed
     launch."""
+    import numpy as np
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     parts = {}
 
@@ -159,6 +163,29 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
     parts["pow2_dense_gemm_4096x7168x7168"] = {
         "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
     del pa, psa, pw, psw
+
+    # backward of the same layer: dY [4096][7168] (same distribution as X
+    # without outliers); Dgrad = forward GEMM with the transposed weights,
+    # Wgrad = dY^T X from 128x1 tiles
+    dy = to_dev_bf16(torch, I.activations(np.random.default_rng(7), M, N, 0.0, 1.0)[0])
+    ms = timed(lambda: F.fp8_quant_act_128x1_t(dy), iters)
+    b = quant_bytes(M, N)
+    parts["bwd_quant_128x1_t_4096x7168"] = {
+        "us": ms * 1e3, "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+    qdy, sdy = F.fp8_quant_act_1x128(dy)
+    qwt, swt = F.fp8_transpose_weight_128x128(qw, sw)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    ms = timed(lambda: F.fp8_block_gemm(qdy, sdy, qwt, swt, out_dtype="bf16", c=dx), iters)
+    parts["bwd_dgrad_4096x7168x7168"] = {
+        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
+    qdy_t, sdy_t = F.fp8_quant_act_128x1_t(dy)
+    qx_t, sx_t = F.fp8_quant_act_128x1_t(X)
+    dw = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    ms = timed(lambda: F.fp8_block_gemm_wgrad(qdy_t, sdy_t, qx_t, sx_t, out_dtype="f32", dw=dw),
+               iters)
+    parts["bwd_wgrad_7168x7168_over_4096"] = {
+        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
+    del dy, qdy, sdy, qwt, swt, dx, qdy_t, sdy_t, qx_t, sx_t, dw
 
     # decode GEMM, 256 x 2048 x 7168 (split-K with workspace)
     gd = I.config_decode(seed=0)

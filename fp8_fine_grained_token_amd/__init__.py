@@ -10,5 +10,6 @@ from .binding import (  # noqa: F401
     FP8_OUT_BF16, FP8_OUT_F32, Fp8Error, fp8_block_gemm, fp8_block_gemm_pow2,
     fp8_block_grouped_gemm, fp8_block_grouped_gemm_pow2, fp8_gemm_workspace_bytes,
     fp8_quant_act_1x128, fp8_quant_act_1x128_pow2, fp8_quant_weight_128x128,
-    fp8_quant_weight_128x128_pow2, lib, status_string,
+    fp8_quant_weight_128x128_pow2, lib, status_string, fp8_quant_act_128x1_t,
+    fp8_transpose_weight_128x128, fp8_block_gemm_wgrad,
 )

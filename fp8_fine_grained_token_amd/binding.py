@@ -10,7 +10,9 @@ Two layers:
     functions (raw device pointers, sizes, stream handle);
   * ``fp8_quant_act_1x128``, ``fp8_quant_weight_128x128``,
     ``fp8_block_gemm`` and ``fp8_block_grouped_gemm`` (and their ``_pow2``
-    forms, power-of-two scales for the block-scaled matrix core) take torch
+    forms, power-of-two scales for the block-scaled matrix core), and the
+    backward-pass pieces ``fp8_quant_act_128x1_t``,
+    ``fp8_transpose_weight_128x128`` and ``fp8_block_gemm_wgrad``, take torch
     tensors on the GPU, allocate outputs when not given, call the C function
     on ``torch.cuda.current_stream()`` and raise ``Fp8Error`` on a nonzero
     status.
@@ -46,6 +48,10 @@ _SIGNATURES = {
                                 _I64, _I64, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "fp8_gemm_workspace_bytes": ([_I64, _I64, _I64, ctypes.c_int], ctypes.c_size_t),
     "fp8_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "fp8_quant_act_128x1_t": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "fp8_transpose_weight_128x128": ([_P, _P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "fp8_block_gemm_wgrad": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P],
+                             ctypes.c_int),
     "fp8_quant_act_1x128_pow2": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "fp8_quant_weight_128x128_pow2": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "fp8_block_gemm_pow2": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P,
@@ -239,3 +245,59 @@ def fp8_block_grouped_gemm_pow2(a, sa, w, sw, group_offsets, out_dtype="bf16", c
     """As fp8_block_grouped_gemm, for power-of-two scales."""
     return _grouped_gemm("fp8_block_grouped_gemm_pow2", a, sa, w, sw, group_offsets, out_dtype,
                          c, workspace, stream)
+
+
+# ---- backward pass ------------------------------------------------------------
+
+def fp8_quant_act_128x1_t(x, q_t=None, scales_t=None, stream=None):
+    """x: bf16 [M][K] -> (q_t uint8 [K][M], scales_t fp32 [K][ceil(M/128)]):
+    128x1 tiles (128 rows of one column), written transposed."""
+    torch = _torch()
+    M, K = x.shape
+    if q_t is None:
+        q_t = torch.empty((K, M), dtype=torch.uint8, device=x.device)
+    if scales_t is None:
+        scales_t = torch.empty((K, (M + 127) // 128), dtype=torch.float32, device=x.device)
+    _check(lib().fp8_quant_act_128x1_t(_dev(x, "x", torch.bfloat16), M, K,
+                                       _dev(q_t, "q_t", torch.uint8),
+                                       _dev(scales_t, "scales_t", torch.float32),
+                                       _stream_handle(stream)), "fp8_quant_act_128x1_t")
+    return q_t, scales_t
+
+
+def fp8_transpose_weight_128x128(q, scales, q_t=None, scales_t=None, stream=None):
+    """q: uint8 [N][K] with scales [ceil(N/128)][ceil(K/128)] -> (q_t [K][N],
+    scales_t [ceil(K/128)][ceil(N/128)])."""
+    torch = _torch()
+    N, K = q.shape
+    if q_t is None:
+        q_t = torch.empty((K, N), dtype=torch.uint8, device=q.device)
+    if scales_t is None:
+        scales_t = torch.empty(((K + 127) // 128, (N + 127) // 128), dtype=torch.float32,
+                               device=q.device)
+    _check(lib().fp8_transpose_weight_128x128(_dev(q, "q", torch.uint8),
+                                              _dev(scales, "scales", torch.float32), N, K,
+                                              _dev(q_t, "q_t", torch.uint8),
+                                              _dev(scales_t, "scales_t", torch.float32),
+                                              _stream_handle(stream)),
+           "fp8_transpose_weight_128x128")
+    return q_t, scales_t
+
+
+def fp8_block_gemm_wgrad(dy_t, dy_t_scales, x_t, x_t_scales, out_dtype="f32", dw=None,
+                         stream=None):
+    """dW [N][K] = dY^T X from 128x1-grouped operands written transposed:
+    dy_t [N][T], x_t [K][T] (uint8 E4M3), scales [N][T/128] and [K][T/128]."""
+    torch = _torch()
+    N, T = dy_t.shape
+    K = x_t.shape[0]
+    code, tdt = _out_code(out_dtype)
+    if dw is None:
+        dw = torch.empty((N, K), dtype=tdt, device=dy_t.device)
+    _check(lib().fp8_block_gemm_wgrad(_dev(dy_t, "dy_t", torch.uint8),
+                                      _dev(dy_t_scales, "dy_t_scales", torch.float32),
+                                      _dev(x_t, "x_t", torch.uint8),
+                                      _dev(x_t_scales, "x_t_scales", torch.float32),
+                                      _dev(dw, "dw", tdt), code, N, K, T,
+                                      _stream_handle(stream)), "fp8_block_gemm_wgrad")
+    return dw

@@ -154,6 +154,40 @@ fp8_status fp8_block_grouped_gemm_pow2(const void *a_e4m3, const float *a_scales
                         N, K, workspace, workspace_bytes, true, hip_stream);
 }
 
+fp8_status fp8_quant_act_128x1_t(const void *x_bf16, int64_t M, int64_t K, void *q_t,
+                                 float *scales_t, void *hip_stream) {
+    fp8_status st = check_quant(x_bf16, M, K, q_t, scales_t);
+    if (st != FP8_OK || M == 0 || K == 0) return st;
+    if (!aligned(x_bf16, 2) || !aligned(scales_t, 4)) return FP8_ERR_ALIGN;
+    return from_hip(
+        fp8blk::launch_quant_act_128x1_t(x_bf16, M, K, q_t, scales_t, as_stream(hip_stream)));
+}
+
+fp8_status fp8_transpose_weight_128x128(const void *q_e4m3, const float *scales, int64_t N,
+                                        int64_t K, void *q_t, float *scales_t,
+                                        void *hip_stream) {
+    if (N < 0 || K < 0) return FP8_ERR_SHAPE;
+    if (N == 0 || K == 0) return FP8_OK;
+    if (!q_e4m3 || !scales || !q_t || !scales_t) return FP8_ERR_NULL;
+    if (N >= kMaxDim || K >= kMaxDim || N * K >= kMaxElems) return FP8_ERR_SHAPE;
+    if (!aligned(scales, 4) || !aligned(scales_t, 4)) return FP8_ERR_ALIGN;
+    return from_hip(fp8blk::launch_transpose_weight(q_e4m3, scales, N, K, q_t, scales_t,
+                                                    as_stream(hip_stream)));
+}
+
+fp8_status fp8_block_gemm_wgrad(const void *dy_t, const float *dy_t_scales, const void *x_t,
+                                const float *x_t_scales, void *dw, int out_dtype, int64_t N,
+                                int64_t K, int64_t T, void *hip_stream) {
+    // rows N, columns K, inner dimension T (tokens)
+    fp8_status st = check_gemm_common(dy_t, dy_t_scales, x_t, x_t_scales, dw, out_dtype, N, K, T,
+                                      nullptr, 0);
+    if (st != FP8_OK || N == 0 || K == 0) return st;
+    if (T == 0) return FP8_ERR_SHAPE;
+    return from_hip(fp8blk::launch_block_gemm_wgrad(dy_t, dy_t_scales, x_t, x_t_scales, dw,
+                                                    out_dtype == FP8_OUT_BF16, N, K, T,
+                                                    as_stream(hip_stream)));
+}
+
 size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int out_dtype) {
     if (out_dtype != FP8_OUT_F32 && out_dtype != FP8_OUT_BF16) return 0;
     if (M <= 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return 0;

@@ -91,7 +91,12 @@ struct GemmParams {
     int64_t n_split;         // two-kind plan: first column of the 192-wide tiles
 };
 
-template <int BM_, int BN_, int WAVES_M, int WAVES_N, int STAGES>
+// SCALE_PIECES: activation scales are staged in chunks of 4 * SCALE_PIECES K
+// blocks.  ROW_SCALED_W: W has one scale per row and K block (1x128 tiles,
+// the Wgrad operands) instead of one per 128-row block; those row scales are
+// staged in chunks like the activation scales.
+template <int BM_, int BN_, int WAVES_M, int WAVES_N, int STAGES, int SCALE_PIECES = 2,
+          bool ROW_SCALED_W = false>
 struct TileCfg {
     static constexpr int kStages = STAGES;
     static constexpr int BM = BM_;
@@ -108,12 +113,19 @@ struct TileCfg {
     static constexpr int kALoads = BM / 8 / kWaves;
     static constexpr int kBLoads = BN / 8 / kWaves;
     // activation scales come in chunks of kScaleChunk K blocks: 16 bytes
-    // (4 blocks) per lane, so one wave instruction fetches 64 row-halves
-    static constexpr int kScaleChunk = 8;
-    static constexpr int kScaleCopies = 2 * BM / 64;  // per chunk, over all waves
+    // (4 blocks, one piece) per lane, so one wave instruction fetches 64 row
+    // pieces
+    static constexpr int kScalePieces = SCALE_PIECES;
+    static constexpr int kScaleChunk = 4 * SCALE_PIECES;
+    static constexpr int kScaleCopies = SCALE_PIECES * BM / 64;  // per chunk, over all waves
     static constexpr int kScaleLoads = (kScaleCopies + kWaves - 1) / kWaves;  // per wave, at most
+    static constexpr bool kRowScaledW = ROW_SCALED_W;
+    static constexpr int kScaleCopiesW = ROW_SCALED_W ? SCALE_PIECES * BN / 64 : 0;
+    static constexpr int kScaleLoadsW = (kScaleCopiesW + kWaves - 1) / kWaves;
     static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "loader");
-    static_assert(BM % 32 == 0, "scale loader");
+    static_assert((SCALE_PIECES * BM) % 64 == 0 && (SCALE_PIECES * BN) % 64 == 0, "scale loader");
+    static_assert(SCALE_PIECES == 1 || SCALE_PIECES == 2, "scale chunk pieces");
+    static_assert(!ROW_SCALED_W || STAGES >= 3, "row-scaled W runs the S >= 3 pipeline");
     static_assert(((BM + BN) * 128) % 4096 == 0, "stage size");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
     // A wave's columns sit in one 128-column weight-scale block when WN
@@ -141,16 +153,16 @@ struct __align__(4096) Stage {
     uint8_t b[BN * 128];
 };
 
-// Activation scales of the tile's BM rows for kScaleChunk = 8 consecutive K
-// blocks, double buffered.  The scales are stored [M][K/128] in memory, so a
-// row's scales for one K block each sit in a different cache line; fetching
-// eight blocks per row at once (two 16-byte pieces) makes one L2 request
-// serve eight blocks instead of one.  Piece h of row r of buffer b holds
-// blocks 8 c + 4 h .. + 3 at float4 index (2 b + h) BM + r: the 16 lanes that
-// read one M tile's rows hit 16 distinct 16-byte bank groups.
-template <int BM>
+// Activation scales of the tile's BM rows for kScaleChunk = 4 P consecutive
+// K blocks (P pieces of 16 bytes), double buffered.  The scales are stored
+// [M][K/128] in memory, so a row's scales for one K block each sit in a
+// different cache line; fetching 4 P blocks per row at once makes one L2
+// request serve several blocks instead of one.  Piece h of row r of buffer b
+// holds blocks 4 P c + 4 h .. + 3 at float4 index (P b + h) ROWS + r: the 16
+// lanes that read one M tile's rows hit 16 distinct 16-byte bank groups.
+template <int ROWS, int P>
 struct ScaleChunks {
-    float v[2][2][BM][4];
+    float v[2][P][ROWS][4];
 };
 
 // Everything a workgroup keeps in LDS: the operand stages, the activation
@@ -159,8 +171,10 @@ struct ScaleChunks {
 template <class C>
 struct TileLds {
     Stage<C::BM, C::BN> stages[C::kStages];
-    ScaleChunks<C::BM> chunks;
+    ScaleChunks<C::BM, C::kScalePieces> chunks;
     float sw[C::kStages][64];
+    // row-scaled W only: its rows' scales, chunked like the activation scales
+    ScaleChunks<(C::kRowScaledW ? C::BN : 4), C::kScalePieces> wchunks;
 };
 
 // LDS layout of an operand tile: rows of 128 bytes (one K block); 16-byte
@@ -254,7 +268,7 @@ __device__ __forceinline__ void copy4(const v4i &r, uint32_t voff, uint32_t soff
 // and columns [n0, n0 + cols) of W are valid; the buffer bounds make every
 // other row read as zero, so ragged edges need no clamping.
 struct TileOperands {
-    v4i a, w, sa, sw;
+    v4i a, w, sa, sw, swr;  // swr: W row scales (row-scaled W only)
 };
 
 template <class C>
@@ -268,8 +282,17 @@ __device__ __forceinline__ TileOperands tile_operands(const uint8_t *a, const fl
     t.a = make_rsrc(a + row0 * K, (uint32_t)(ra * K));
     t.w = make_rsrc(w + n0 * K, (uint32_t)(cw * K));
     t.sa = make_rsrc(sa + row0 * G, (uint32_t)(ra * G * 4));
-    const int64_t nb0 = n0 >> 7, nbs = ((n0 + cw - 1) >> 7) - nb0 + 1;
-    t.sw = make_rsrc(sw + nb0 * G, (uint32_t)(nbs * G * 4));
+    if constexpr (C::kRowScaledW) {
+        // sw is [cols][G]: rows n0 .. n0 + cw of it.  The per-block weight
+        // scale copy still runs (from an empty buffer) so the wait counts
+        // stay those of the block-scaled layout.
+        t.swr = make_rsrc(sw + n0 * G, (uint32_t)(cw * G * 4));
+        t.sw = make_rsrc(sw, 0);
+    } else {
+        const int64_t nb0 = n0 >> 7, nbs = ((n0 + cw - 1) >> 7) - nb0 + 1;
+        t.sw = make_rsrc(sw + nb0 * G, (uint32_t)(nbs * G * 4));
+        t.swr = make_rsrc(sw, 0);
+    }
     return t;
 }
 
@@ -333,6 +356,14 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         const int q = 64 * (wave + C::kWaves * t) + lane;
         sa_voff[t] = (uint32_t)((q % C::BM) * G * 4 + (q / C::BM) * 16);
     }
+    // Row-scaled W: W chunk copy t of wave v fills float4 slots q = 64 (v +
+    // kWaves t) + L of a W chunk buffer, piece q / BN of W row q % BN.
+    uint32_t swr_voff[C::kScaleLoadsW > 0 ? C::kScaleLoadsW : 1];
+#pragma unroll
+    for (int t = 0; t < C::kScaleLoadsW; ++t) {
+        const int q = 64 * (wave + C::kWaves * t) + lane;
+        swr_voff[t] = (uint32_t)((q % C::BN) * G * 4 + (q / C::BN) * 16);
+    }
     const uint32_t sw_voff = (uint32_t)(lane * G * 4);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // for uniform branches
     // LDS destinations of this wave's copies in stage 0 (stage s is s *
@@ -342,6 +373,8 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     const uint32_t lds_sw0 = lds_addr(&L.sw[0][0]);
     const uint32_t lds_sc0 =
         lds_addr(reinterpret_cast<const uint8_t *>(&L.chunks.v[0][0][0][0]) + 1024 * wave);
+    const uint32_t lds_wc0 =
+        lds_addr(reinterpret_cast<const uint8_t *>(&L.wchunks.v[0][0][0][0]) + 1024 * wave);
 
     // Copy t of A fills tile rows [8 kWaves t, +8 kWaves); with two stages
     // a block's A rows go in two halves: the rows of every wave's first
@@ -375,6 +408,14 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
                 if (wave_u + C::kWaves * t < C::kScaleCopies)
                     copy16(src.sa, sa_voff[t], (uint32_t)c * (4u * C::kScaleChunk),
                            lds_sc0 + so + 1024 * C::kWaves * t);
+            if constexpr (C::kRowScaledW) {
+                const uint32_t sow = (uint32_t)((c & 1) * sizeof(L.wchunks.v[0]));
+#pragma unroll
+                for (int t = 0; t < C::kScaleLoadsW; ++t)
+                    if (wave_u + C::kWaves * t < C::kScaleCopiesW)
+                        copy16(src.swr, swr_voff[t], (uint32_t)c * (4u * C::kScaleChunk),
+                               lds_wc0 + sow + 1024 * C::kWaves * t);
+            }
         }
         // every wave fetches the (one or two) weight scales of the block to
         // the same LDS words; the duplicates carry identical values
@@ -407,11 +448,24 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     };
     // Scales of block kb (stage s): sc[i] = sa(i) * sw for waves inside one
     // weight-scale block, else sc[i] = sa(i) and swj[j] = sw(fragment j);
-    // with power-of-two scales, sc[i] and swj[j] hold the E8M0 codes.
+    // with power-of-two scales, sc[i] and swj[j] hold the E8M0 codes.  With
+    // row-scaled W, sc[i] = sa(i) and swr[j][e] = the scale of W row 16 j +
+    // 4 (lane / 16) + e of the wave's columns (the rows of this lane's four
+    // outputs of fragment j).
+    static_assert(!(kPow2 && C::kRowScaledW), "row-scaled W runs with FP32 scales");
+    float swr[C::kTN][4];
     auto load_scales = [&](int s, int kb, float (&sc)[C::kTM], float (&swj)[C::kTN]) {
-        const float *sa_lane =
-            &L.chunks.v[(kb / C::kScaleChunk) & 1][(kb >> 2) & 1][wm * C::WM + lr][kb & 3];
-        if constexpr (kPow2) {
+        const int cb = (kb / C::kScaleChunk) & 1, piece = (kb >> 2) & (C::kScalePieces - 1);
+        const float *sa_lane = &L.chunks.v[cb][piece][wm * C::WM + lr][kb & 3];
+        if constexpr (C::kRowScaledW) {
+            const float *sw_lane = &L.wchunks.v[cb][piece][wn * C::WN + 4 * lk][kb & 3];
+#pragma unroll
+            for (int i = 0; i < C::kTM; ++i) sc[i] = sa_lane[64 * i];
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) swr[j][e] = sw_lane[4 * (16 * j + e)];
+        } else if constexpr (kPow2) {
 #pragma unroll
             for (int i = 0; i < C::kTM; ++i) sc[i] = e8m0_code(sa_lane[64 * i]);
 #pragma unroll
@@ -465,11 +519,17 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         // the VALU FMAs never wait on the MFMA that produced their operand, and
         // the next A fragment is read from LDS one row of tiles ahead.
         auto promote = [&](int i, int j, const v4f &p) {
-            const float f = scale(i, j);
-            acc[i][j][0] = __builtin_fmaf(p[0], f, acc[i][j][0]);
-            acc[i][j][1] = __builtin_fmaf(p[1], f, acc[i][j][1]);
-            acc[i][j][2] = __builtin_fmaf(p[2], f, acc[i][j][2]);
-            acc[i][j][3] = __builtin_fmaf(p[3], f, acc[i][j][3]);
+            if constexpr (C::kRowScaledW) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[i][j][e] = __builtin_fmaf(p[e], sc[i] * swr[j][e], acc[i][j][e]);
+            } else {
+                const float f = scale(i, j);
+                acc[i][j][0] = __builtin_fmaf(p[0], f, acc[i][j][0]);
+                acc[i][j][1] = __builtin_fmaf(p[1], f, acc[i][j][1]);
+                acc[i][j][2] = __builtin_fmaf(p[2], f, acc[i][j][2]);
+                acc[i][j][3] = __builtin_fmaf(p[3], f, acc[i][j][3]);
+            }
         };
         v8i af;
         if constexpr (kSplit)
@@ -718,6 +778,11 @@ using BigTile = TileCfg<256, 256, 2, 4, 2>;
 using NarrowTile = TileCfg<256, 192, 2, 4, 2>;
 using SmallTile = TileCfg<128, 64, 2, 2, 4>;
 using MidTile = TileCfg<128, 256, 2, 4, 3>;
+// Wgrad: both operands carry one scale per row and K block (128x1 token
+// groups of dY and X, transposed).  128 x 256 tiles on 8 waves with three
+// stages, and scale chunks of 4 K blocks for both operands so the W row
+// chunks fit in LDS beside the stages.
+using WgradTile = TileCfg<128, 256, 2, 4, 3, 1, true>;
 
 // Logical tile index of this workgroup after the XCD remap (gridDim.x is a
 // multiple of 8; each XCD gets a contiguous range of logical tiles).
@@ -1104,6 +1169,27 @@ hipError_t launch_block_gemm(const void *a, const float *sa, const void *w, cons
                         : block_gemm<kOutF32, true>(p, pl, c, stream);
     return bf16_out ? block_gemm<kOutBF16, false>(p, pl, c, stream)
                     : block_gemm<kOutF32, false>(p, pl, c, stream);
+}
+
+hipError_t launch_block_gemm_wgrad(const void *a, const float *sa, const void *b,
+                                   const float *sb, void *c, bool bf16_out, int64_t M, int64_t N,
+                                   int64_t K, hipStream_t stream) {
+    GemmParams p{};
+    p.a = static_cast<const uint8_t *>(a);
+    p.sa = sa;
+    p.w = static_cast<const uint8_t *>(b);
+    p.sw = sb;
+    p.c = c;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.G = (int)(K / 128);
+    p.NB = (int)(N / 128);
+    p.group_m = 8;
+    p.ksplit = 1;
+    p.kb_per_split = p.G;
+    return bf16_out ? launch_dense<WgradTile, kOutBF16, false>(p, stream)
+                    : launch_dense<WgradTile, kOutF32, false>(p, stream);
 }
 
 hipError_t launch_grouped_gemm(const void *a, const float *sa, const void *w, const float *sw,

@@ -15,9 +15,25 @@ hipError_t launch_quant_act_1x128(const void *x, int64_t M, int64_t K, void *q, 
 hipError_t launch_quant_weight_128x128(const void *w, int64_t N, int64_t K, void *q,
                                        float *scales, bool pow2, hipStream_t stream);
 
+// 128x1 tiles (128 rows of one column) of x [M][K], written transposed:
+// q_t [K][M], scales_t [K][ceil(M/128)].
+hipError_t launch_quant_act_128x1_t(const void *x, int64_t M, int64_t K, void *q_t,
+                                    float *scales_t, hipStream_t stream);
+
+// E4M3 weights [N][K] with 128x128 block scales [ceil(N/128)][ceil(K/128)],
+// transposed: q_t [K][N], scales_t [ceil(K/128)][ceil(N/128)].
+hipError_t launch_transpose_weight(const void *q, const float *s, int64_t N, int64_t K,
+                                   void *q_t, float *s_t, hipStream_t stream);
+
 // Bytes of fp32 split-K partials the dense GEMM would use for this shape
 // (0 when it runs without splitting K).
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+// C[M][N] = sum_kb sa[m][kb] sb[n][kb] sum_{k in kb} a[m][k] b[n][k]: one
+// scale per row and K block on both operands (the Wgrad GEMM).
+hipError_t launch_block_gemm_wgrad(const void *a, const float *sa, const void *b,
+                                   const float *sb, void *c, bool bf16_out, int64_t M, int64_t N,
+                                   int64_t K, hipStream_t stream);
 
 // pow2: every scale is a power of two, applied by the block-scaled MFMA.
 hipError_t launch_block_gemm(const void *a, const float *sa, const void *w, const float *sw,

@@ -203,6 +203,150 @@ __global__ __launch_bounds__(kQuantThreads) void quant_weight_kernel(
 
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// 128x1 tiles written transposed (the Wgrad operands: 128 tokens of one
+// channel per group, token axis contiguous in the output).  A workgroup
+// takes 128 rows x 64 columns of x [M][K]: the rows go to LDS as fp32
+// (16-byte loads when kVec: K % 8 == 0, x 16-byte aligned), then four
+// lanes per column take 32 rows each, reduce the column's amax over its
+// 128 rows with two xor shuffles, quantize with the 1x128 kernels' quotient
+// and write 32 consecutive bytes of the transposed row q_t[k][m0 .. +128)
+// (two 16-byte stores when kVecOut: M % 16 == 0, q_t 16-byte aligned).
+// Rows past M load as zero, which leaves every amax unchanged.
+constexpr int kTRows = 128, kTCols = 64;
+
+template <bool kVec, bool kVecOut>
+__global__ __launch_bounds__(kQuantThreads) void quant_act_128x1_t_kernel(
+    const uint16_t *__restrict__ x, uint8_t *__restrict__ q_t, float *__restrict__ scales_t,
+    int64_t M, int64_t K, int64_t GM, int64_t KT) {
+    __shared__ float tile[kTRows][kTCols + 1];
+    const int64_t kt = (int64_t)blockIdx.x % KT, mb = (int64_t)blockIdx.x / KT;
+    const int64_t k0 = kt * kTCols, m0 = mb * kTRows;
+    const int t = threadIdx.x;
+    {
+        const int r = t >> 1, c0 = (t & 1) * 32;
+        const int64_t m = m0 + r;
+        if (kVec) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t k = k0 + c0 + 8 * v;  // K % 8 == 0: all 8 in or all out
+                float f[8];
+                if (m < M && k < K) {
+                    unpack8(*reinterpret_cast<const uint4 *>(x + m * K + k), f);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) f[e] = 0.0f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) tile[r][c0 + 8 * v + e] = f[e];
+            }
+        } else {
+            for (int c = 0; c < 32; ++c) {
+                const int64_t k = k0 + c0 + c;
+                tile[r][c0 + c] =
+                    (m < M && k < K) ? __uint_as_float((uint32_t)x[m * K + k] << 16) : 0.0f;
+            }
+        }
+    }
+    __syncthreads();
+    const int c = t >> 2, part = t & 3;
+    const int64_t k = k0 + c;
+    float f[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        f[i] = tile[32 * part + i][c];
+        amax = fmaxf(amax, fabsf(f[i]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const QuotientCtx qc(amax);
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t o = 0;
+        o = cvt_pk_e4m3<false>(qc(f[4 * j]), qc(f[4 * j + 1]), o);
+        o = cvt_pk_e4m3<true>(qc(f[4 * j + 2]), qc(f[4 * j + 3]), o);
+        w[j] = o;
+    }
+    if (k < K) {
+        const int64_t mq = m0 + 32 * part;
+        const int64_t n = M - mq;  // rows of this part in range
+        uint8_t *dst = q_t + k * M + mq;
+        if (kVecOut && n >= 32) {
+            reinterpret_cast<uint4 *>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            reinterpret_cast<uint4 *>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        } else if (n > 0) {
+            const uint8_t *b = reinterpret_cast<const uint8_t *>(w);
+            const int cnt = n < 32 ? (int)n : 32;
+            for (int i = 0; i < cnt; ++i) dst[i] = b[i];
+        }
+        if (part == 0) scales_t[k * GM + mb] = qc.s;
+    }
+}
+
+// Transpose of E4M3 weights in 128 x 128 tiles through LDS: q [N][K] ->
+// q_t [K][N], and the tile's block scale s[nb][kb] -> s_t[kb][nb] (a block's
+// scale serves whichever way the block is read).  Offline work, once per
+// weight update.  kVec: K % 16 == 0 and N % 16 == 0 with both pointers
+// 16-byte aligned, so rows move as 16-byte vectors.
+template <bool kVec>
+__global__ __launch_bounds__(kQuantThreads) void transpose_weight_kernel(
+    const uint8_t *__restrict__ q, const float *__restrict__ s, uint8_t *__restrict__ q_t,
+    float *__restrict__ s_t, int64_t N, int64_t K, int64_t NB, int64_t G) {
+    __shared__ uint8_t tile[128][128 + 16];
+    const int64_t nb = (int64_t)blockIdx.x / G, kb = (int64_t)blockIdx.x % G;
+    const int64_t n0 = nb * 128, k0 = kb * 128;
+    const int t = threadIdx.x;
+    const int r = t >> 1, h = (t & 1) * 64;
+    {  // tile row r = q row n0 + r, bytes k0 + h .. + 64
+        const int64_t n = n0 + r;
+        if (kVec) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t k = k0 + h + 16 * v;
+                uint4 d = make_uint4(0, 0, 0, 0);
+                if (n < N && k < K) d = *reinterpret_cast<const uint4 *>(q + n * K + k);
+                *reinterpret_cast<uint4 *>(&tile[r][h + 16 * v]) = d;
+            }
+        } else {
+            for (int j = 0; j < 64; ++j) {
+                const int64_t k = k0 + h + j;
+                tile[r][h + j] = (n < N && k < K) ? q[n * K + k] : 0;
+            }
+        }
+    }
+    __syncthreads();
+    {  // q_t row k0 + r, bytes n0 + h .. + 64, gathered from tile column r
+        const int64_t k = k0 + r;
+        if (k < K) {
+            if (kVec) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int64_t n = n0 + h + 16 * v;
+                    if (n < N) {
+                        uint32_t wd[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int b = h + 16 * v + 4 * e;
+                            wd[e] = (uint32_t)tile[b][r] | ((uint32_t)tile[b + 1][r] << 8) |
+                                    ((uint32_t)tile[b + 2][r] << 16) |
+                                    ((uint32_t)tile[b + 3][r] << 24);
+                        }
+                        *reinterpret_cast<uint4 *>(q_t + k * N + n) =
+                            make_uint4(wd[0], wd[1], wd[2], wd[3]);
+                    }
+                }
+            } else {
+                for (int j = 0; j < 64; ++j) {
+                    const int64_t n = n0 + h + j;
+                    if (n < N) q_t[k * N + n] = tile[h + j][r];
+                }
+            }
+        }
+    }
+    if (t == 0) s_t[kb * NB + nb] = s[nb * G + kb];
+}
+
 template <bool kPow2>
 hipError_t quant_act(const void *x, int64_t M, int64_t K, void *q, float *scales,
                      hipStream_t stream) {
@@ -255,6 +399,46 @@ hipError_t launch_quant_act_1x128(const void *x, int64_t M, int64_t K, void *q, 
                                   bool pow2, hipStream_t stream) {
     return pow2 ? quant_act<true>(x, M, K, q, scales, stream)
                 : quant_act<false>(x, M, K, q, scales, stream);
+}
+
+hipError_t launch_quant_act_128x1_t(const void *x, int64_t M, int64_t K, void *q_t,
+                                    float *scales_t, hipStream_t stream) {
+    const int64_t GM = (M + kTRows - 1) / kTRows;
+    const int64_t KT = (K + kTCols - 1) / kTCols;
+    const dim3 grid((unsigned)(GM * KT));
+    const bool vec = (K % 8 == 0) && aligned(x, 16);
+    const bool vec_out = (M % 16 == 0) && aligned(q_t, 16);
+    const uint16_t *xx = static_cast<const uint16_t *>(x);
+    uint8_t *qq = static_cast<uint8_t *>(q_t);
+    if (vec && vec_out)
+        hipLaunchKernelGGL((quant_act_128x1_t_kernel<true, true>), grid, dim3(kQuantThreads), 0,
+                           stream, xx, qq, scales_t, M, K, GM, KT);
+    else if (vec)
+        hipLaunchKernelGGL((quant_act_128x1_t_kernel<true, false>), grid, dim3(kQuantThreads), 0,
+                           stream, xx, qq, scales_t, M, K, GM, KT);
+    else if (vec_out)
+        hipLaunchKernelGGL((quant_act_128x1_t_kernel<false, true>), grid, dim3(kQuantThreads), 0,
+                           stream, xx, qq, scales_t, M, K, GM, KT);
+    else
+        hipLaunchKernelGGL((quant_act_128x1_t_kernel<false, false>), grid, dim3(kQuantThreads), 0,
+                           stream, xx, qq, scales_t, M, K, GM, KT);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_weight(const void *q, const float *s, int64_t N, int64_t K,
+                                   void *q_t, float *s_t, hipStream_t stream) {
+    const int64_t NB = (N + 127) / 128, G = (K + 127) / 128;
+    const dim3 grid((unsigned)(NB * G));
+    const bool vec = K % 16 == 0 && N % 16 == 0 && aligned(q, 16) && aligned(q_t, 16);
+    const uint8_t *qq = static_cast<const uint8_t *>(q);
+    uint8_t *qt = static_cast<uint8_t *>(q_t);
+    if (vec)
+        hipLaunchKernelGGL(transpose_weight_kernel<true>, grid, dim3(kQuantThreads), 0, stream, qq,
+                           s, qt, s_t, N, K, NB, G);
+    else
+        hipLaunchKernelGGL(transpose_weight_kernel<false>, grid, dim3(kQuantThreads), 0, stream,
+                           qq, s, qt, s_t, N, K, NB, G);
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_weight_128x128(const void *w, int64_t N, int64_t K, void *q,

@@ -184,6 +184,63 @@ fp8_status fp8_block_grouped_gemm_pow2(const void *a_e4m3,
                                        size_t workspace_bytes,
                                        void *hip_stream);
 
+/*
+ * Backward pass (page "dssusan.co.kr qna 93378", passages on FP8 in Fprop,
+ * Dgrad and Wgrad with E4M3 on every tensor, on keeping activations in FP8
+ * for the Wgrad GEMM, and on per-group scales along each GEMM's inner
+ * dimension; page "why-be.co.kr as_center 36949", passage recommending
+ * transposed reads of matrices before the MMA).  The grouping along the
+ * transposed axis is a reading:
+ *   - Dgrad, dX[m][k] = sum_n dY[m][n] W[n][k]: dY is quantized in 1x128
+ *     tiles along N by fp8_quant_act_1x128; W keeps its 128x128 blocks and is
+ *     read transposed, so dX = fp8_block_gemm(dY, W^T) with W^T from
+ *     fp8_transpose_weight_128x128 (once per weight update).
+ *   - Wgrad, dW[n][k] = sum_m dY[m][n] X[m][k]: the sum runs over tokens, so
+ *     dY and X are quantized in 128x1 tiles (128 tokens of one channel) and
+ *     written transposed by fp8_quant_act_128x1_t; fp8_block_gemm_wgrad
+ *     multiplies the two with one scale per row and K block on both.
+ */
+
+/*
+ * 128x1 tiles written transposed.
+ *   x_bf16    [M][K] bf16, input
+ *   q_t       [K][M] E4M3 bytes, output: q_t[k][m] is the code of x[m][k]
+ *   scales_t  [K][ceil(M/128)] fp32, output: scales_t[k][g] = fl32(amax/448)
+ *             of x[m][k] for m in [128g, min(128g+128, M))
+ * Quantization rule, sizes, alignment and errors as fp8_quant_act_1x128
+ * (a partial last group holds M % 128 rows).
+ */
+fp8_status fp8_quant_act_128x1_t(const void *x_bf16, int64_t M, int64_t K,
+                                 void *q_t, float *scales_t, void *hip_stream);
+
+/*
+ * Transpose of 128x128-quantized weights (for Dgrad).
+ *   q_e4m3    [N][K] E4M3, scales [ceil(N/128)][ceil(K/128)] fp32, inputs
+ *   q_t       [K][N] E4M3, scales_t [ceil(K/128)][ceil(N/128)] fp32, outputs
+ * Any N, K >= 0.  Errors: FP8_ERR_NULL, FP8_ERR_SHAPE, FP8_ERR_HIP.
+ */
+fp8_status fp8_transpose_weight_128x128(const void *q_e4m3,
+                                        const float *scales, int64_t N,
+                                        int64_t K, void *q_t, float *scales_t,
+                                        void *hip_stream);
+
+/*
+ * Wgrad GEMM on 128x1-grouped operands (as fp8_quant_act_128x1_t writes
+ * them):
+ *   dw[n][k] = sum_g dy_t_scales[n][g] * x_t_scales[k][g]
+ *                    * sum_{m in [128g, 128g+128)} dy_t[n][m] * x_t[k][m]
+ *   dy_t [N][T] E4M3, dy_t_scales [N][T/128]; x_t [K][T] E4M3,
+ *   x_t_scales [K][T/128]; dw [N][K] fp32 or bf16 (RNE), overwritten.
+ * T % 128 == 0 and K % 128 == 0 are required (FP8_ERR_SHAPE; pad the token
+ * axis with zero rows before quantizing), N may be anything >= 0; dy_t,
+ * x_t and dw must be 16-byte aligned (FP8_ERR_ALIGN).  FP32 accumulation in
+ * a fixed order: deterministic.
+ */
+fp8_status fp8_block_gemm_wgrad(const void *dy_t, const float *dy_t_scales,
+                                const void *x_t, const float *x_t_scales,
+                                void *dw, int out_dtype, int64_t N, int64_t K,
+                                int64_t T, void *hip_stream);
+
 /* Workspace bytes that let fp8_block_gemm use its split-K path for this
  * shape (0 when the shape does not use it). */
 size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int out_dtype);

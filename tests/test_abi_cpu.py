@@ -33,6 +33,7 @@ def test_header_declares_the_boundary():
               "fp8_block_grouped_gemm"]
     assert declared_functions() == sorted(
         method + [m + "_pow2" for m in method]
+        + ["fp8_quant_act_128x1_t", "fp8_transpose_weight_128x128", "fp8_block_gemm_wgrad"]
         + ["fp8_gemm_workspace_bytes", "fp8_status_string"])
 
 
@@ -129,6 +130,31 @@ def test_grouped_argument_errors(suffix):
     assert grouped_(lib, ws=A16, wsb=0) == B.FP8_ERR_WORKSPACE
     # T = 0 is a no-op (E = 0 allowed then)
     assert grouped_(lib, T=0, E=0, a=NUL, sa=NUL, off=NUL, c=NUL) == B.FP8_OK
+
+
+def test_backward_argument_errors():
+    lib = B.lib()
+    q = lib.fp8_quant_act_128x1_t
+    assert q(NUL, 4, 128, A16, A16, NUL) == B.FP8_ERR_NULL
+    assert q(A16, -1, 128, A16, A16, NUL) == B.FP8_ERR_SHAPE
+    assert q(NUL, 0, 128, NUL, NUL, NUL) == B.FP8_OK
+    assert q(ctypes.c_void_p(0x10001), 4, 128, A16, A16, NUL) == B.FP8_ERR_ALIGN
+    t = lib.fp8_transpose_weight_128x128
+    assert t(NUL, A16, 128, 128, A16, A16, NUL) == B.FP8_ERR_NULL
+    assert t(A16, A16, -1, 128, A16, A16, NUL) == B.FP8_ERR_SHAPE
+    assert t(NUL, NUL, 0, 128, NUL, NUL, NUL) == B.FP8_OK
+    assert t(A16, ctypes.c_void_p(0x10002), 128, 128, A16, A16, NUL) == B.FP8_ERR_ALIGN
+    w = lib.fp8_block_gemm_wgrad
+
+    def wg(a=A16, sa=A16, b=A16, sb=A16, c=A16, dt=B.FP8_OUT_F32, N=256, K=256, T=512):
+        return w(a, sa, b, sb, c, dt, N, K, T, NUL)
+    assert wg(T=500) == B.FP8_ERR_SHAPE          # the token axis must be whole 128-blocks
+    assert wg(K=200) == B.FP8_ERR_SHAPE
+    assert wg(T=0) == B.FP8_ERR_SHAPE
+    assert wg(dt=9) == B.FP8_ERR_DTYPE
+    assert wg(a=NUL) == B.FP8_ERR_NULL
+    assert wg(c=A8) == B.FP8_ERR_ALIGN
+    assert wg(N=0, a=NUL, sa=NUL, c=NUL) == B.FP8_OK
 
 
 def test_workspace_query():

@@ -1,0 +1,135 @@
+"""GPU parity of the backward-pass pieces (Dgrad and Wgrad).
+
+Page "dssusan.co.kr qna 93378": E4M3 in Fprop, Dgrad and Wgrad; FP8 Wgrad
+keeps activations in FP8; per-group scales along each GEMM's inner
+dimension.  Reading for the transposed axis: Dgrad = forward GEMM of dY
+(1x128 tiles) with the transposed 128x128-quantized weights; Wgrad = GEMM of
+128x1-grouped dY and X, written transposed, with one scale per row on both
+operands.  The 128x1 quantizer and the weight transpose must match the
+oracle bit for bit; the GEMMs must meet the same tolerances as the forward.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fp8_fine_grained_token_amd import binding as B
+from fp8_fine_grained_token_amd import inputs as I
+
+from .gpu_util import check_gemm, dev, dev_bf16, host, log, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = torch()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    yield
+    t.cuda.synchronize()
+
+
+def assert_bytes_and_scales(qg, sg, qo, so, what):
+    nbad = int((qg != qo).sum())
+    sbad = int((sg.view(np.uint32) != so.view(np.uint32)).sum())
+    log(f"  {what}: byte mismatches={nbad} scale mismatches={sbad}")
+    assert nbad == 0 and sbad == 0
+
+
+@pytest.mark.parametrize("M,K", [(128, 64), (300, 200), (129, 130), (1, 5), (4096, 7168),
+                                 (200, 72)])
+def test_quant_128x1_transposed(M, K):
+    # (300, 200): partial token group and partial column tile; (129, 130)
+    # and (1, 5): the scalar load and byte store paths; (200, 72): vector
+    # loads with byte stores (M % 16 != 0)
+    x, _ = I.activations(np.random.default_rng(M + 3 * K), M, K, 0.01, 50.0)
+    qo, so = oracle.quant_act_128x1_t(x)
+    q, s = B.fp8_quant_act_128x1_t(dev_bf16(x))
+    assert_bytes_and_scales(host(q), host(s), qo, so, f"128x1 transposed {M}x{K}")
+
+
+def test_quant_128x1_transposed_zero_and_tiny_groups():
+    x, _ = I.activations(np.random.default_rng(41), 256, 128, 0.0, 1.0)
+    x = x.copy()
+    x[:128, 3] = 0                 # all-zero group: zero scale and bytes
+    x[128:, 5] = 0x8000            # all -0 group
+    x[:128, 7] = 0x0001            # subnormal amax
+    x[128:, 9] = 0x7F7F            # largest bf16
+    qo, so = oracle.quant_act_128x1_t(x)
+    q, s = B.fp8_quant_act_128x1_t(dev_bf16(x))
+    assert_bytes_and_scales(host(q), host(s), qo, so, "128x1 special groups")
+
+
+@pytest.mark.parametrize("N,K", [(256, 512), (200, 130), (7168, 7168), (3, 5), (384, 256)])
+def test_transpose_weight(N, K):
+    w = I.weights(np.random.default_rng(N + K + 7), (N, K))
+    qw, sw = oracle.quant_weight_128x128(w)
+    qo, so = oracle.transpose_weight(qw, sw)
+    q, s = B.fp8_transpose_weight_128x128(dev(qw), dev(sw))
+    assert_bytes_and_scales(host(q), host(s), qo, so, f"weight transpose {N}x{K}")
+
+
+# ---- Dgrad ----------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(64, 256, 384), (4096, 7168, 7168)])
+def test_dgrad_chain(M, N, K):
+    # dX [M][K] = dY [M][N] W [N][K]: GPU quantizer, GPU transpose and the
+    # forward GEMM, against the oracle's chain (bytes compared on the way)
+    rng = np.random.default_rng(M + N + K)
+    dy, _ = I.activations(rng, M, N, 0.0, 1.0)
+    w = I.weights(rng, (N, K))
+    qw, sw = oracle.quant_weight_128x128(w)
+    qdy_o, sdy_o = oracle.quant_act_1x128(dy)
+    qwt_o, swt_o = oracle.transpose_weight(qw, sw)
+    qdy, sdy = B.fp8_quant_act_1x128(dev_bf16(dy))
+    qwt, swt = B.fp8_transpose_weight_128x128(dev(qw), dev(sw))
+    assert_bytes_and_scales(host(qdy), host(sdy), qdy_o, sdy_o, "dY 1x128")
+    assert_bytes_and_scales(host(qwt), host(swt), qwt_o, swt_o, "W^T")
+    rows = np.arange(M) if M <= 256 else np.array([0, 1, 255, 256, 2047, 4095])
+    R = oracle.block_gemm(qdy_o, sdy_o, qwt_o, swt_o, rows)
+    for out in ("f32", "bf16"):
+        c = B.fp8_block_gemm(qdy, sdy, qwt, swt, out_dtype=out)
+        check_gemm(c[torch().from_numpy(rows).cuda()], R, out, f"dgrad {M}x{K}x{N} {out}")
+
+
+# ---- Wgrad ----------------------------------------------------------------------
+
+def wgrad_operands(T, N, K, seed):
+    rng = np.random.default_rng(seed)
+    dy, _ = I.activations(rng, T, N, 0.0, 1.0)
+    x, _ = I.activations(rng, T, K, 0.01, 50.0)
+    return dy, x
+
+
+@pytest.mark.parametrize("T,N,K", [(128, 128, 128), (512, 300, 256), (384, 64, 640)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_wgrad_small(T, N, K, out):
+    dy, x = wgrad_operands(T, N, K, T + N + K)
+    qdy, sdy = oracle.quant_act_128x1_t(dy)     # [N][T]
+    qx, sx = oracle.quant_act_128x1_t(x)        # [K][T]
+    R = oracle.rowscaled_gemm(qdy, sdy, qx, sx)
+    c = B.fp8_block_gemm_wgrad(dev(qdy), dev(sdy), dev(qx), dev(sx), out_dtype=out)
+    check_gemm(c, R, out, f"wgrad {N}x{K} over {T} tokens {out}")
+
+
+def test_wgrad_workload_chain_sampled_rows_and_deterministic():
+    # dW [7168][7168] over 4096 tokens: GPU 128x1 quantizers feed the GPU
+    # GEMM; sampled rows against the oracle chain; repeated calls bitwise
+    # equal
+    T, N, K = 4096, 7168, 7168
+    dy, x = wgrad_operands(T, N, K, 42)
+    qdy, sdy = B.fp8_quant_act_128x1_t(dev_bf16(dy))
+    qx, sx = B.fp8_quant_act_128x1_t(dev_bf16(x))
+    log("  oracle 128x1 quantization of dY and X ...")
+    qdy_o, sdy_o = oracle.quant_act_128x1_t(dy)
+    qx_o, sx_o = oracle.quant_act_128x1_t(x)
+    assert_bytes_and_scales(host(qdy), host(sdy), qdy_o, sdy_o, "dY^T 128x1")
+    assert_bytes_and_scales(host(qx), host(sx), qx_o, sx_o, "X^T 128x1")
+    c0 = B.fp8_block_gemm_wgrad(qdy, sdy, qx, sx, out_dtype="f32")
+    c1 = B.fp8_block_gemm_wgrad(qdy, sdy, qx, sx, out_dtype="f32")
+    assert torch().equal(c0, c1)
+    rows = np.array([0, 1, 127, 128, 3583, 3584, 7167])
+    log(f"  oracle Wgrad on {rows.size} rows of 7168x7168 over 4096 tokens ...")
+    R = oracle.rowscaled_gemm(qdy_o, sdy_o, qx_o, sx_o, rows)
+    check_gemm(c0[torch().from_numpy(rows).cuda()], R, "f32", "wgrad workload rows")
