@@ -205,45 +205,49 @@ inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 
 // 128x1 tiles written transposed (the Wgrad operands: 128 tokens of one
 // channel per group, token axis contiguous in the output).  A workgroup
-// takes 128 rows x 64 columns of x [M][K]: the rows go to LDS as fp32
+// takes 128 rows x 128 columns of x [M][K] (256 contiguous bytes of each
+// row: wider row pieces read HBM pages more fully): the rows go to LDS as bf16
 // (16-byte loads when kVec: K % 8 == 0, x 16-byte aligned), then four
 // lanes per column take 32 rows each, reduce the column's amax over its
 // 128 rows with two xor shuffles, quantize with the 1x128 kernels' quotient
 // and write 32 consecutive bytes of the transposed row q_t[k][m0 .. +128)
 // (two 16-byte stores when kVecOut: M % 16 == 0, q_t 16-byte aligned).
-// Rows past M load as zero, which leaves every amax unchanged.
-constexpr int kTRows = 128, kTCols = 64;
+// Rows past M load as zero, which leaves every amax unchanged.  Keeping the
+// tile as bf16 (33 KiB of LDS) lets twice as many workgroups share a CU as
+// fp32 would, and each one waits on its loads and stores in turn.
+constexpr int kTRows = 128, kTCols = 128;
+constexpr int kTThreads = 4 * kTCols;  // four lanes per column
+constexpr int kTPitch = kTCols + 4;    // bf16 per LDS row: 8-byte aligned rows
 
 template <bool kVec, bool kVecOut>
-__global__ __launch_bounds__(kQuantThreads) void quant_act_128x1_t_kernel(
+__global__ __launch_bounds__(kTThreads) void quant_act_128x1_t_kernel(
     const uint16_t *__restrict__ x, uint8_t *__restrict__ q_t, float *__restrict__ scales_t,
     int64_t M, int64_t K, int64_t GM, int64_t KT) {
-    __shared__ float tile[kTRows][kTCols + 1];
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kTRows][kTPitch];
     const int64_t kt = (int64_t)blockIdx.x % KT, mb = (int64_t)blockIdx.x / KT;
     const int64_t k0 = kt * kTCols, m0 = mb * kTRows;
     const int t = threadIdx.x;
     {
-        const int r = t >> 1, c0 = (t & 1) * 32;
+        const int r = t / (kTCols / 32), c0 = (t % (kTCols / 32)) * 32;
         const int64_t m = m0 + r;
         if (kVec) {
+            uint4 d[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int64_t k = k0 + c0 + 8 * v;  // K % 8 == 0: all 8 in or all out
-                float f[8];
-                if (m < M && k < K) {
-                    unpack8(*reinterpret_cast<const uint4 *>(x + m * K + k), f);
-                } else {
+                d[v] = (m < M && k < K) ? *reinterpret_cast<const uint4 *>(x + m * K + k)
+                                        : make_uint4(0, 0, 0, 0);
+            }
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) f[e] = 0.0f;
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) tile[r][c0 + 8 * v + e] = f[e];
+            for (int v = 0; v < 4; ++v) {
+                uint2 *row = reinterpret_cast<uint2 *>(&tile[r][c0 + 8 * v]);  // 8-byte aligned
+                row[0] = make_uint2(d[v].x, d[v].y);
+                row[1] = make_uint2(d[v].z, d[v].w);
             }
         } else {
             for (int c = 0; c < 32; ++c) {
                 const int64_t k = k0 + c0 + c;
-                tile[r][c0 + c] =
-                    (m < M && k < K) ? __uint_as_float((uint32_t)x[m * K + k] << 16) : 0.0f;
+                tile[r][c0 + c] = (m < M && k < K) ? x[m * K + k] : (uint16_t)0;
             }
         }
     }
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_128x1_t_kernel(
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        f[i] = tile[32 * part + i][c];
+        f[i] = __uint_as_float((uint32_t)tile[32 * part + i][c] << 16);
         amax = fmaxf(amax, fabsf(f[i]));
     }
     amax = fmaxf(amax, __shfl_xor(amax, 1));
@@ -411,16 +415,16 @@ hipError_t launch_quant_act_128x1_t(const void *x, int64_t M, int64_t K, void *q
     const uint16_t *xx = static_cast<const uint16_t *>(x);
     uint8_t *qq = static_cast<uint8_t *>(q_t);
     if (vec && vec_out)
-        hipLaunchKernelGGL((quant_act_128x1_t_kernel<true, true>), grid, dim3(kQuantThreads), 0,
+        hipLaunchKernelGGL((quant_act_128x1_t_kernel<true, true>), grid, dim3(kTThreads), 0,
                            stream, xx, qq, scales_t, M, K, GM, KT);
     else if (vec)
-        hipLaunchKernelGGL((quant_act_128x1_t_kernel<true, false>), grid, dim3(kQuantThreads), 0,
+        hipLaunchKernelGGL((quant_act_128x1_t_kernel<true, false>), grid, dim3(kTThreads), 0,
                            stream, xx, qq, scales_t, M, K, GM, KT);
     else if (vec_out)
-        hipLaunchKernelGGL((quant_act_128x1_t_kernel<false, true>), grid, dim3(kQuantThreads), 0,
+        hipLaunchKernelGGL((quant_act_128x1_t_kernel<false, true>), grid, dim3(kTThreads), 0,
                            stream, xx, qq, scales_t, M, K, GM, KT);
     else
-        hipLaunchKernelGGL((quant_act_128x1_t_kernel<false, false>), grid, dim3(kQuantThreads), 0,
+        hipLaunchKernelGGL((quant_act_128x1_t_kernel<false, false>), grid, dim3(kTThreads), 0,
                            stream, xx, qq, scales_t, M, K, GM, KT);
     return hipGetLastError();
 }
