@@ -19,6 +19,10 @@ inline hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
 constexpr int64_t kMaxTiles = (int64_t)1 << 30;
+// GEMM inner dimension: a tile's 256 operand rows of K bytes are addressed
+// through one buffer resource, whose byte range and offsets are 32-bit, so
+// 256 K < 2^32.
+constexpr int64_t kMaxInner = (int64_t)1 << 24;
 
 fp8_status check_quant(const void *x, int64_t R, int64_t K, const void *q, const float *s) {
     if (R < 0 || K < 0) return FP8_ERR_SHAPE;
@@ -34,7 +38,7 @@ fp8_status check_gemm_common(const void *a, const float *sa, const void *w, cons
     if (out_dtype != FP8_OUT_F32 && out_dtype != FP8_OUT_BF16) return FP8_ERR_DTYPE;
     if (rows < 0 || N < 0 || K < 0) return FP8_ERR_SHAPE;
     if (N % 128 != 0 || K % 128 != 0) return FP8_ERR_SHAPE;
-    if (rows >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return FP8_ERR_SHAPE;
+    if (rows >= kMaxDim || N >= kMaxDim || K >= kMaxInner) return FP8_ERR_SHAPE;
     if (rows * K >= kMaxElems || rows * N >= kMaxElems) return FP8_ERR_SHAPE;
     if (((rows + 127) / 128 + 1) * (N / 128) >= kMaxTiles) return FP8_ERR_SHAPE;
     if ((ws == nullptr) != (ws_bytes == 0)) return FP8_ERR_WORKSPACE;

@@ -96,7 +96,8 @@ fp8_status fp8_quant_weight_128x128(const void *w_bf16, int64_t N, int64_t K,
  *   w_e4m3    [N][K] E4M3, w_scales [N/128][K/128] fp32
  *   c         [M][N], fp32 (FP8_OUT_F32) or bf16 by round-to-nearest-even of
  *             the fp32 accumulator (FP8_OUT_BF16)
- * K % 128 == 0 and N % 128 == 0 are required (FP8_ERR_SHAPE otherwise);
+ * K % 128 == 0, N % 128 == 0 and K < 2^24 are required (FP8_ERR_SHAPE
+ * otherwise; a tile's operand rows are addressed with 32-bit offsets);
  * a_e4m3, w_e4m3 and c must be 16-byte aligned (FP8_ERR_ALIGN).  M may be
  * anything >= 0.
  *   workspace / workspace_bytes: optional caller-owned device scratch
@@ -231,8 +232,9 @@ fp8_status fp8_transpose_weight_128x128(const void *q_e4m3,
  *                    * sum_{m in [128g, 128g+128)} dy_t[n][m] * x_t[k][m]
  *   dy_t [N][T] E4M3, dy_t_scales [N][T/128]; x_t [K][T] E4M3,
  *   x_t_scales [K][T/128]; dw [N][K] fp32 or bf16 (RNE), overwritten.
- * T % 128 == 0 and K % 128 == 0 are required (FP8_ERR_SHAPE; pad the token
- * axis with zero rows before quantizing), N may be anything >= 0; dy_t,
+ * T % 128 == 0, T < 2^24 and K % 128 == 0 are required (FP8_ERR_SHAPE;
+ * pad the token axis with zero rows before quantizing), N may be anything
+ * >= 0; dy_t,
  * x_t and dw must be 16-byte aligned (FP8_ERR_ALIGN).  FP32 accumulation in
  * a fixed order: deterministic.
  */

@@ -107,6 +107,10 @@ def test_gemm_argument_errors(suffix):
     assert gemm_(lib, ws=NUL, wsb=1024) == B.FP8_ERR_WORKSPACE
     assert gemm_(lib, ws=ctypes.c_void_p(0x10010), wsb=1024) == B.FP8_ERR_WORKSPACE
     assert gemm_(lib, K=0) == B.FP8_ERR_SHAPE
+    # inner dimension at or beyond the 32-bit tile addressing (256 K < 2^32);
+    # the largest valid K passes validation (M = 0: a no-op, nothing launches)
+    assert gemm_(lib, K=1 << 24) == B.FP8_ERR_SHAPE
+    assert gemm_(lib, K=(1 << 24) - 128, M=0) == B.FP8_OK
     # M = 0 is a no-op
     assert gemm_(lib, a=NUL, sa=NUL, c=NUL, M=0) == B.FP8_OK
     # dtype is checked before the empty-problem shortcut
@@ -151,6 +155,7 @@ def test_backward_argument_errors():
     assert wg(T=500) == B.FP8_ERR_SHAPE          # the token axis must be whole 128-blocks
     assert wg(K=200) == B.FP8_ERR_SHAPE
     assert wg(T=0) == B.FP8_ERR_SHAPE
+    assert wg(T=1 << 24) == B.FP8_ERR_SHAPE
     assert wg(dt=9) == B.FP8_ERR_DTYPE
     assert wg(a=NUL) == B.FP8_ERR_NULL
     assert wg(c=A8) == B.FP8_ERR_ALIGN
