@@ -204,87 +204,139 @@ __global__ __launch_bounds__(kQuantThreads) void quant_weight_kernel(
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // 128x1 tiles written transposed (the Wgrad operands: 128 tokens of one
-// channel per group, token axis contiguous in the output).  A workgroup
-// takes 128 rows x 128 columns of x [M][K] (256 contiguous bytes of each
-// row: wider row pieces read HBM pages more fully): the rows go to LDS as bf16
-// (16-byte loads when kVec: K % 8 == 0, x 16-byte aligned), then four
-// lanes per column take 32 rows each, reduce the column's amax over its
-// 128 rows with two xor shuffles, quantize with the 1x128 kernels' quotient
-// and write 32 consecutive bytes of the transposed row q_t[k][m0 .. +128)
-// (two 16-byte stores when kVecOut: M % 16 == 0, q_t 16-byte aligned).
-// Rows past M load as zero, which leaves every amax unchanged.  Keeping the
-// tile as bf16 (33 KiB of LDS) lets twice as many workgroups share a CU as
-// fp32 would, and each one waits on its loads and stores in turn.
+// channel per group, token axis contiguous in the output).  A tile is 128
+// rows x 128 columns of x [M][K] (256 contiguous bytes of each row).  Its
+// rows go to LDS as bf16; four lanes per column then take 32 rows each,
+// reduce the column's amax over its 128 rows with two xor shuffles and
+// quantize with the 1x128 kernels' quotient; the E4M3 bytes go to a second
+// LDS tile laid out as the output, q_t[k][m0 .. +128), and leave it in
+// whole 128-byte rows.  Rows past M load as zero, which leaves every amax
+// unchanged.
+//
+// Memory access (kVec: K % 8 == 0 and x 16-byte aligned; kVecOut: M % 16 ==
+// 0 and q_t 16-byte aligned): load instruction v of thread t moves 16-byte
+// chunk (512 v + t) of the tile in row-major order, so a wave reads four
+// whole 256-byte row pieces per instruction; store instruction v writes
+// 16-byte piece (512 v + t) of the output tile, eight whole 128-byte rows
+// per wave.  Without kVec the tile is loaded element by element, without
+// kVecOut stored byte by byte.
+//
+// In the bf16 tile, element (r, c) sits at column c ^ 16 ((r / 32) % 4): the
+// four lanes of a column read rows 32 apart, which the 66-word row pitch
+// maps to one bank group; the swizzle gives each of them its own.
+//
+// Workgroups are persistent: each takes tiles blockIdx.x, + gridDim.x, ...
+// With kVec the next tile's chunks are fetched into registers as soon as
+// the current tile is in LDS, so they are in flight while it is quantized
+// and stored.
 constexpr int kTRows = 128, kTCols = 128;
 constexpr int kTThreads = 4 * kTCols;  // four lanes per column
 constexpr int kTPitch = kTCols + 4;    // bf16 per LDS row: 8-byte aligned rows
+constexpr int kTOutPitch = 9;          // 16-byte pieces per output row in LDS (8 + 1 pad)
+constexpr int kTBlocksPerCU = 2;       // resident workgroups per CU (VGPR-bound)
+constexpr int kTCUs = 256;
+__device__ __forceinline__ int tswz(int r) { return 16 * ((r >> 5) & 3); }
 
 template <bool kVec, bool kVecOut>
 __global__ __launch_bounds__(kTThreads) void quant_act_128x1_t_kernel(
     const uint16_t *__restrict__ x, uint8_t *__restrict__ q_t, float *__restrict__ scales_t,
     int64_t M, int64_t K, int64_t GM, int64_t KT) {
     __shared__ __attribute__((aligned(16))) uint16_t tile[kTRows][kTPitch];
-    const int64_t kt = (int64_t)blockIdx.x % KT, mb = (int64_t)blockIdx.x / KT;
-    const int64_t k0 = kt * kTCols, m0 = mb * kTRows;
+    __shared__ uint4 qs[kTCols][kTOutPitch];
     const int t = threadIdx.x;
-    {
-        const int r = t / (kTCols / 32), c0 = (t % (kTCols / 32)) * 32;
-        const int64_t m = m0 + r;
+    const int64_t ntiles = GM * KT;
+    uint4 d[4];
+    // chunk 512 v + t: tile row (512 v + t) / 16, columns 8 ((512 v + t) % 16) .. + 8
+    auto fetch = [&](int64_t id) {
+        const int64_t m0 = (id / KT) * kTRows, k0 = (id % KT) * kTCols;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int q = kTThreads * v + t;
+            const int64_t m = m0 + (q >> 4), k = k0 + 8 * (q & 15);  // all 8 in or all out
+            d[v] = (m < M && k < K) ? *reinterpret_cast<const uint4 *>(x + m * K + k)
+                                    : make_uint4(0, 0, 0, 0);
+        }
+    };
+    if (kVec && (int64_t)blockIdx.x < ntiles) fetch(blockIdx.x);
+    for (int64_t id = blockIdx.x; id < ntiles; id += gridDim.x) {
+        const int64_t mb = id / KT;
+        const int64_t k0 = (id % KT) * kTCols, m0 = mb * kTRows;
+        __syncthreads();  // every lane is done with the previous tile's LDS
         if (kVec) {
-            uint4 d[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int64_t k = k0 + c0 + 8 * v;  // K % 8 == 0: all 8 in or all out
-                d[v] = (m < M && k < K) ? *reinterpret_cast<const uint4 *>(x + m * K + k)
-                                        : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                uint2 *row = reinterpret_cast<uint2 *>(&tile[r][c0 + 8 * v]);  // 8-byte aligned
+                const int q = kTThreads * v + t, r = q >> 4;
+                uint2 *row = reinterpret_cast<uint2 *>(&tile[r][(8 * (q & 15)) ^ tswz(r)]);
                 row[0] = make_uint2(d[v].x, d[v].y);
                 row[1] = make_uint2(d[v].z, d[v].w);
             }
         } else {
+            const int lr = t >> 2, lc0 = (t & 3) * 32;
+            const int64_t m = m0 + lr;
             for (int c = 0; c < 32; ++c) {
-                const int64_t k = k0 + c0 + c;
-                tile[r][c0 + c] = (m < M && k < K) ? x[m * K + k] : (uint16_t)0;
+                const int64_t k = k0 + lc0 + c;
+                tile[lr][(lc0 + c) ^ tswz(lr)] = (m < M && k < K) ? x[m * K + k] : (uint16_t)0;
             }
         }
-    }
-    __syncthreads();
-    const int c = t >> 2, part = t & 3;
-    const int64_t k = k0 + c;
-    float f[32];
-    float amax = 0.0f;
+        __syncthreads();
+        if (kVec && id + gridDim.x < ntiles) fetch(id + gridDim.x);
+
+        const int c = t >> 2, part = t & 3;
+        float f[32];
+        float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        f[i] = __uint_as_float((uint32_t)tile[32 * part + i][c] << 16);
-        amax = fmaxf(amax, fabsf(f[i]));
-    }
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const QuotientCtx qc(amax);
-    uint32_t w[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        uint32_t o = 0;
-        o = cvt_pk_e4m3<false>(qc(f[4 * j]), qc(f[4 * j + 1]), o);
-        o = cvt_pk_e4m3<true>(qc(f[4 * j + 2]), qc(f[4 * j + 3]), o);
-        w[j] = o;
-    }
-    if (k < K) {
-        const int64_t mq = m0 + 32 * part;
-        const int64_t n = M - mq;  // rows of this part in range
-        uint8_t *dst = q_t + k * M + mq;
-        if (kVecOut && n >= 32) {
-            reinterpret_cast<uint4 *>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-            reinterpret_cast<uint4 *>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
-        } else if (n > 0) {
-            const uint8_t *b = reinterpret_cast<const uint8_t *>(w);
-            const int cnt = n < 32 ? (int)n : 32;
-            for (int i = 0; i < cnt; ++i) dst[i] = b[i];
+        for (int i = 0; i < 32; ++i) {
+            f[i] = __uint_as_float((uint32_t)tile[32 * part + i][c ^ (16 * part)] << 16);
+            amax = fmaxf(amax, fabsf(f[i]));
         }
-        if (part == 0) scales_t[k * GM + mb] = qc.s;
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        // As in the 1x128 kernel: when every column of the wave has amax >=
+        // 2^-60, one branch-free path (constant-division scale, reciprocal +
+        // FMA quotients) serves the wave; otherwise the per-group selection.
+        float y[32], s;
+        if (__all(amax >= 0x1p-60f)) {
+            s = scale_fast(amax);
+            const float r = 1.0f / s;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) y[i] = quot_fast(f[i], s, r);
+        } else {
+            const QuotientCtx qc(amax);
+            s = qc.s;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) y[i] = qc(f[i]);
+        }
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t o = 0;
+            o = cvt_pk_e4m3<false>(y[4 * j], y[4 * j + 1], o);
+            o = cvt_pk_e4m3<true>(y[4 * j + 2], y[4 * j + 3], o);
+            w[j] = o;
+        }
+        qs[c][2 * part] = make_uint4(w[0], w[1], w[2], w[3]);
+        qs[c][2 * part + 1] = make_uint4(w[4], w[5], w[6], w[7]);
+        if (part == 0 && k0 + c < K) scales_t[(k0 + c) * GM + mb] = s;
+        __syncthreads();
+        // piece 512 v + t of the output tile: row (512 v + t) / 8, tokens
+        // 16 ((512 v + t) % 8) .. + 16
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const int q = kTThreads * v + t;
+            const int kk = q >> 3, pc = q & 7;
+            const int64_t k = k0 + kk, m = m0 + 16 * pc;
+            if (k < K && m < M) {
+                const uint4 o = qs[kk][pc];
+                uint8_t *dst = q_t + k * M + m;
+                if (kVecOut) {
+                    *reinterpret_cast<uint4 *>(dst) = o;  // M % 16 == 0: all 16 in range
+                } else {
+                    const uint8_t *b = reinterpret_cast<const uint8_t *>(&o);
+                    const int cnt = M - m < 16 ? (int)(M - m) : 16;
+                    for (int i = 0; i < cnt; ++i) dst[i] = b[i];
+                }
+            }
+        }
     }
 }
 
@@ -409,7 +461,8 @@ hipError_t launch_quant_act_128x1_t(const void *x, int64_t M, int64_t K, void *q
                                     float *scales_t, hipStream_t stream) {
     const int64_t GM = (M + kTRows - 1) / kTRows;
     const int64_t KT = (K + kTCols - 1) / kTCols;
-    const dim3 grid((unsigned)(GM * KT));
+    const int64_t ntiles = GM * KT;
+    const dim3 grid((unsigned)(ntiles < kTCUs * kTBlocksPerCU ? ntiles : kTCUs * kTBlocksPerCU));
     const bool vec = (K % 8 == 0) && aligned(x, 16);
     const bool vec_out = (M % 16 == 0) && aligned(q_t, 16);
     const uint16_t *xx = static_cast<const uint16_t *>(x);
