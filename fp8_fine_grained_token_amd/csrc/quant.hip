@@ -26,89 +26,80 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQuantThreads = 256;
 
-// Fast path: K % 128 == 0, x and q 16-byte aligned.  The tensor is a flat
-// sequence of 128-element groups.  Eight lanes own one group, 16 elements
-// (32 bytes) each: unit c (16 elements) belongs to group c / 8, whose scale
-// index is that group index (scales are [M][K/128]).  A wave streams 2 KiB
-// of bf16 per unit step and stores 1 KiB of E4M3.  When every group of the
-// wave has amax >= 2^-60 (the normal case) a branch-free path runs: scale
-// by constant division, reciprocal by one IEEE divide per lane, and the
-// reciprocal + FMA quotient per element; otherwise the wave takes the
-// general per-group selection (all-zero, tiny or ordinary groups).
-// One unit per thread: more, shorter workgroups keep more of the stream in
-// flight than two or four units per thread (measured ~5% faster on
-// 4096 x 7168).
+// Fast path: K % 128 == 0, x 16-byte and q 8-byte aligned.  The tensor is a
+// flat sequence of 128-element groups (the scale index of a group is its
+// index: scales are [M][K/128]).  A wave takes 4 kFlatLoads consecutive
+// groups in kFlatLoads load instructions: in load h, lane l reads elements
+// 512 h + 8 l .. + 8 of the wave's range, so each instruction reads 1 KiB
+// contiguously, and the 16 lanes of a DPP row hold one group (group 4 h +
+// l / 16 of the wave).  The group maximum is a 16-lane DPP reduction; each
+// lane stores 8 bytes, 512 contiguous bytes per store instruction.  When
+// every group of the wave has amax >= 2^-60 (the normal case) a branch-free
+// path runs: scale by constant division, reciprocal by one IEEE divide per
+// lane, and the reciprocal + FMA quotient per element; otherwise the wave
+// takes the general per-group selection (all-zero, tiny or ordinary
+// groups).
 // kPow2: power-of-two scales (scale_pow2); the reciprocal is then exact and
 // the fast path serves every group with amax > 0.
-constexpr int kFlatUnroll = 1;  // 16-element units per thread per block
+constexpr int kFlatLoads = 2;  // 16-byte loads per lane; 1 or 4 measured slower
 
 template <bool kPow2>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_flat_kernel(
-    const u32x4 *__restrict__ x, u32x4 *__restrict__ q, float *__restrict__ scales,
-    int64_t n_units) {
-    const int64_t base = (int64_t)blockIdx.x * (kQuantThreads * kFlatUnroll) + threadIdx.x;
-    u32x4 v[kFlatUnroll][2];
+    const u32x4 *__restrict__ x, uint2 *__restrict__ q, float *__restrict__ scales,
+    int64_t n_groups) {
+    const int lane = threadIdx.x & 63;
+    const int64_t g0 = ((int64_t)blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6)) * (4 * kFlatLoads);
+    int64_t g[kFlatLoads], chunk[kFlatLoads];
+    bool in[kFlatLoads];
+    u32x4 v[kFlatLoads];
 #pragma unroll
-    for (int u = 0; u < kFlatUnroll; ++u) {
-        const int64_t c = base + (int64_t)u * kQuantThreads;
-        if (c < n_units) {
-            v[u][0] = __builtin_nontemporal_load(x + 2 * c);
-            v[u][1] = __builtin_nontemporal_load(x + 2 * c + 1);
-        } else {
-            v[u][0] = u32x4{0, 0, 0, 0};
-            v[u][1] = u32x4{0, 0, 0, 0};
+    for (int h = 0; h < kFlatLoads; ++h) {
+        g[h] = g0 + 4 * h + (lane >> 4);
+        chunk[h] = g0 * 16 + 64 * h + lane;  // 8-element chunk lane % 16 of group g[h]
+        in[h] = g[h] < n_groups;             // the 16 lanes of a group agree
+        v[h] = in[h] ? __builtin_nontemporal_load(x + chunk[h]) : u32x4{0, 0, 0, 0};
+    }
+    float f[kFlatLoads][8], amax[kFlatLoads];
+#pragma unroll
+    for (int h = 0; h < kFlatLoads; ++h) {
+        unpack8(make_uint4(v[h].x, v[h].y, v[h].z, v[h].w), f[h]);
+        amax[h] = row16_max(absmax8(f[h]));
+    }
+    auto fast_ok = [&](int h) {
+        return !in[h] || (kPow2 ? amax[h] > 0.0f : amax[h] >= 0x1p-60f);
+    };
+    float y[kFlatLoads][8], s[kFlatLoads];
+    bool all_fast = true;
+#pragma unroll
+    for (int h = 0; h < kFlatLoads; ++h) all_fast = all_fast && fast_ok(h);
+    if (__all(all_fast)) {
+#pragma unroll
+        for (int h = 0; h < kFlatLoads; ++h) {
+            s[h] = kPow2 ? scale_pow2(amax[h]) : scale_fast(amax[h]);
+            const float r = 1.0f / s[h];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[h][i] = quot_fast(f[h][i], s[h], r);
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < kFlatLoads; ++h) {
+            const QuotientCtx qc(amax[h], kPow2);
+            s[h] = qc.s;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[h][i] = qc(f[h][i]);
         }
     }
 #pragma unroll
-    for (int u = 0; u < kFlatUnroll; ++u) {
-        const int64_t c = base + (int64_t)u * kQuantThreads;
-        const bool in = c < n_units;
-        float f[16];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const u32x4 t = v[u][h];
-            f[8 * h + 0] = bf16_lo(t.x); f[8 * h + 1] = bf16_hi(t.x);
-            f[8 * h + 2] = bf16_lo(t.y); f[8 * h + 3] = bf16_hi(t.y);
-            f[8 * h + 4] = bf16_lo(t.z); f[8 * h + 5] = bf16_hi(t.z);
-            f[8 * h + 6] = bf16_lo(t.w); f[8 * h + 7] = bf16_hi(t.w);
-        }
-        float m = fabsf(f[0]);
-#pragma unroll
-        for (int i = 1; i < 16; ++i) m = fmaxf(m, fabsf(f[i]));
-        // n_units is a multiple of 8 and groups start at multiples of 8, so
-        // an 8-lane group is entirely in or out of range.
-        const float amax = row8_max(m);
-        float y[16];
-        float s;
-        if (__all(!in || (kPow2 ? amax > 0.0f : amax >= 0x1p-60f))) {
-            s = kPow2 ? scale_pow2(amax) : scale_fast(amax);
-            const float r = 1.0f / s;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) y[i] = quot_fast(f[i], s, r);
-        } else {
-            const QuotientCtx qc(amax, kPow2);
-            s = qc.s;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) y[i] = qc(f[i]);
-        }
-        u32x4 o;
-        uint32_t w0 = 0, w1 = 0, w2 = 0, w3 = 0;
-        w0 = cvt_pk_e4m3<false>(y[0], y[1], w0);
-        w0 = cvt_pk_e4m3<true>(y[2], y[3], w0);
-        w1 = cvt_pk_e4m3<false>(y[4], y[5], w1);
-        w1 = cvt_pk_e4m3<true>(y[6], y[7], w1);
-        w2 = cvt_pk_e4m3<false>(y[8], y[9], w2);
-        w2 = cvt_pk_e4m3<true>(y[10], y[11], w2);
-        w3 = cvt_pk_e4m3<false>(y[12], y[13], w3);
-        w3 = cvt_pk_e4m3<true>(y[14], y[15], w3);
-        o.x = w0;
-        o.y = w1;
-        o.z = w2;
-        o.w = w3;
-        if (in) {
+    for (int h = 0; h < kFlatLoads; ++h) {
+        uint32_t lo = 0, hi = 0;
+        lo = cvt_pk_e4m3<false>(y[h][0], y[h][1], lo);
+        lo = cvt_pk_e4m3<true>(y[h][2], y[h][3], lo);
+        hi = cvt_pk_e4m3<false>(y[h][4], y[h][5], hi);
+        hi = cvt_pk_e4m3<true>(y[h][6], y[h][7], hi);
+        if (in[h]) {
             // default cache policy: the GEMM that follows reads q back
-            q[c] = o;
-            if ((threadIdx.x & 7) == 0) scales[c >> 3] = s;
+            q[chunk[h]] = make_uint2(lo, hi);
+            if ((lane & 15) == 0) scales[g[h]] = s[h];
         }
     }
 }
@@ -408,13 +399,13 @@ hipError_t quant_act(const void *x, int64_t M, int64_t K, void *q, float *scales
                      hipStream_t stream) {
     const int64_t G = (K + kGroup - 1) / kGroup;
     const bool vec = (K % 8 == 0) && aligned(x, 16) && aligned(q, 8);
-    if (K % kGroup == 0 && aligned(x, 16) && aligned(q, 16)) {
-        const int64_t n_units = M * K / 16;
-        const int64_t per_block = (int64_t)kQuantThreads * kFlatUnroll;
-        const int64_t blocks = (n_units + per_block - 1) / per_block;
+    if (K % kGroup == 0 && aligned(x, 16) && aligned(q, 8)) {
+        const int64_t n_groups = M * K / kGroup;
+        const int64_t per_block = (int64_t)(kQuantThreads / 64) * 4 * kFlatLoads;
+        const int64_t blocks = (n_groups + per_block - 1) / per_block;
         hipLaunchKernelGGL(quant_act_flat_kernel<kPow2>, dim3((unsigned)blocks),
                            dim3(kQuantThreads), 0, stream, static_cast<const u32x4 *>(x),
-                           static_cast<u32x4 *>(q), scales, n_units);
+                           static_cast<uint2 *>(q), scales, n_groups);
     } else {
         const int64_t groups = M * G;
         const int64_t per_block = kQuantThreads / 16;
