@@ -47,8 +47,10 @@ def assert_quant_equal(qg, sg, qo, so, what):
 # ---- activation quantizer ---------------------------------------------------
 
 @pytest.mark.parametrize("M,K", [(1, 128), (3, 300), (17, 7168), (64, 1000), (5, 1001),
-                                 (33, 8), (2, 130)])
+                                 (33, 8), (2, 130), (5, 384), (7, 896)])
 def test_quant_act_shapes(M, K):
+    # (5, 384), (7, 896): 15 and 49 groups, so the last wave of the K % 128
+    # == 0 kernel (8 groups per wave) is partly out of range
     x, _ = I.activations(np.random.default_rng(M * 7 + K), M, K, 0.01, 50.0)
     qo, so = oracle.quant_act_1x128(x)
     qg, sg = quant_act_gpu(x)
@@ -88,6 +90,22 @@ def test_quant_act_misaligned_pointer():
     qo, so = oracle.quant_act_1x128(np.ascontiguousarray(x[1:]))
     assert_quant_equal(host(q), host(s), qo, so, "misaligned")
     del t
+
+
+def test_quant_act_output_8_byte_aligned():
+    # E4M3 output at an 8-byte (not 16-byte) offset: the K % 128 == 0 kernel
+    # stores 8 bytes per lane, so it still serves this layout
+    M, K = 12, 640
+    x, _ = I.activations(np.random.default_rng(5), M, K, 0.01, 50.0)
+    t = torch()
+    qbuf = t.full((M * K + 16,), 0x5A, dtype=t.uint8, device="cuda")
+    q = qbuf[8:8 + M * K].view(M, K)
+    s = t.empty((M, K // 128), dtype=t.float32, device="cuda")
+    B.fp8_quant_act_1x128(dev_bf16(x), q, s)
+    qo, so = oracle.quant_act_1x128(x)
+    assert_quant_equal(host(q), host(s), qo, so, "act, 8-byte aligned output")
+    hb = host(qbuf)
+    assert np.all(hb[:8] == 0x5A) and np.all(hb[8 + M * K:] == 0x5A), "bytes outside q written"
 
 
 # ---- weight quantizer ---------------------------------------------------------
