@@ -119,15 +119,6 @@ __device__ __forceinline__ float quot_fast(float x, float s, float r) {
     return __builtin_amdgcn_fmed3f(y, -kE4M3Max, kE4M3Max);
 }
 
-// Max over the 8 lanes of one half DPP row (two quad permutations, then the
-// half-row mirror).
-__device__ __forceinline__ float row8_max(float v) {
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
-    return v;
-}
-
 // Two fp32 -> two OCP E4M3 bytes (gfx950 v_cvt_pk_fp8_f32, round to nearest
 // even) packed into the low (kHi = false) or high 16 bits of `old`.
 template <bool kHi>
