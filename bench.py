@@ -23,7 +23,7 @@ Printed as one JSON line, with:
     on dY and X, Dgrad on the transposed weights, Wgrad over the 4096
     tokens);
   * cpu_baseline: the CPU oracle timed on this host on a bounded sample of
-    the same step (first 256 tokens).
+    the same step (first 512 tokens, ~11 s of CPU work).
 
 Usage: python bench.py [--gpus 1] [--steps 500] [--warmup 300]
        [--no-parts] [--no-cpu-baseline] [--copy-calib]
@@ -50,7 +50,7 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_dense_gemm.json")
 GEMM_SOURCE = os.path.join(ROOT, "fp8_fine_grained_token_amd", "csrc", "gemm.hip")
 
 M, N, K = 4096, 7168, 7168
-CPU_SAMPLE_ROWS = 256
+CPU_SAMPLE_ROWS = 512  # ~11 s of oracle work on 16 host threads
 
 
 def log(msg):
