@@ -335,10 +335,9 @@ __global__ __launch_bounds__(kTThreads) void quant_act_128x1_t_kernel(
 // Transpose of E4M3 weights in 128 x 128 tiles through LDS: q [N][K] ->
 // q_t [K][N], and the tile's block scale s[nb][kb] -> s_t[kb][nb] (a block's
 // scale serves whichever way the block is read).  Offline work, once per
-// weight update.  kVec: K % 16 == 0 and N % 16 == 0 with both pointers
-// 16-byte aligned, so rows move as 16-byte vectors.
-template <bool kVec>
-__global__ __launch_bounds__(kQuantThreads) void transpose_weight_kernel(
+// weight update.  This is the byte-wise path for shapes and pointers the
+// vector kernel below does not take.
+__global__ __launch_bounds__(kQuantThreads) void transpose_weight_scalar_kernel(
     const uint8_t *__restrict__ q, const float *__restrict__ s, uint8_t *__restrict__ q_t,
     float *__restrict__ s_t, int64_t N, int64_t K, int64_t NB, int64_t G) {
     __shared__ uint8_t tile[128][128 + 16];
@@ -348,49 +347,84 @@ __global__ __launch_bounds__(kQuantThreads) void transpose_weight_kernel(
     const int r = t >> 1, h = (t & 1) * 64;
     {  // tile row r = q row n0 + r, bytes k0 + h .. + 64
         const int64_t n = n0 + r;
-        if (kVec) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t k = k0 + h + 16 * v;
-                uint4 d = make_uint4(0, 0, 0, 0);
-                if (n < N && k < K) d = *reinterpret_cast<const uint4 *>(q + n * K + k);
-                *reinterpret_cast<uint4 *>(&tile[r][h + 16 * v]) = d;
-            }
-        } else {
-            for (int j = 0; j < 64; ++j) {
-                const int64_t k = k0 + h + j;
-                tile[r][h + j] = (n < N && k < K) ? q[n * K + k] : 0;
-            }
+        for (int j = 0; j < 64; ++j) {
+            const int64_t k = k0 + h + j;
+            tile[r][h + j] = (n < N && k < K) ? q[n * K + k] : 0;
         }
     }
     __syncthreads();
     {  // q_t row k0 + r, bytes n0 + h .. + 64, gathered from tile column r
         const int64_t k = k0 + r;
         if (k < K) {
-            if (kVec) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int64_t n = n0 + h + 16 * v;
-                    if (n < N) {
-                        uint32_t wd[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int b = h + 16 * v + 4 * e;
-                            wd[e] = (uint32_t)tile[b][r] | ((uint32_t)tile[b + 1][r] << 8) |
-                                    ((uint32_t)tile[b + 2][r] << 16) |
-                                    ((uint32_t)tile[b + 3][r] << 24);
-                        }
-                        *reinterpret_cast<uint4 *>(q_t + k * N + n) =
-                            make_uint4(wd[0], wd[1], wd[2], wd[3]);
-                    }
-                }
-            } else {
-                for (int j = 0; j < 64; ++j) {
-                    const int64_t n = n0 + h + j;
-                    if (n < N) q_t[k * N + n] = tile[h + j][r];
-                }
+            for (int j = 0; j < 64; ++j) {
+                const int64_t n = n0 + h + j;
+                if (n < N) q_t[k * N + n] = tile[h + j][r];
             }
         }
+    }
+    if (t == 0) s_t[kb * NB + nb] = s[nb * G + kb];
+}
+
+// Vector path (K % 16 == 0 and N % 16 == 0, q and q_t 16-byte aligned).  A
+// workgroup of 256 threads moves one 128 x 128-byte tile:
+//   - load v of thread t brings 16-byte chunk 256 v + t of the tile in
+//     row-major order (a wave reads eight whole 128-byte rows per
+//     instruction) into an LDS tile of 32-bit words, where word (r, c) sits
+//     in row r ^ ((r / 16) % 2) at column c ^ 8 ((r / 32) % 4);
+//   - thread t then reads the 16 x 4-byte block of rows 16 (t % 8) .. + 16
+//     and byte columns 4 (t / 8) .. + 4 as 16 words (the row and column
+//     swizzles put the wave's 64 reads on 64 different banks) and
+//     transposes it in registers with byte permutes, four 4 x 4 blocks of
+//     eight v_perm_b32 each;
+//   - it writes the four transposed rows, 16 bytes each, to q_t rows k0 + 4
+//     (t / 8) .. + 4 at bytes n0 + 16 (t % 8): a wave's store instruction
+//     fills eight whole 128-byte rows.
+__device__ __forceinline__ int wt_row(int r) { return r ^ ((r >> 4) & 1); }
+__device__ __forceinline__ int wt_col(int r, int c) { return c ^ (8 * ((r >> 5) & 3)); }
+
+__global__ __launch_bounds__(kQuantThreads) void transpose_weight_kernel(
+    const uint8_t *__restrict__ q, const float *__restrict__ s, uint8_t *__restrict__ q_t,
+    float *__restrict__ s_t, int64_t N, int64_t K, int64_t NB, int64_t G) {
+    __shared__ __attribute__((aligned(16))) uint32_t tile[128][32];
+    const int64_t nb = (int64_t)blockIdx.x / G, kb = (int64_t)blockIdx.x % G;
+    const int64_t n0 = nb * 128, k0 = kb * 128;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int c = kQuantThreads * v + t, r = c >> 3;
+        const int64_t n = n0 + r, k = k0 + 16 * (c & 7);  // all 16 bytes in or all out
+        const uint4 d = (n < N && k < K) ? *reinterpret_cast<const uint4 *>(q + n * K + k)
+                                         : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4 *>(&tile[wt_row(r)][wt_col(r, 4 * (c & 7))]) = d;
+    }
+    __syncthreads();
+    const int g = t & 7, kg = t >> 3;
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = tile[wt_row(16 * g + i)][wt_col(16 * g + i, kg)];
+    // out[j][h]: bytes (rows 16 g + 4 h .. + 4, byte column 4 kg + j).
+    // v_perm_b32 picks result byte i from {src0 (bytes 4-7), src1 (bytes
+    // 0-3)} by selector byte i: first interleave two rows' bytes pairwise,
+    // then pairs of pairs.
+    uint32_t out[4][4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const uint32_t lo01 = __builtin_amdgcn_perm(w[4 * h + 1], w[4 * h], 0x05010400u);
+        const uint32_t hi01 = __builtin_amdgcn_perm(w[4 * h + 1], w[4 * h], 0x07030602u);
+        const uint32_t lo23 = __builtin_amdgcn_perm(w[4 * h + 3], w[4 * h + 2], 0x05010400u);
+        const uint32_t hi23 = __builtin_amdgcn_perm(w[4 * h + 3], w[4 * h + 2], 0x07030602u);
+        out[0][h] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);
+        out[1][h] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+        out[2][h] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+        out[3][h] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+    }
+    const int64_t n = n0 + 16 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t k = k0 + 4 * kg + j;
+        if (k < K && n < N)  // N % 16 == 0: all 16 bytes in range
+            *reinterpret_cast<uint4 *>(q_t + k * N + n) =
+                make_uint4(out[j][0], out[j][1], out[j][2], out[j][3]);
     }
     if (t == 0) s_t[kb * NB + nb] = s[nb * G + kb];
 }
@@ -482,10 +516,10 @@ hipError_t launch_transpose_weight(const void *q, const float *s, int64_t N, int
     const uint8_t *qq = static_cast<const uint8_t *>(q);
     uint8_t *qt = static_cast<uint8_t *>(q_t);
     if (vec)
-        hipLaunchKernelGGL(transpose_weight_kernel<true>, grid, dim3(kQuantThreads), 0, stream, qq,
-                           s, qt, s_t, N, K, NB, G);
+        hipLaunchKernelGGL(transpose_weight_kernel, grid, dim3(kQuantThreads), 0, stream, qq, s,
+                           qt, s_t, N, K, NB, G);
     else
-        hipLaunchKernelGGL(transpose_weight_kernel<false>, grid, dim3(kQuantThreads), 0, stream,
+        hipLaunchKernelGGL(transpose_weight_scalar_kernel, grid, dim3(kQuantThreads), 0, stream,
                            qq, s, qt, s_t, N, K, NB, G);
     return hipGetLastError();
 }

@@ -61,8 +61,11 @@ def test_quant_128x1_transposed_zero_and_tiny_groups():
     assert_bytes_and_scales(host(q), host(s), qo, so, "128x1 special groups")
 
 
-@pytest.mark.parametrize("N,K", [(256, 512), (200, 130), (7168, 7168), (3, 5), (384, 256)])
+@pytest.mark.parametrize("N,K", [(256, 512), (200, 130), (7168, 7168), (3, 5), (384, 256),
+                                 (208, 336), (1040, 144)])
 def test_transpose_weight(N, K):
+    # (200, 130), (3, 5): the byte-wise kernel; the rest the vector kernel,
+    # (208, 336) and (1040, 144) with partial edge tiles
     w = I.weights(np.random.default_rng(N + K + 7), (N, K))
     qw, sw = oracle.quant_weight_128x128(w)
     qo, so = oracle.transpose_weight(qw, sw)
