@@ -20,8 +20,8 @@ Printed as one JSON line, with:
     GB/s vs HBM), the power-of-two-scale variants (quantizer, dense and
     grouped GEMM on the block-scaled MFMA) on the same workloads, and the
     backward pass of the same linear layer (the 128x1 transposed quantizer
-    on dY and X, Dgrad on the transposed weights, Wgrad over the 4096
-    tokens);
+    on dY and X, the weight transpose, Dgrad on the transposed weights,
+    Wgrad over the 4096 tokens);
   * cpu_baseline: the CPU oracle timed on this host on a bounded sample of
     the same step (first 512 tokens, ~11 s of CPU work).
 
@@ -210,6 +210,11 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
         "us": ms * 1e3, "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
     qdy, sdy = F.fp8_quant_act_1x128(dy)
     qwt, swt = F.fp8_transpose_weight_128x128(qw, sw)
+    # the weight transpose Dgrad reads, once per weight update
+    ms = timed(lambda: F.fp8_transpose_weight_128x128(qw, sw, qwt, swt), iters)
+    b = 2 * N * K + 2 * 4 * (N // 128) * (K // 128)
+    parts["bwd_transpose_weight_7168x7168"] = {
+        "us": ms * 1e3, "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
     dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
     ms = timed(lambda: F.fp8_block_gemm(qdy, sdy, qwt, swt, out_dtype="bf16", c=dx), iters)
     parts["bwd_dgrad_4096x7168x7168"] = {
