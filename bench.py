@@ -120,6 +120,16 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
     flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
     parts = {}
 
+    spread_us = {}  # p10 / p90 of the last measurement, in µs
+
+    def set_spread(v_ms):
+        v = sorted(v_ms)
+        spread_us["p10_us"] = v[int(0.1 * (len(v) - 1))] * 1e3
+        spread_us["p90_us"] = v[int(0.9 * (len(v) - 1) + 0.5)] * 1e3
+
+    def spread():
+        return dict(spread_us)
+
     def timed(fn, n):
         t = Timer(torch, n)
         for _ in range(n):
@@ -128,13 +138,14 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
             fn()
             t.stop()
         torch.cuda.synchronize()
+        set_spread([a.elapsed_time(b) for a, b in t.ev[: t.i]])
         return t.median_ms()
 
     # activation quantizer, 4096 x 7168
     ms = timed(lambda: F.fp8_quant_act_1x128(X, qa, sa), iters)
     b = quant_bytes(M, K)
     parts["act_quant_4096x7168"] = {
-        "us": ms * 1e3, "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
+        "us": ms * 1e3, **spread(), "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
         "bytes": b}
 
     # context: a plain device copy moving the quantizer's byte count
@@ -143,7 +154,7 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
     dst = torch.empty_like(src)
     ms = timed(lambda: dst.copy_(src), iters)
     parts["copy_reference_same_bytes"] = {
-        "us": ms * 1e3, "GB/s": 2 * src.numel() / ms / 1e6,
+        "us": ms * 1e3, **spread(), "GB/s": 2 * src.numel() / ms / 1e6,
         "frac_hbm": 2 * src.numel() / ms / 1e6 / PEAK_HBM_GBS}
     del src, dst
 
@@ -153,7 +164,7 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
     # still reads its input from HBM, while the launch latency that a
     # single timed launch includes overlaps the previous kernel.
     def back_to_back(fns, rounds=8, reps=5):
-        best = None
+        per_rep = []
         for _ in range(reps):
             flush.sum()
             a = torch.cuda.Event(enable_timing=True)
@@ -164,29 +175,29 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
                     fn()
             b.record()
             torch.cuda.synchronize()
-            ms = a.elapsed_time(b) / (rounds * len(fns))
-            best = ms if best is None else min(best, ms)
-        return best
+            per_rep.append(a.elapsed_time(b) / (rounds * len(fns)))
+        set_spread(per_rep)
+        return min(per_rep)
 
     sets = [(X.clone(), torch.empty_like(qa), torch.empty_like(sa)) for _ in range(6)]
     ms = back_to_back([lambda s=s: F.fp8_quant_act_1x128(s[0], s[1], s[2]) for s in sets])
     b = quant_bytes(M, K)
     parts["act_quant_4096x7168_back_to_back"] = {
-        "us": ms * 1e3, "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
+        "us": ms * 1e3, **spread(), "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
         "launches": "6 sets x 8 rounds, best of 5"}
     del sets
     pairs = [(torch.empty(b // 2, dtype=torch.uint8, device="cuda"),
               torch.empty(b // 2, dtype=torch.uint8, device="cuda")) for _ in range(6)]
     ms = back_to_back([lambda p=p: p[1].copy_(p[0]) for p in pairs])
     parts["copy_reference_same_bytes_back_to_back"] = {
-        "us": ms * 1e3, "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+        "us": ms * 1e3, **spread(), "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
     del pairs
 
     # dense GEMM alone, 4096 x 7168 x 7168
     ms = timed(lambda: F.fp8_block_gemm(qa, sa, qw, sw, out_dtype="bf16", c=C), iters)
     fl = 2 * M * N * K
     parts["dense_gemm_4096x7168x7168"] = {
-        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
+        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
 
     # power-of-two scales: quantizer and dense GEMM on the same workload
     pa, psa = F.fp8_quant_act_1x128_pow2(X)
@@ -194,10 +205,10 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
     ms = timed(lambda: F.fp8_quant_act_1x128_pow2(X, pa, psa), iters)
     b = quant_bytes(M, K)
     parts["pow2_act_quant_4096x7168"] = {
-        "us": ms * 1e3, "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+        "us": ms * 1e3, **spread(), "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
     ms = timed(lambda: F.fp8_block_gemm_pow2(pa, psa, pw, psw, out_dtype="bf16", c=C), iters)
     parts["pow2_dense_gemm_4096x7168x7168"] = {
-        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
+        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
     del pa, psa, pw, psw
 
     # backward of the same layer: dY [4096][7168] (same distribution as X
@@ -207,25 +218,25 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
     ms = timed(lambda: F.fp8_quant_act_128x1_t(dy), iters)
     b = quant_bytes(M, N)
     parts["bwd_quant_128x1_t_4096x7168"] = {
-        "us": ms * 1e3, "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+        "us": ms * 1e3, **spread(), "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
     qdy, sdy = F.fp8_quant_act_1x128(dy)
     qwt, swt = F.fp8_transpose_weight_128x128(qw, sw)
     # the weight transpose Dgrad reads, once per weight update
     ms = timed(lambda: F.fp8_transpose_weight_128x128(qw, sw, qwt, swt), iters)
     b = 2 * N * K + 2 * 4 * (N // 128) * (K // 128)
     parts["bwd_transpose_weight_7168x7168"] = {
-        "us": ms * 1e3, "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
+        "us": ms * 1e3, **spread(), "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
     dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
     ms = timed(lambda: F.fp8_block_gemm(qdy, sdy, qwt, swt, out_dtype="bf16", c=dx), iters)
     parts["bwd_dgrad_4096x7168x7168"] = {
-        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
+        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
     qdy_t, sdy_t = F.fp8_quant_act_128x1_t(dy)
     qx_t, sx_t = F.fp8_quant_act_128x1_t(X)
     dw = torch.empty((N, K), dtype=torch.float32, device="cuda")
     ms = timed(lambda: F.fp8_block_gemm_wgrad(qdy_t, sdy_t, qx_t, sx_t, out_dtype="f32", dw=dw),
                iters)
     parts["bwd_wgrad_7168x7168_over_4096"] = {
-        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
+        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
     del dy, qdy, sdy, qwt, swt, dx, qdy_t, sdy_t, qx_t, sx_t, dw
 
     # decode GEMM, 256 x 2048 x 7168 (split-K with workspace)
@@ -242,7 +253,7 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
     fl = 2 * 256 * 2048 * 7168
     b = dense_gemm_bytes(256, 2048, 7168)
     parts["decode_gemm_256x2048x7168"] = {
-        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
+        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
         "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
         "split_k_workspace_bytes": nbytes}
     # back to back, as a decode step calls one layer after another: 40
@@ -253,7 +264,7 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
                                                     c=s[4], workspace=ws) for s in sets],
                       rounds=2)
     parts["decode_gemm_256x2048x7168_back_to_back"] = {
-        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
+        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
         "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
         "launches": "40 sets x 2 rounds, best of 5"}
     del sets
@@ -278,7 +289,7 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
     b = (gi.T * gi.K + gi.E * gi.N * gi.K + gi.T * gi.N * 2 + 4 * gi.T * (gi.K // 128)
          + 4 * gi.E * (gi.N // 128) * (gi.K // 128))
     parts["grouped_gemm_e32_t8192_n4096_k7168"] = {
-        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
+        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
         "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
         "counts": [int(c) for c in gi.counts]}
     del gq, gsa, gw, gsw
@@ -295,7 +306,7 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
     ms = timed(lambda: F.fp8_block_grouped_gemm_pow2(gq, gsa, gw, gsw, off, out_dtype="bf16",
                                                      c=gc), iters)
     parts["pow2_grouped_gemm_e32_t8192_n4096_k7168"] = {
-        "us": ms * 1e3, "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
+        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
         "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
     del gq, gsa, gw, gsw, gc, flush
     torch.cuda.empty_cache()
@@ -390,6 +401,7 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     gemm_ms = gemm_t.mean_ms()
     achieved = flops / (gemm_ms * 1e-3) / 1e12
+    props = torch.cuda.get_device_properties(0)
     result = {
         "metric": "FP8 block-scaled GEMM TFLOP/s + % FP8 MFMA peak; act-quant GB/s % HBM",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -405,6 +417,11 @@ def main():
                      "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                      "traffic": traffic_from_counters(),
                      "gemm_us": round(gemm_ms * 1e3, 2)},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                   "compute_units": props.multi_processor_count,
+                   "memory_bytes": props.total_memory},
+        "inputs_sha256": {"X_bf16_4096x7168": hashlib.sha256(X_bits.tobytes()).hexdigest()[:16],
+                          "W_bf16_7168x7168": hashlib.sha256(w_bits.tobytes()).hexdigest()[:16]},
     }
     if args.copy_calib:
         result["copy_calibration"] = copy_calibration(torch)
