@@ -184,6 +184,35 @@ def test_gemm_split_k_many_and_uneven_splits(M, N, K, splits, out):
     assert t.equal(c1, c2), "split-K result changed between identical calls"
 
 
+def test_gemm_split_k_workspace_garbage_and_repeats():
+    # The workspace needs no initialization: full of garbage (random bytes,
+    # then all ones) before every call, it must still give the oracle's
+    # result, bit for bit the same on every call (the partials are summed in
+    # a fixed order).
+    t = torch()
+    M, N, K = 200, 512, 7168
+    g = I.gemm_inputs(M, N, K, seed=77, outlier_frac=0.01, outlier_mult=20.0)
+    qa, sa, qw, sw = quantize(g)
+    R = oracle.block_gemm(qa, sa, qw, sw)
+    nbytes = B.fp8_gemm_workspace_bytes(M, N, K, "f32")
+    assert nbytes > 0
+    ws = t.empty(nbytes, dtype=t.uint8, device="cuda")
+    gen = t.Generator(device="cuda")
+    gen.manual_seed(5)
+    outs = []
+    for r in range(6):
+        if r % 2 == 0:
+            ws.random_(0, 256, generator=gen)
+        else:
+            ws.fill_(0xFF)
+        outs.append(run_gemm(qa, sa, qw, sw, "f32", workspace=ws))
+    for _ in range(3):  # and back to back on the same workspace
+        outs.append(run_gemm(qa, sa, qw, sw, "f32", workspace=ws))
+    check_gemm(outs[0], R, "f32", "split-K, garbage workspace")
+    for o in outs[1:]:
+        assert t.equal(o, outs[0]), "split-K result changed between calls"
+
+
 def test_gemm_dense_workload_sampled_rows():
     g = I.config_dense(seed=0)
     qa, sa, qw, sw = quantize(g)
