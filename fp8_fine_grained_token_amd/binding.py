@@ -124,6 +124,25 @@ def _dev(t, name, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _shape(t, name, shape):
+    """The kernels index every buffer by the sizes they are given, so a
+    tensor of another shape would be read or written out of bounds: refuse
+    it here, before anything is launched."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _rank(t, name, n):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != n:
+        raise ValueError(f"{name} must be {n}-dimensional, got shape {tuple(t.shape)}")
+
+
 def _out_code(out_dtype):
     torch = _torch()
     if out_dtype in (torch.float32, "f32", FP8_OUT_F32):
@@ -135,12 +154,15 @@ def _out_code(out_dtype):
 
 def _quant_act(fn, x, q, scales, stream):
     torch = _torch()
+    _rank(x, "x", 2)
     M, K = x.shape
     G = (K + 127) // 128
     if q is None:
         q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((M, G), dtype=torch.float32, device=x.device)
+    _shape(q, "q", (M, K))
+    _shape(scales, "scales", (M, G))
     _check(getattr(lib(), fn)(_dev(x, "x", torch.bfloat16), M, K, _dev(q, "q", torch.uint8),
                               _dev(scales, "scales", torch.float32), _stream_handle(stream)), fn)
     return q, scales
@@ -158,12 +180,15 @@ def fp8_quant_act_1x128_pow2(x, q=None, scales=None, stream=None):
 
 def _quant_weight(fn, w, q, scales, stream):
     torch = _torch()
+    _rank(w, "w", 2)
     N, K = w.shape
     if q is None:
         q = torch.empty((N, K), dtype=torch.uint8, device=w.device)
     if scales is None:
         scales = torch.empty(((N + 127) // 128, (K + 127) // 128), dtype=torch.float32,
                              device=w.device)
+    _shape(q, "q", (N, K))
+    _shape(scales, "scales", ((N + 127) // 128, (K + 127) // 128))
     _check(getattr(lib(), fn)(_dev(w, "w", torch.bfloat16), N, K, _dev(q, "q", torch.uint8),
                               _dev(scales, "scales", torch.float32), _stream_handle(stream)), fn)
     return q, scales
@@ -193,11 +218,20 @@ def _workspace_args(workspace):
 
 def _block_gemm(fn, a, sa, w, sw, out_dtype, c, workspace, stream):
     torch = _torch()
+    _rank(a, "a", 2)
+    _rank(w, "w", 2)
     M, K = a.shape
     N = w.shape[0]
     code, tdt = _out_code(out_dtype)
     if c is None:
         c = torch.empty((M, N), dtype=tdt, device=a.device)
+    _shape(w, "w", (N, K))
+    # K and N must be multiples of 128 (the library returns FP8_ERR_SHAPE
+    # otherwise); the scale shapes are checked for those that are
+    if K % 128 == 0 and N % 128 == 0:
+        _shape(sa, "sa", (M, K // 128))
+        _shape(sw, "sw", (N // 128, K // 128))
+    _shape(c, "c", (M, N))
     wp, wb = _workspace_args(workspace)
     _check(getattr(lib(), fn)(_dev(a, "a", torch.uint8), _dev(sa, "sa", torch.float32),
                               _dev(w, "w", torch.uint8), _dev(sw, "sw", torch.float32),
@@ -219,11 +253,19 @@ def fp8_block_gemm_pow2(a, sa, w, sw, out_dtype="bf16", c=None, workspace=None, 
 
 def _grouped_gemm(fn, a, sa, w, sw, group_offsets, out_dtype, c, workspace, stream):
     torch = _torch()
+    _rank(a, "a", 2)
+    _rank(w, "w", 3)
     T, K = a.shape
     E, N, _ = w.shape
     code, tdt = _out_code(out_dtype)
     if c is None:
         c = torch.empty((T, N), dtype=tdt, device=a.device)
+    _shape(w, "w", (E, N, K))
+    if K % 128 == 0 and N % 128 == 0:
+        _shape(sa, "sa", (T, K // 128))
+        _shape(sw, "sw", (E, N // 128, K // 128))
+    _shape(group_offsets, "group_offsets", (E + 1,))
+    _shape(c, "c", (T, N))
     wp, wb = _workspace_args(workspace)
     _check(getattr(lib(), fn)(_dev(a, "a", torch.uint8), _dev(sa, "sa", torch.float32),
                               _dev(w, "w", torch.uint8), _dev(sw, "sw", torch.float32),
@@ -253,11 +295,14 @@ def fp8_quant_act_128x1_t(x, q_t=None, scales_t=None, stream=None):
     """x: bf16 [M][K] -> (q_t uint8 [K][M], scales_t fp32 [K][ceil(M/128)]):
     128x1 tiles (128 rows of one column), written transposed."""
     torch = _torch()
+    _rank(x, "x", 2)
     M, K = x.shape
     if q_t is None:
         q_t = torch.empty((K, M), dtype=torch.uint8, device=x.device)
     if scales_t is None:
         scales_t = torch.empty((K, (M + 127) // 128), dtype=torch.float32, device=x.device)
+    _shape(q_t, "q_t", (K, M))
+    _shape(scales_t, "scales_t", (K, (M + 127) // 128))
     _check(lib().fp8_quant_act_128x1_t(_dev(x, "x", torch.bfloat16), M, K,
                                        _dev(q_t, "q_t", torch.uint8),
                                        _dev(scales_t, "scales_t", torch.float32),
@@ -269,12 +314,16 @@ def fp8_transpose_weight_128x128(q, scales, q_t=None, scales_t=None, stream=None
     """q: uint8 [N][K] with scales [ceil(N/128)][ceil(K/128)] -> (q_t [K][N],
     scales_t [ceil(K/128)][ceil(N/128)])."""
     torch = _torch()
+    _rank(q, "q", 2)
     N, K = q.shape
     if q_t is None:
         q_t = torch.empty((K, N), dtype=torch.uint8, device=q.device)
     if scales_t is None:
         scales_t = torch.empty(((K + 127) // 128, (N + 127) // 128), dtype=torch.float32,
                                device=q.device)
+    _shape(scales, "scales", ((N + 127) // 128, (K + 127) // 128))
+    _shape(q_t, "q_t", (K, N))
+    _shape(scales_t, "scales_t", ((K + 127) // 128, (N + 127) // 128))
     _check(lib().fp8_transpose_weight_128x128(_dev(q, "q", torch.uint8),
                                               _dev(scales, "scales", torch.float32), N, K,
                                               _dev(q_t, "q_t", torch.uint8),
@@ -289,11 +338,18 @@ def fp8_block_gemm_wgrad(dy_t, dy_t_scales, x_t, x_t_scales, out_dtype="f32", dw
     """dW [N][K] = dY^T X from 128x1-grouped operands written transposed:
     dy_t [N][T], x_t [K][T] (uint8 E4M3), scales [N][T/128] and [K][T/128]."""
     torch = _torch()
+    _rank(dy_t, "dy_t", 2)
+    _rank(x_t, "x_t", 2)
     N, T = dy_t.shape
     K = x_t.shape[0]
     code, tdt = _out_code(out_dtype)
     if dw is None:
         dw = torch.empty((N, K), dtype=tdt, device=dy_t.device)
+    _shape(x_t, "x_t", (K, T))
+    if T % 128 == 0:
+        _shape(dy_t_scales, "dy_t_scales", (N, T // 128))
+        _shape(x_t_scales, "x_t_scales", (K, T // 128))
+    _shape(dw, "dw", (N, K))
     _check(lib().fp8_block_gemm_wgrad(_dev(dy_t, "dy_t", torch.uint8),
                                       _dev(dy_t_scales, "dy_t_scales", torch.float32),
                                       _dev(x_t, "x_t", torch.uint8),
