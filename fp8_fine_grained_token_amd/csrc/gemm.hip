@@ -783,6 +783,11 @@ using MidTile = TileCfg<128, 256, 2, 4, 3>;
 // stages, and scale chunks of 4 K blocks for both operands so the W row
 // chunks fit in LDS beside the stages.
 using WgradTile = TileCfg<128, 256, 2, 4, 3, 1, true>;
+// 128 x 192 on 8 waves (wave tile 64 x 48): covers part of the Wgrad columns
+// when 128 x 256 tiles alone would leave a nearly empty last round (see
+// plan_wgrad_two_kind).  Row-scaled W has a scale per column, so a wave's
+// 48 columns may straddle 128-column boundaries freely.
+using WgradNarrowTile = TileCfg<128, 192, 2, 4, 3, 1, true>;
 
 // Logical tile index of this workgroup after the XCD remap (gridDim.x is a
 // multiple of 8; each XCD gets a contiguous range of logical tiles).
@@ -851,22 +856,14 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int grou
     tn = in / gm;
 }
 
-// Dense GEMM with two tile widths.  When 256 x 256 tiles alone would leave
-// the last round of workgroups partly filled, columns [0, n_split) are
-// covered by 256 x 256 tiles and [n_split, N) by 256 x 192 tiles, chosen so
-// that each kind fills whole rounds (e.g. 4096 x 7168: 256 of each, one of
-// each per CU instead of two 256 x 256 tiles on 192 CUs and one on the
-// rest).  Each XCD takes a contiguous share of each kind, the wide tiles
-// first; the LDS holds either layout.
-template <int OUT, bool kPow2>
-__global__ __launch_bounds__(BigTile::kThreads) void dense_gemm_two_kind_kernel(GemmParams p) {
-    using CB = BigTile;
-    using CN = NarrowTile;
+// Tile of a two-kind plan: slots [0, per1) of each XCD take its contiguous
+// share of the CB tiles (columns [0, n_split)), the rest its share of the CN
+// tiles (columns [n_split, N)).  The wide tiles are dispatched first; the
+// LDS union holds either layout.
+template <class CB, class CN, int OUT, bool kPow2>
+__device__ __forceinline__ void two_kind_tile(const GemmParams &p, TileLds<CB> &lds_b,
+                                              TileLds<CN> &lds_n) {
     static_assert(CB::kThreads == CN::kThreads && CB::BM == CN::BM, "two-kind tiles");
-    __shared__ union DenseLds {
-        TileLds<CB> big;
-        TileLds<CN> narrow;
-    } lds;
     const int t1 = p.tiles_m * p.tn1, t2 = p.tiles_m * p.tn2;
     const int per1 = (t1 + kNumXcd - 1) / kNumXcd, per2 = (t2 + kNumXcd - 1) / kNumXcd;
     const int xcd = blockIdx.x % kNumXcd;
@@ -876,14 +873,41 @@ __global__ __launch_bounds__(BigTile::kThreads) void dense_gemm_two_kind_kernel(
         const int t = xcd * per1 + slot;
         if (t >= t1) return;
         raster(t, p.tiles_m, p.tn1, p.group_m, tm, tn);
-        dense_tile<CB, OUT, kPow2>(p, lds.big, (int64_t)tm * CB::BM, (int64_t)tn * CB::BN);
+        dense_tile<CB, OUT, kPow2>(p, lds_b, (int64_t)tm * CB::BM, (int64_t)tn * CB::BN);
     } else {
         const int t = xcd * per2 + (slot - per1);
         if (slot - per1 >= per2 || t >= t2) return;
         raster(t, p.tiles_m, p.tn2, p.group_m, tm, tn);
-        dense_tile<CN, OUT, kPow2>(p, lds.narrow, (int64_t)tm * CN::BM,
+        dense_tile<CN, OUT, kPow2>(p, lds_n, (int64_t)tm * CN::BM,
                                    p.n_split + (int64_t)tn * CN::BN);
     }
+}
+
+// Dense GEMM with two tile widths.  When 256 x 256 tiles alone would leave
+// the last round of workgroups partly filled, columns [0, n_split) are
+// covered by 256 x 256 tiles and [n_split, N) by 256 x 192 tiles, chosen so
+// that each kind fills whole rounds (e.g. 4096 x 7168: 256 of each, one of
+// each per CU instead of two 256 x 256 tiles on 192 CUs and one on the
+// rest).  Each XCD takes a contiguous share of each kind, the wide tiles
+// first; the LDS holds either layout.
+template <int OUT, bool kPow2>
+__global__ __launch_bounds__(BigTile::kThreads) void dense_gemm_two_kind_kernel(GemmParams p) {
+    __shared__ union DenseLds {
+        TileLds<BigTile> big;
+        TileLds<NarrowTile> narrow;
+    } lds;
+    two_kind_tile<BigTile, NarrowTile, OUT, kPow2>(p, lds.big, lds.narrow);
+}
+
+// Wgrad with 128 x 256 tiles on columns [0, n_split) and 128 x 192 tiles on
+// the rest (plan_wgrad_two_kind).
+template <int OUT>
+__global__ __launch_bounds__(WgradTile::kThreads) void wgrad_two_kind_kernel(GemmParams p) {
+    __shared__ union WgradLds {
+        TileLds<WgradTile> wide;
+        TileLds<WgradNarrowTile> narrow;
+    } lds;
+    two_kind_tile<WgradTile, WgradNarrowTile, OUT, false>(p, lds.wide, lds.narrow);
 }
 
 // Split-K reduction: C = sum over splits in fixed order 0..S-1, then the
@@ -1071,6 +1095,68 @@ bool plan_two_kind(int64_t M, int64_t N, int &tn1, int &tn2) {
     return found;
 }
 
+// Wgrad column split: 128 x 256 tiles on columns [0, 256 a), 128 x 192
+// tiles on the rest (the last one possibly ragged).  With 56 row tiles (7168
+// rows) neither kind can fill whole rounds, so the split is chosen by
+// modelling the dispatch: each XCD's 32 CUs take its share of wide tiles
+// first, then its narrow ones, each tile going to the CU that is free first;
+// a narrow tile costs kWgradNarrowCost of a wide one.  The busiest XCD (the
+// first, whose shares are the largest) sets the finishing time.  A split is
+// used when it finishes at least 3% before the wide tiles alone: for
+// dW 7168 x 7168, a = 16 and b = 16 model at 6.46 wide-tile times against 7.
+constexpr double kWgradNarrowCost = 0.82;
+
+double xcd_finish(int64_t wide, int64_t narrow) {
+    constexpr int kCUsPerXcd = kCUs / kNumXcd;
+    double load[kCUsPerXcd];
+    for (int i = 0; i < kCUsPerXcd; ++i)
+        load[i] = (double)(wide / kCUsPerXcd + (i < wide % kCUsPerXcd ? 1 : 0));
+    for (int64_t j = 0; j < narrow; ++j) {
+        int lo = 0;
+        for (int i = 1; i < kCUsPerXcd; ++i)
+            if (load[i] < load[lo]) lo = i;
+        load[lo] += kWgradNarrowCost;
+    }
+    double end = 0.0;
+    for (int i = 0; i < kCUsPerXcd; ++i) end = load[i] > end ? load[i] : end;
+    return end;
+}
+
+bool plan_wgrad_two_kind(int64_t M, int64_t N, int &tn1, int &tn2) {
+    // the same shapes come back every training step
+    thread_local int64_t last_m = -1, last_n = -1;
+    thread_local int last_a = 0, last_b = 0;
+    if (M == last_m && N == last_n) {
+        tn1 = last_a;
+        tn2 = last_b;
+        return last_b > 0;
+    }
+    const int64_t tm = (M + WgradTile::BM - 1) / WgradTile::BM;
+    const int64_t tn_wide = (N + WgradTile::BN - 1) / WgradTile::BN;
+    const double base = xcd_finish((tm * tn_wide + kNumXcd - 1) / kNumXcd, 0);
+    double best = 0.97 * base;
+    int best_a = (int)tn_wide, best_b = 0;
+    // a grid of at most one round of wide tiles finishes in one tile time
+    // either way
+    const int64_t a_end = tm * tn_wide > kCUs ? (N + WgradTile::BN - 1) / WgradTile::BN : 0;
+    for (int64_t a = 0; a < a_end; ++a) {
+        const int64_t rest = N - WgradTile::BN * a;
+        if (rest <= 0) break;
+        const int64_t b = (rest + WgradNarrowTile::BN - 1) / WgradNarrowTile::BN;
+        const double t = xcd_finish((tm * a + kNumXcd - 1) / kNumXcd, (tm * b + kNumXcd - 1) / kNumXcd);
+        if (t < best) {
+            best = t;
+            best_a = (int)a;
+            best_b = (int)b;
+        }
+    }
+    last_m = M;
+    last_n = N;
+    last_a = tn1 = best_a;
+    last_b = tn2 = best_b;
+    return best_b > 0;
+}
+
 Plan plan_dense(int64_t M, int64_t N, int64_t K) {
     const int G = (int)(K / 128);
     const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
@@ -1188,6 +1274,23 @@ hipError_t launch_block_gemm_wgrad(const void *a, const float *sa, const void *b
     p.group_m = 8;
     p.ksplit = 1;
     p.kb_per_split = p.G;
+    int tn1, tn2;
+    if (plan_wgrad_two_kind(M, N, tn1, tn2)) {
+        p.tiles_m = (int)((M + WgradTile::BM - 1) / WgradTile::BM);
+        p.tn1 = tn1;
+        p.tn2 = tn2;
+        p.n_split = (int64_t)tn1 * WgradTile::BN;
+        const int per1 = (p.tiles_m * tn1 + kNumXcd - 1) / kNumXcd;
+        const int per2 = (p.tiles_m * tn2 + kNumXcd - 1) / kNumXcd;
+        const dim3 grid((unsigned)(kNumXcd * (per1 + per2)));
+        if (bf16_out)
+            hipLaunchKernelGGL((wgrad_two_kind_kernel<kOutBF16>), grid, dim3(WgradTile::kThreads),
+                               0, stream, p);
+        else
+            hipLaunchKernelGGL((wgrad_two_kind_kernel<kOutF32>), grid, dim3(WgradTile::kThreads),
+                               0, stream, p);
+        return hipGetLastError();
+    }
     return bf16_out ? launch_dense<WgradTile, kOutBF16, false>(p, stream)
                     : launch_dense<WgradTile, kOutF32, false>(p, stream);
 }

@@ -116,6 +116,27 @@ def test_wgrad_small(T, N, K, out):
     check_gemm(c, R, out, f"wgrad {N}x{K} over {T} tokens {out}")
 
 
+@pytest.mark.parametrize("T,N,K,rows", [
+    # 9 row tiles x 39 columns of 192-wide tiles (351 tiles, more than one
+    # round; the last column tile covers 128 of its 192 columns, the last row
+    # tile 76 rows)
+    (256, 1100, 7424, [0, 1, 127, 128, 555, 1023, 1024, 1099]),
+    # 16 row tiles: 10 columns of 256-wide tiles, then 22 of 192-wide tiles
+    # from column 2560 (the last row tile 80 rows)
+    (256, 2000, 6784, [0, 127, 128, 1023, 1024, 1919, 1920, 1999]),
+])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_wgrad_two_tile_widths_sampled_rows(T, N, K, rows, out):
+    dy, x = wgrad_operands(T, N, K, T + N + K)
+    qdy, sdy = oracle.quant_act_128x1_t(dy)     # [N][T]
+    qx, sx = oracle.quant_act_128x1_t(x)        # [K][T]
+    rows = np.array(rows)
+    R = oracle.rowscaled_gemm(qdy, sdy, qx, sx, rows)
+    c = B.fp8_block_gemm_wgrad(dev(qdy), dev(sdy), dev(qx), dev(sx), out_dtype=out)
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, out,
+               f"wgrad {N}x{K} over {T} tokens {out}, sampled rows")
+
+
 def test_wgrad_workload_chain_sampled_rows_and_deterministic():
     # dW [7168][7168] over 4096 tokens: GPU 128x1 quantizers feed the GPU
     # GEMM; sampled rows against the oracle chain; repeated calls bitwise
