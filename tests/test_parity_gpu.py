@@ -344,6 +344,33 @@ def test_grouped_edge_cases(counts, T, out):
         check_gemm(c[:routed], R[:routed], out, f"grouped {counts} {out}")
 
 
+def _counts_150(case):
+    if case == "zipf":
+        return None                                   # zipf routing of all 2000 tokens
+    if case == "last_expert":
+        return [0] * 149 + [700]                      # only the last chunk's last expert
+    c = [0] * 150                                     # experts either side of 64 and 128
+    c[63], c[64], c[127], c[128], c[149] = 200, 129, 1, 256, 3
+    return c
+
+
+@pytest.mark.parametrize("case", ["zipf", "last_expert", "chunk_boundaries"])
+def test_grouped_more_than_64_experts(case):
+    # The tile lookup scans the offsets 64 experts per wave step, carrying
+    # the prefix maximum and the tile count from one chunk to the next; 150
+    # experts make three chunks.  Every routed row is checked.
+    E, N, K = 150, 256, 256
+    counts = _counts_150(case)
+    T = 2000 if counts is None else sum(counts)
+    gi = I.grouped_inputs(E, T, N, K, seed=150 + len(case), counts=counts)
+    qa, sa, qw, sw = quantize_grouped(gi)
+    R, found = oracle.grouped_gemm(qa, sa, qw, sw, gi.offsets)
+    c = run_grouped(qa, sa, qw, sw, gi.offsets, "f32")
+    routed = int(gi.offsets[-1])
+    assert routed > 0 and found[:routed].all()
+    check_gemm(c[:routed], R[:routed], "f32", f"grouped {E} experts ({case})")
+
+
 def test_grouped_garbage_offsets_are_memory_safe():
     # Offsets beyond T and decreasing ranges are clamped/empty: no fault, and
     # rows outside [clamped off[0], clamped off[E]) stay untouched.
