@@ -1106,19 +1106,30 @@ bool plan_two_kind(int64_t M, int64_t N, int &tn1, int &tn2) {
 // dW 7168 x 7168, a = 16 and b = 16 model at 6.46 wide-tile times against 7.
 constexpr double kWgradNarrowCost = 0.82;
 
+// Finishing time of one XCD, in wide-tile times.  After the wide tiles, the
+// 32 - rem CUs holding q of them are free at q, the rem CUs holding q + 1 at
+// q + 1.  Each narrow tile goes to the CU free first, so the narrow tiles end
+// level by level: all CUs of the first group at q + r, q + 2r, ..., those
+// of the second at q + 1 + r, ..., merged in time order.
 double xcd_finish(int64_t wide, int64_t narrow) {
     constexpr int kCUsPerXcd = kCUs / kNumXcd;
-    double load[kCUsPerXcd];
-    for (int i = 0; i < kCUsPerXcd; ++i)
-        load[i] = (double)(wide / kCUsPerXcd + (i < wide % kCUsPerXcd ? 1 : 0));
-    for (int64_t j = 0; j < narrow; ++j) {
-        int lo = 0;
-        for (int i = 1; i < kCUsPerXcd; ++i)
-            if (load[i] < load[lo]) lo = i;
-        load[lo] += kWgradNarrowCost;
+    const double r = kWgradNarrowCost;
+    const int64_t q = wide / kCUsPerXcd, rem = wide % kCUsPerXcd;
+    double end = (double)(q + (rem ? 1 : 0));
+    int64_t left = narrow, k_lo = 1, k_hi = 1;
+    while (left > 0) {
+        const double t_lo = (double)q + (double)k_lo * r;
+        const double t_hi = (double)(q + 1) + (double)k_hi * r;
+        if (rem == 0 || t_lo <= t_hi) {
+            left -= kCUsPerXcd - rem;
+            end = t_lo > end ? t_lo : end;
+            ++k_lo;
+        } else {
+            left -= rem;
+            end = t_hi > end ? t_hi : end;
+            ++k_hi;
+        }
     }
-    double end = 0.0;
-    for (int i = 0; i < kCUsPerXcd; ++i) end = load[i] > end ? load[i] : end;
     return end;
 }
 
