@@ -5,9 +5,18 @@
  * workspace from fp8_gemm_workspace_bytes) on a HIP stream of this program,
  * and are checked against the CPU oracle's C functions (test
  * infrastructure, linked here only): E4M3 bytes and scale bits equal, and a
- * relative Frobenius error of at most 1e-3 against the binary64 GEMM.  The
- * argument checks are exercised too (a K that is not a multiple of 128,
- * NULL pointers, an unknown output type).
+ * relative Frobenius error of at most 1e-3 against the binary64 GEMM.  Then
+ * the other entry points on the same activations:
+ *   - fp8_block_grouped_gemm over three experts (the middle one empty, BF16
+ *     output; every row against the binary64 reference, at most 8e-3);
+ *   - fp8_quant_act_128x1_t (bytes and scale bits equal);
+ *   - fp8_transpose_weight_128x128 (equal to the transposed oracle bytes and
+ *     scales);
+ *   - fp8_block_gemm_wgrad, dW = X^T X over the whole 128-token blocks of
+ *     the activations (sampled rows, at most 1e-3).
+ * The argument checks are exercised too (a K that is not a multiple of 128,
+ * NULL pointers, an unknown output type, a token count that is not a
+ * multiple of 128 for Wgrad, no experts for routed tokens).
  *
  * Usage: c_abi_check [M N K]   (defaults 200 384 2688: two M tiles, the
  * second ragged, and K split four ways through the workspace).  Prints one
@@ -29,6 +38,15 @@ void orc_quant_weight_128x128(const uint16_t *w, int64_t N, int64_t K, uint8_t *
 void orc_block_gemm_rows(const uint8_t *qa, const float *sa, const uint8_t *qw,
                          const float *sw, int64_t M, int64_t N, int64_t K,
                          const int64_t *rows, int64_t nrows, double *R);
+void orc_quant_act_128x1_t(const uint16_t *x, int64_t M, int64_t K, uint8_t *q_t,
+                           float *scales_t);
+void orc_rowscaled_gemm_rows(const uint8_t *qa, const float *sa, const uint8_t *qb,
+                             const float *sb, int64_t M, int64_t N, int64_t K,
+                             const int64_t *rows, int64_t nrows, double *R);
+void orc_grouped_gemm_rows(const uint8_t *qa, const float *sa, const uint8_t *qw,
+                           const float *sw, const int32_t *off, int64_t E, int64_t T,
+                           int64_t N, int64_t K, const int64_t *rows, int64_t nrows,
+                           double *R, int32_t *found);
 
 #define HIP_OK(call)                                                              \
     do {                                                                          \
@@ -54,6 +72,17 @@ static uint16_t to_bf16(float f) {
     memcpy(&u, &f, 4);
     u += 0x7FFFu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
+}
+
+/* relative Frobenius error of got (n values) against the binary64 ref */
+static double rel_fro_of(const float *got, const double *ref, int64_t n) {
+    double num = 0.0, den = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        const double d = (double)got[i] - ref[i];
+        num += d * d;
+        den += ref[i] * ref[i];
+    }
+    return den > 0.0 ? sqrt(num / den) : sqrt(num);
 }
 
 static void *dev_alloc(size_t n) {
@@ -138,10 +167,115 @@ int main(int argc, char **argv) {
                                          stream) == FP8_ERR_DTYPE;
     fails += !err_shape + !err_null + !err_dtype;
 
+    /* ---- grouped GEMM: three experts over the M tokens, expert 1 empty ---- */
+    const int64_t E = 3;
+    const int32_t off[4] = {0, (int32_t)(M / 2), (int32_t)(M / 2), (int32_t)M};
+    uint16_t *we = malloc(sizeof(uint16_t) * E * N * K);
+    for (int64_t i = 0; i < E * N * K; ++i) we[i] = to_bf16((float)(0.04 * uniform01() - 0.02));
+    void *dwe = dev_alloc(2 * E * N * K), *dqwe = dev_alloc(E * N * K);
+    float *dswe = dev_alloc(4 * E * NB * G);
+    int32_t *doff = dev_alloc(sizeof(off));
+    uint16_t *dcg = dev_alloc(2 * M * N);
+    HIP_OK(hipMemcpy(dwe, we, 2 * E * N * K, hipMemcpyHostToDevice));
+    HIP_OK(hipMemcpy(doff, off, sizeof(off), hipMemcpyHostToDevice));
+    st = fp8_quant_weight_128x128(dwe, E * N, K, dqwe, dswe, stream);
+    if (st == FP8_OK)
+        st = fp8_block_grouped_gemm(dqa, dsa, dqwe, dswe, doff, E, M, dcg, FP8_OUT_BF16, N, K,
+                                    NULL, 0, stream);
+    if (st != FP8_OK) {
+        printf("c-abi FAIL (grouped): %s\n", fp8_status_string(st));
+        return 1;
+    }
+    HIP_OK(hipStreamSynchronize(stream));
+    uint8_t *qwe_o = malloc(E * N * K);
+    float *swe_o = malloc(4 * E * NB * G);
+    uint16_t *cg16 = malloc(2 * M * N);
+    float *cg = malloc(4 * M * N);
+    double *Rg = malloc(sizeof(double) * M * N);
+    int32_t *found = malloc(sizeof(int32_t) * M);
+    HIP_OK(hipMemcpy(cg16, dcg, 2 * M * N, hipMemcpyDeviceToHost));
+    for (int64_t i = 0; i < M * N; ++i) {
+        const uint32_t u = (uint32_t)cg16[i] << 16;
+        memcpy(&cg[i], &u, 4);
+    }
+    orc_quant_weight_128x128(we, E * N, K, qwe_o, swe_o);
+    orc_grouped_gemm_rows(qa_o, sa_o, qwe_o, swe_o, off, E, M, N, K, rows, M, Rg, found);
+    int all_found = 1;
+    for (int64_t m = 0; m < M; ++m) all_found &= found[m] != 0;
+    const double grouped_rel_fro = rel_fro_of(cg, Rg, M * N);
+    fails += !all_found + !(grouped_rel_fro <= 8e-3);
+
+    /* ---- backward pieces ---- */
+    const int64_t GM = (M + 127) / 128, T = (M / 128) * 128;
+    void *dqt = dev_alloc(K * M), *dqwt = dev_alloc(K * N);
+    float *dst = dev_alloc(4 * K * GM), *dswt = dev_alloc(4 * G * NB);
+    st = fp8_quant_act_128x1_t(dx, M, K, dqt, dst, stream);
+    if (st == FP8_OK) st = fp8_transpose_weight_128x128(dqw, dsw, N, K, dqwt, dswt, stream);
+    if (st != FP8_OK) {
+        printf("c-abi FAIL (backward): %s\n", fp8_status_string(st));
+        return 1;
+    }
+    HIP_OK(hipStreamSynchronize(stream));
+    uint8_t *qt = malloc(K * M), *qt_o = malloc(K * M), *qwt = malloc(K * N);
+    float *st_ = malloc(4 * K * GM), *st_o = malloc(4 * K * GM), *swt = malloc(4 * G * NB);
+    HIP_OK(hipMemcpy(qt, dqt, K * M, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(st_, dst, 4 * K * GM, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(qwt, dqwt, K * N, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(swt, dswt, 4 * G * NB, hipMemcpyDeviceToHost));
+    orc_quant_act_128x1_t(x, M, K, qt_o, st_o);
+    const int t_equal = !memcmp(qt, qt_o, K * M) && !memcmp(st_, st_o, 4 * K * GM);
+    int tr_equal = 1;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) tr_equal &= qwt[k * N + n] == qw_o[n * K + k];
+    for (int64_t nb = 0; nb < NB; ++nb)
+        for (int64_t g = 0; g < G; ++g) tr_equal &= swt[g * NB + nb] == sw_o[nb * G + g];
+    fails += !t_equal + !tr_equal;
+
+    /* Wgrad dW = X^T X over the first T tokens (their 128x1 groups), if any */
+    double wgrad_rel_fro = 0.0;
+    if (T > 0) {
+        void *dq2 = dev_alloc(K * T);
+        float *ds2 = dev_alloc(4 * K * (T / 128)), *ddw = dev_alloc(4 * K * K);
+        st = fp8_quant_act_128x1_t(dx, T, K, dq2, ds2, stream);
+        if (st == FP8_OK) st = fp8_block_gemm_wgrad(dq2, ds2, dq2, ds2, ddw, FP8_OUT_F32, K, K, T, stream);
+        if (st != FP8_OK) {
+            printf("c-abi FAIL (wgrad): %s\n", fp8_status_string(st));
+            return 1;
+        }
+        HIP_OK(hipStreamSynchronize(stream));
+        int64_t wrows[8], nw = 0;
+        const int64_t cand[8] = {0, 1, 127, 128, K / 2, K - 129, K - 128, K - 1};
+        for (int i = 0; i < 8; ++i)
+            if (cand[i] >= 0 && cand[i] < K && (nw == 0 || cand[i] > wrows[nw - 1])) wrows[nw++] = cand[i];
+        uint8_t *q2 = malloc(K * T);
+        float *s2 = malloc(4 * K * (T / 128)), *dwr = malloc(4 * nw * K);
+        double *Rw = malloc(sizeof(double) * nw * K);
+        for (int64_t i = 0; i < nw; ++i)
+            HIP_OK(hipMemcpy(dwr + i * K, ddw + wrows[i] * K, 4 * K, hipMemcpyDeviceToHost));
+        orc_quant_act_128x1_t(x, T, K, q2, s2);
+        orc_rowscaled_gemm_rows(q2, s2, q2, s2, K, K, T, wrows, nw, Rw);
+        wgrad_rel_fro = rel_fro_of(dwr, Rw, nw * K);
+        fails += !(wgrad_rel_fro <= 1e-3);
+        hipFree(dq2); hipFree(ds2); hipFree(ddw);
+        free(q2); free(s2); free(dwr); free(Rw);
+    }
+    const int err_tokens = fp8_block_gemm_wgrad(dqt, dst, dqt, dst, dc, FP8_OUT_F32, K, K, 200,
+                                                stream) == FP8_ERR_SHAPE;
+    const int err_experts = fp8_block_grouped_gemm(dqa, dsa, dqwe, dswe, doff, 0, M, dcg,
+                                                   FP8_OUT_BF16, N, K, NULL, 0,
+                                                   stream) == FP8_ERR_SHAPE;
+    fails += !err_tokens + !err_experts;
+
     printf("c-abi %s: M=%lld N=%lld K=%lld workspace=%zu bytes_equal=%d scales_equal=%d "
-           "rel_fro=%.3e error_codes=%d%d%d\n",
+           "rel_fro=%.3e grouped_rel_fro=%.3e q128x1_t_equal=%d transpose_equal=%d "
+           "wgrad_tokens=%lld wgrad_rel_fro=%.3e error_codes=%d%d%d%d%d\n",
            fails ? "FAIL" : "ok", (long long)M, (long long)N, (long long)K, ws_bytes, bytes_equal,
-           scales_equal, rel_fro, err_shape, err_null, err_dtype);
+           scales_equal, rel_fro, grouped_rel_fro, t_equal, tr_equal, (long long)T, wgrad_rel_fro,
+           err_shape, err_null, err_dtype, err_tokens, err_experts);
+    hipFree(dwe); hipFree(dqwe); hipFree(dswe); hipFree(doff); hipFree(dcg);
+    hipFree(dqt); hipFree(dqwt); hipFree(dst); hipFree(dswt);
+    free(we); free(qwe_o); free(swe_o); free(cg16); free(cg); free(Rg); free(found);
+    free(qt); free(qt_o); free(qwt); free(st_); free(st_o); free(swt);
 
     HIP_OK(hipStreamDestroy(stream));
     hipFree(dx); hipFree(dw); hipFree(dqa); hipFree(dqw); hipFree(dsa); hipFree(dsw);
