@@ -12,13 +12,23 @@ inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 
 inline fp8_status from_hip(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_HIP; }
 
+// The launchers report hipGetLastError() after their launches, which also
+// returns an error that an earlier, unrelated HIP call left on this thread.
+// Every entry point clears it just before its first launch, so FP8_ERR_HIP
+// names a failure of this call's own launches.
+inline void clear_last_error() { (void)hipGetLastError(); }
+
 inline hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 
 // Limits of the kernels' grid arithmetic: any one size below 2^31, a tensor
-// below 2^40 elements, a GEMM below 2^30 output tiles of 128 x 128.
+// below 2^40 elements, a GEMM below 2^22 output tiles of 128 x 128 (counted
+// with one extra row of tiles, or one per expert).  A launch may not exceed
+// 2^32 work-items: with at most 512 threads per workgroup and at most two
+// workgroups per 128 x 128 tile, 2^22 tiles stay below it.
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
-constexpr int64_t kMaxTiles = (int64_t)1 << 30;
+constexpr int64_t kMaxTiles = (int64_t)1 << 22;
+constexpr int64_t kMaxWorkItems = (int64_t)1 << 32;
 // GEMM inner dimension: a tile's 256 operand rows of K bytes are addressed
 // through one buffer resource, whose byte range and offsets are 32-bit, so
 // 256 K < 2^32.
@@ -29,6 +39,15 @@ fp8_status check_quant(const void *x, int64_t R, int64_t K, const void *q, const
     if (R == 0 || K == 0) return FP8_OK;
     if (!x || !q || !s) return FP8_ERR_NULL;
     if (R >= kMaxDim || K >= kMaxDim || R * K >= kMaxElems) return FP8_ERR_SHAPE;
+    // Grids: the 1x128 kernels launch at most 16 threads per group (R rows
+    // of ceil(K/128) groups); the 128x128 kernels and the weight transpose
+    // 256 threads per block (with R rows there are ceil(R/128) block rows,
+    // at most R * ceil(K/128) / 8 + ceil(K/128) blocks, below 16 threads per
+    // row and group as well).  The 128x1 kernel is persistent (capped grid).
+    const int64_t groups = R * ((K + 127) / 128);
+    if (groups >= kMaxWorkItems / 16) return FP8_ERR_SHAPE;
+    const int64_t blocks = ((R + 127) / 128) * ((K + 127) / 128);
+    if (blocks >= kMaxWorkItems / 256) return FP8_ERR_SHAPE;
     return FP8_OK;
 }
 
@@ -55,6 +74,7 @@ fp8_status quant_act(const void *x_bf16, int64_t M, int64_t K, void *q_e4m3, flo
     fp8_status st = check_quant(x_bf16, M, K, q_e4m3, scales);
     if (st != FP8_OK || M == 0 || K == 0) return st;
     if (!aligned(x_bf16, 2) || !aligned(scales, 4)) return FP8_ERR_ALIGN;
+    clear_last_error();
     return from_hip(fp8blk::launch_quant_act_1x128(x_bf16, M, K, q_e4m3, scales, pow2,
                                                    as_stream(hip_stream)));
 }
@@ -64,6 +84,7 @@ fp8_status quant_weight(const void *w_bf16, int64_t N, int64_t K, void *q_e4m3, 
     fp8_status st = check_quant(w_bf16, N, K, q_e4m3, scales);
     if (st != FP8_OK || N == 0 || K == 0) return st;
     if (!aligned(w_bf16, 2) || !aligned(scales, 4)) return FP8_ERR_ALIGN;
+    clear_last_error();
     return from_hip(fp8blk::launch_quant_weight_128x128(w_bf16, N, K, q_e4m3, scales, pow2,
                                                         as_stream(hip_stream)));
 }
@@ -76,6 +97,7 @@ fp8_status block_gemm(const void *a_e4m3, const float *a_scales, const void *w_e
                                       workspace, workspace_bytes);
     if (st != FP8_OK || M == 0 || N == 0) return st;
     if (K == 0) return FP8_ERR_SHAPE;
+    clear_last_error();
     return from_hip(fp8blk::launch_block_gemm(a_e4m3, a_scales, w_e4m3, w_scales, c,
                                               out_dtype == FP8_OUT_BF16, M, N, K, workspace,
                                               workspace_bytes, pow2, as_stream(hip_stream)));
@@ -95,6 +117,7 @@ fp8_status grouped_gemm(const void *a_e4m3, const float *a_scales, const void *w
     if (E == 0 || K == 0) return FP8_ERR_SHAPE;
     if (!group_offsets) return FP8_ERR_NULL;
     if (!aligned(group_offsets, 4)) return FP8_ERR_ALIGN;
+    clear_last_error();
     return from_hip(fp8blk::launch_grouped_gemm(a_e4m3, a_scales, w_e4m3, w_scales, group_offsets,
                                                 E, T, c, out_dtype == FP8_OUT_BF16, N, K, pow2,
                                                 as_stream(hip_stream)));
@@ -163,6 +186,7 @@ fp8_status fp8_quant_act_128x1_t(const void *x_bf16, int64_t M, int64_t K, void 
     fp8_status st = check_quant(x_bf16, M, K, q_t, scales_t);
     if (st != FP8_OK || M == 0 || K == 0) return st;
     if (!aligned(x_bf16, 2) || !aligned(scales_t, 4)) return FP8_ERR_ALIGN;
+    clear_last_error();
     return from_hip(
         fp8blk::launch_quant_act_128x1_t(x_bf16, M, K, q_t, scales_t, as_stream(hip_stream)));
 }
@@ -174,7 +198,9 @@ fp8_status fp8_transpose_weight_128x128(const void *q_e4m3, const float *scales,
     if (N == 0 || K == 0) return FP8_OK;
     if (!q_e4m3 || !scales || !q_t || !scales_t) return FP8_ERR_NULL;
     if (N >= kMaxDim || K >= kMaxDim || N * K >= kMaxElems) return FP8_ERR_SHAPE;
+    if (((N + 127) / 128) * ((K + 127) / 128) >= kMaxWorkItems / 256) return FP8_ERR_SHAPE;
     if (!aligned(scales, 4) || !aligned(scales_t, 4)) return FP8_ERR_ALIGN;
+    clear_last_error();
     return from_hip(fp8blk::launch_transpose_weight(q_e4m3, scales, N, K, q_t, scales_t,
                                                     as_stream(hip_stream)));
 }
@@ -187,6 +213,7 @@ fp8_status fp8_block_gemm_wgrad(const void *dy_t, const float *dy_t_scales, cons
                                       nullptr, 0);
     if (st != FP8_OK || N == 0 || K == 0) return st;
     if (T == 0) return FP8_ERR_SHAPE;
+    clear_last_error();
     return from_hip(fp8blk::launch_block_gemm_wgrad(dy_t, dy_t_scales, x_t, x_t_scales, dw,
                                                     out_dtype == FP8_OUT_BF16, N, K, T,
                                                     as_stream(hip_stream)));

@@ -397,24 +397,65 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         for (int t = 0; t < C::kBLoads; ++t)
             copy16_nt(src.w, wave_voff + t * rowstep, soff, lds_b0 + so + 1024 * C::kWaves * t);
     };
+    // A chunk that runs past the last K block (G not a multiple of
+    // kScaleChunk) is fetched one dword per lane instead: the buffer range
+    // check covers the lane's voffset only (not soffset), and it may treat a
+    // 16-byte access that straddles the end as wholly out of range, so a
+    // 16-byte piece of the last row would either read past the buffer or lose
+    // its valid scales.  Here every lane's offset includes the chunk's K
+    // offset, and each dword is checked on its own.  Dword copy u of a
+    // chunk buffer fills its dwords 64 u .. + 63: dword d is block j = d % 4
+    // of piece h = d / (4 ROWS) of row r = (d / 4) % ROWS.  More copies in a
+    // block only make the pipeline's waits stricter.
+    auto issue_chunk_dwords = [&](const v4i &rsrc, int rows, int c, uint32_t lds_buf) {
+        const int copies = C::kScalePieces * rows / 16;  // over all waves
+        // the lane index passes through an empty asm statement so that the
+        // offsets below are computed here, in this rarely taken branch,
+        // rather than hoisted out of the main loop into live registers
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int t = 0; t < (C::kScalePieces * (C::BM > C::BN ? C::BM : C::BN) / 16 + C::kWaves - 1) /
+                                C::kWaves;
+             ++t) {
+            const int u = wave_u + C::kWaves * t;
+            if (u < copies) {
+                const int d = 64 * u + ln;
+                const int h = d / (4 * rows), r = (d >> 2) % rows, j = d & 3;
+                const uint32_t off =
+                    (uint32_t)(r * G * 4 + (C::kScaleChunk * c + 4 * h + j) * 4);
+                copy4(rsrc, off, 0u, lds_buf + 256u * (uint32_t)u);
+            }
+        }
+    };
     // block kb's scales: its activation-scale chunk if one starts there, and
     // its weight scales
     auto issue_scales = [&](const TileOperands &src, int kb, int st) {
         if (kb == kb0 || (kb & (C::kScaleChunk - 1)) == 0) {
             const int c = kb / C::kScaleChunk;
+            const bool whole = (c + 1) * C::kScaleChunk <= G;
             const uint32_t so = (uint32_t)((c & 1) * sizeof(L.chunks.v[0]));
+            if (whole) {
 #pragma unroll
-            for (int t = 0; t < C::kScaleLoads; ++t)
-                if (wave_u + C::kWaves * t < C::kScaleCopies)
-                    copy16(src.sa, sa_voff[t], (uint32_t)c * (4u * C::kScaleChunk),
-                           lds_sc0 + so + 1024 * C::kWaves * t);
+                for (int t = 0; t < C::kScaleLoads; ++t)
+                    if (wave_u + C::kWaves * t < C::kScaleCopies)
+                        copy16(src.sa, sa_voff[t], (uint32_t)c * (4u * C::kScaleChunk),
+                               lds_sc0 + so + 1024 * C::kWaves * t);
+            } else {
+                issue_chunk_dwords(src.sa, C::BM, c, lds_addr(&L.chunks.v[0][0][0][0]) + so);
+            }
             if constexpr (C::kRowScaledW) {
                 const uint32_t sow = (uint32_t)((c & 1) * sizeof(L.wchunks.v[0]));
+                if (whole) {
 #pragma unroll
-                for (int t = 0; t < C::kScaleLoadsW; ++t)
-                    if (wave_u + C::kWaves * t < C::kScaleCopiesW)
-                        copy16(src.swr, swr_voff[t], (uint32_t)c * (4u * C::kScaleChunk),
-                               lds_wc0 + sow + 1024 * C::kWaves * t);
+                    for (int t = 0; t < C::kScaleLoadsW; ++t)
+                        if (wave_u + C::kWaves * t < C::kScaleCopiesW)
+                            copy16(src.swr, swr_voff[t], (uint32_t)c * (4u * C::kScaleChunk),
+                                   lds_wc0 + sow + 1024 * C::kWaves * t);
+                } else {
+                    issue_chunk_dwords(src.swr, C::BN, c,
+                                       lds_addr(&L.wchunks.v[0][0][0][0]) + sow);
+                }
             }
         }
         // every wave fetches the (one or two) weight scales of the block to

@@ -162,6 +162,27 @@ def test_backward_argument_errors():
     assert wg(N=0, a=NUL, sa=NUL, c=NUL) == B.FP8_OK
 
 
+def test_grid_limits_are_refused_as_shape_errors():
+    """Shapes whose launch would pass 2^32 work-items are refused with
+    FP8_ERR_SHAPE before anything is enqueued; the largest shapes that fit
+    pass validation (checked with a NULL output, so nothing launches)."""
+    lib = B.lib()
+    act, wq = lib.fp8_quant_act_1x128, lib.fp8_quant_weight_128x128
+    # 1x128: at most 16 threads per group, so M * ceil(K/128) < 2^28 groups
+    assert act(A16, 1 << 20, 1 << 15, A16, A16, NUL) == B.FP8_ERR_SHAPE     # 2^28 groups
+    assert act(A16, (1 << 20) - 1, 1 << 15, NUL, A16, NUL) == B.FP8_ERR_NULL
+    assert act(A16, (1 << 31) - 1, 1, A16, A16, NUL) == B.FP8_ERR_SHAPE     # tiny K, many rows
+    # 128x128: 256 threads per block, so ceil(N/128) ceil(K/128) < 2^24 blocks
+    assert wq(A16, 1 << 19, 1 << 19, A16, A16, NUL) == B.FP8_ERR_SHAPE
+    assert lib.fp8_transpose_weight_128x128(A16, A16, 1 << 19, 1 << 19, A16, A16,
+                                            NUL) == B.FP8_ERR_SHAPE
+    # GEMMs: fewer than 2^22 output tiles of 128 x 128 (with one extra row)
+    assert gemm(lib, M=(1 << 22) * 128, N=128, K=128) == B.FP8_ERR_SHAPE
+    assert gemm(lib, M=1 << 20, N=1 << 16, K=128) == B.FP8_ERR_SHAPE
+    assert gemm(lib, M=(1 << 20) - 256, N=1 << 16, K=128, c=NUL) == B.FP8_ERR_NULL
+    assert grouped(lib, E=1 << 14, T=128, N=1 << 15) == B.FP8_ERR_SHAPE
+
+
 def test_workspace_query():
     lib = B.lib()
     # decode-shaped GEMMs have few output tiles and split K

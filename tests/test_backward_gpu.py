@@ -15,7 +15,7 @@ import oracle
 from fp8_fine_grained_token_amd import binding as B
 from fp8_fine_grained_token_amd import inputs as I
 
-from .gpu_util import check_gemm, dev, dev_bf16, host, log, torch
+from .gpu_util import check_gemm, dev, dev_bf16, gemm_error_bound, host, log, tile_rows, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -89,11 +89,12 @@ def test_dgrad_chain(M, N, K):
     qwt, swt = B.fp8_transpose_weight_128x128(dev(qw), dev(sw))
     assert_bytes_and_scales(host(qdy), host(sdy), qdy_o, sdy_o, "dY 1x128")
     assert_bytes_and_scales(host(qwt), host(swt), qwt_o, swt_o, "W^T")
-    rows = np.arange(M) if M <= 256 else np.array([0, 1, 255, 256, 2047, 4095])
+    rows = np.arange(M) if M <= 256 else tile_rows(M, 256, per_tile=1)
     R = oracle.block_gemm(qdy_o, sdy_o, qwt_o, swt_o, rows)
+    b = gemm_error_bound(qdy_o, sdy_o, qwt_o, swt_o, rows)
     for out in ("f32", "bf16"):
         c = B.fp8_block_gemm(qdy, sdy, qwt, swt, out_dtype=out)
-        check_gemm(c[torch().from_numpy(rows).cuda()], R, out, f"dgrad {M}x{K}x{N} {out}")
+        check_gemm(c[torch().from_numpy(rows).cuda()], R, out, f"dgrad {M}x{K}x{N} {out}", b)
 
 
 # ---- Wgrad ----------------------------------------------------------------------
@@ -113,7 +114,8 @@ def test_wgrad_small(T, N, K, out):
     qx, sx = oracle.quant_act_128x1_t(x)        # [K][T]
     R = oracle.rowscaled_gemm(qdy, sdy, qx, sx)
     c = B.fp8_block_gemm_wgrad(dev(qdy), dev(sdy), dev(qx), dev(sx), out_dtype=out)
-    check_gemm(c, R, out, f"wgrad {N}x{K} over {T} tokens {out}")
+    check_gemm(c, R, out, f"wgrad {N}x{K} over {T} tokens {out}",
+               gemm_error_bound(qdy, sdy, qx, sx, row_scaled_w=True))
 
 
 @pytest.mark.parametrize("T,N,K,rows", [
@@ -134,7 +136,8 @@ def test_wgrad_two_tile_widths_sampled_rows(T, N, K, rows, out):
     R = oracle.rowscaled_gemm(qdy, sdy, qx, sx, rows)
     c = B.fp8_block_gemm_wgrad(dev(qdy), dev(sdy), dev(qx), dev(sx), out_dtype=out)
     check_gemm(c[torch().from_numpy(rows).cuda()], R, out,
-               f"wgrad {N}x{K} over {T} tokens {out}, sampled rows")
+               f"wgrad {N}x{K} over {T} tokens {out}, sampled rows",
+               gemm_error_bound(qdy, sdy, qx, sx, rows, row_scaled_w=True))
 
 
 def test_wgrad_workload_chain_sampled_rows_and_deterministic():
@@ -153,7 +156,8 @@ def test_wgrad_workload_chain_sampled_rows_and_deterministic():
     c0 = B.fp8_block_gemm_wgrad(qdy, sdy, qx, sx, out_dtype="f32")
     c1 = B.fp8_block_gemm_wgrad(qdy, sdy, qx, sx, out_dtype="f32")
     assert torch().equal(c0, c1)
-    rows = np.array([0, 1, 127, 128, 3583, 3584, 7167])
+    rows = tile_rows(N, 128, per_tile=1)
     log(f"  oracle Wgrad on {rows.size} rows of 7168x7168 over 4096 tokens ...")
     R = oracle.rowscaled_gemm(qdy_o, sdy_o, qx_o, sx_o, rows)
-    check_gemm(c0[torch().from_numpy(rows).cuda()], R, "f32", "wgrad workload rows")
+    check_gemm(c0[torch().from_numpy(rows).cuda()], R, "f32", "wgrad workload rows",
+               gemm_error_bound(qdy_o, sdy_o, qx_o, sx_o, rows, row_scaled_w=True))

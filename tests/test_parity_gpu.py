@@ -13,7 +13,8 @@ import oracle
 from fp8_fine_grained_token_amd import binding as B
 from fp8_fine_grained_token_amd import inputs as I
 
-from .gpu_util import check_gemm, dev, dev_bf16, host, log, torch
+from .gpu_util import (check_gemm, dev, dev_bf16, gemm_error_bound, grouped_error_bound, host,
+                       log, tile_rows, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -135,7 +136,8 @@ def test_gemm_tiny_fp32_out():
     g = I.config_tiny(seed=0)
     qa, sa, qw, sw = quantize(g)
     R = oracle.block_gemm(qa, sa, qw, sw)
-    check_gemm(run_gemm(qa, sa, qw, sw, "f32"), R, "f32", "tiny 128x256x512 f32")
+    check_gemm(run_gemm(qa, sa, qw, sw, "f32"), R, "f32", "tiny 128x256x512 f32",
+               gemm_error_bound(qa, sa, qw, sw))
 
 
 @pytest.mark.parametrize("M", [1, 15, 17, 129, 255, 300])
@@ -145,7 +147,8 @@ def test_gemm_ragged(M, N, K, out):
     g = I.gemm_inputs(M, N, K, seed=M * 1000 + N + K, outlier_frac=0.01, outlier_mult=20.0)
     qa, sa, qw, sw = quantize(g)
     R = oracle.block_gemm(qa, sa, qw, sw)
-    check_gemm(run_gemm(qa, sa, qw, sw, out), R, out, f"{M}x{N}x{K} {out}")
+    check_gemm(run_gemm(qa, sa, qw, sw, out), R, out, f"{M}x{N}x{K} {out}",
+               gemm_error_bound(qa, sa, qw, sw))
 
 
 def test_gemm_decode_workload_with_and_without_workspace():
@@ -159,10 +162,12 @@ def test_gemm_decode_workload_with_and_without_workspace():
     ws = t.empty(nbytes, dtype=t.uint8, device="cuda")
     c1 = run_gemm(qa, sa, qw, sw, "bf16", workspace=ws)
     c2 = run_gemm(qa, sa, qw, sw, "bf16")
-    check_gemm(c1, R, "bf16", "decode split-K")
-    check_gemm(c2, R, "bf16", "decode no workspace")
+    splits = nbytes // (256 * 2048 * 4)
+    b = gemm_error_bound(qa, sa, qw, sw, splits=splits)
+    check_gemm(c1, R, "bf16", "decode split-K", b)
+    check_gemm(c2, R, "bf16", "decode no workspace", gemm_error_bound(qa, sa, qw, sw))
     c3 = run_gemm(qa, sa, qw, sw, "f32", workspace=ws)
-    check_gemm(c3, R, "f32", "decode split-K f32")
+    check_gemm(c3, R, "f32", "decode split-K f32", b)
 
 
 @pytest.mark.parametrize("M,N,K,splits", [(128, 128, 8192, 16), (100, 256, 2688, 4)])
@@ -180,7 +185,8 @@ def test_gemm_split_k_many_and_uneven_splits(M, N, K, splits, out):
     ws = t.empty(nbytes, dtype=t.uint8, device="cuda")
     c1 = run_gemm(qa, sa, qw, sw, out, workspace=ws)
     c2 = run_gemm(qa, sa, qw, sw, out, workspace=ws)
-    check_gemm(c1, R, out, f"split-K x{splits} {M}x{N}x{K} {out}")
+    check_gemm(c1, R, out, f"split-K x{splits} {M}x{N}x{K} {out}",
+               gemm_error_bound(qa, sa, qw, sw, splits=splits))
     assert t.equal(c1, c2), "split-K result changed between identical calls"
 
 
@@ -208,24 +214,24 @@ def test_gemm_split_k_workspace_garbage_and_repeats():
         outs.append(run_gemm(qa, sa, qw, sw, "f32", workspace=ws))
     for _ in range(3):  # and back to back on the same workspace
         outs.append(run_gemm(qa, sa, qw, sw, "f32", workspace=ws))
-    check_gemm(outs[0], R, "f32", "split-K, garbage workspace")
+    check_gemm(outs[0], R, "f32", "split-K, garbage workspace",
+               gemm_error_bound(qa, sa, qw, sw, splits=nbytes // (M * N * 4)))
     for o in outs[1:]:
         assert t.equal(o, outs[0]), "split-K result changed between calls"
 
 
-def test_gemm_dense_workload_sampled_rows():
+def test_gemm_dense_workload_rows_of_every_tile():
+    # 4096 x 7168 x 7168 runs 256-row tiles: three rows of every M tile
+    # (and the first and last row), every column, each output within its
+    # bound.  The columns cover both tile widths of the two-kind plan.
     g = I.config_dense(seed=0)
     qa, sa, qw, sw = quantize(g)
-    c = host(run_gemm(qa, sa, qw, sw, "bf16"))
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 2047, 2048, 4094, 4095],
-                                     np.random.default_rng(1).choice(4096, 22, replace=False)]))
-    log(f"  oracle GEMM on {rows.size} sampled rows of 4096x7168x7168 ...")
+    c = run_gemm(qa, sa, qw, sw, "bf16")
+    rows = tile_rows(4096, 256, per_tile=3)
+    log(f"  oracle GEMM on {rows.size} rows of 4096x7168x7168 ...")
     R = oracle.block_gemm(qa, sa, qw, sw, rows)
-    from .gpu_util import rel_fro
-    rf = rel_fro(c[rows], R)
-    log(f"  dense sampled rows: rel_fro={rf:.3e}")
-    assert np.isfinite(c).all()
-    assert rf <= 4e-3
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, "bf16", "dense workload rows",
+               gemm_error_bound(qa, sa, qw, sw, rows))
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
@@ -239,7 +245,8 @@ def test_gemm_big_tiles_ragged_edges(out):
     c = run_gemm(qa, sa, qw, sw, out)
     rows = np.unique(np.concatenate([np.arange(0, M, 97), [255, 256, 3839, 3840, 3999]]))
     R = oracle.block_gemm(qa, sa, qw, sw, rows)
-    check_gemm(c[torch().from_numpy(rows).cuda()], R, out, f"big tiles ragged {out}")
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, out, f"big tiles ragged {out}",
+               gemm_error_bound(qa, sa, qw, sw, rows))
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
@@ -254,7 +261,8 @@ def test_gemm_192_wide_tiles_all_columns(out):
     c = run_gemm(qa, sa, qw, sw, out)
     rows = np.unique(np.concatenate([np.arange(0, M, 127), [255, 256, 4095]]))
     R = oracle.block_gemm(qa, sa, qw, sw, rows)
-    check_gemm(c[torch().from_numpy(rows).cuda()], R, out, f"192-wide tiles {out}")
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, out, f"192-wide tiles {out}",
+               gemm_error_bound(qa, sa, qw, sw, rows))
 
 
 @pytest.mark.parametrize("shape", [(4096, 4096, 128), (4096, 4096, 256), (4096, 7168, 128)])
@@ -268,7 +276,8 @@ def test_gemm_big_tiles_one_or_two_k_blocks(shape):
     c = run_gemm(qa, sa, qw, sw, "f32")
     rows = np.array([0, 17, 255, 256, 1000, 2047, 2048, 4095])
     R = oracle.block_gemm(qa, sa, qw, sw, rows)
-    check_gemm(c[torch().from_numpy(rows).cuda()], R, "f32", f"big tiles {M}x{N}x{K}")
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, "f32", f"big tiles {M}x{N}x{K}",
+               gemm_error_bound(qa, sa, qw, sw, rows))
 
 
 def test_gemm_two_tile_widths_metamorphic_and_deterministic():
@@ -285,7 +294,8 @@ def test_gemm_two_tile_widths_metamorphic_and_deterministic():
     assert np.array_equal(c2, c0 * np.float32(8.0))
     rows = np.array([0, 255, 256, 2047, 4095])
     R = oracle.block_gemm(qa, sa, qw, sw, rows)
-    check_gemm(torch().from_numpy(c0[rows]), R, "f32", "two tile widths")
+    check_gemm(torch().from_numpy(c0[rows]), R, "f32", "two tile widths",
+               gemm_error_bound(qa, sa, qw, sw, rows))
 
 
 def test_gemm_power_of_two_metamorphic_and_deterministic():
@@ -341,7 +351,8 @@ def test_grouped_edge_cases(counts, T, out):
     routed = int(gi.offsets[-1])
     assert np.all(ch[routed:] == 7.0), "unrouted rows were written"
     if routed:
-        check_gemm(c[:routed], R[:routed], out, f"grouped {counts} {out}")
+        check_gemm(c[:routed], R[:routed], out, f"grouped {counts} {out}",
+                   grouped_error_bound(qa, sa, qw, sw, gi.offsets, np.arange(routed)))
 
 
 def _counts_150(case):
@@ -368,7 +379,8 @@ def test_grouped_more_than_64_experts(case):
     c = run_grouped(qa, sa, qw, sw, gi.offsets, "f32")
     routed = int(gi.offsets[-1])
     assert routed > 0 and found[:routed].all()
-    check_gemm(c[:routed], R[:routed], "f32", f"grouped {E} experts ({case})")
+    check_gemm(c[:routed], R[:routed], "f32", f"grouped {E} experts ({case})",
+               grouped_error_bound(qa, sa, qw, sw, gi.offsets, np.arange(routed)))
 
 
 def test_grouped_garbage_offsets_are_memory_safe():
@@ -387,33 +399,106 @@ def test_grouped_garbage_offsets_are_memory_safe():
     # Clamped and made non-overlapping: expert 0 keeps [10, 60), expert 1 is
     # empty, expert 2 starts where expert 0 ended: [60, 90), expert 3 gets
     # [90, 100).
-    R, _ = oracle.grouped_gemm(qa, sa, qw, sw, np.array([10, 60, 60, 90, 100], np.int32))
-    check_gemm(c[10:60], R[10:60], "f32", "garbage offsets expert 0")
-    check_gemm(c[60:90], R[60:90], "f32", "garbage offsets expert 2")
-    check_gemm(c[90:100], R[90:100], "f32", "garbage offsets expert 3")
+    eff = np.array([10, 60, 60, 90, 100], np.int32)
+    R, _ = oracle.grouped_gemm(qa, sa, qw, sw, eff)
+    b = grouped_error_bound(qa, sa, qw, sw, eff, np.arange(T))
+    check_gemm(c[10:60], R[10:60], "f32", "garbage offsets expert 0", b[10:60])
+    check_gemm(c[60:90], R[60:90], "f32", "garbage offsets expert 2", b[60:90])
+    check_gemm(c[90:100], R[90:100], "f32", "garbage offsets expert 3", b[90:100])
 
 
-def test_grouped_workload_sampled_rows():
+def expert_tile_rows(off, tile=128, per_tile=1, salt=0):
+    """Rows of every expert's every `tile`-row M tile (the grouped kernel's
+    tiles start at each expert's first row), plus each expert's first and
+    last row."""
+    rows = []
+    for e in range(len(off) - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            rows += list(lo + tile_rows(hi - lo, tile, per_tile, salt + e))
+    return np.unique(np.array(rows, dtype=np.int64))
+
+
+def test_grouped_workload_rows_of_every_tile():
+    # 32 experts over 8192 tokens: one row inside every 128-row M tile of
+    # every expert (plus its first and last row), all 4096 columns, each
+    # output within its bound.
     gi = I.config_grouped(seed=0)
     log("  quantizing grouped workload with the oracle ...")
     qa, sa, qw, sw = quantize_grouped(gi)
-    c = host(run_grouped(qa, sa, qw, sw, gi.offsets, "bf16"))
+    c = run_grouped(qa, sa, qw, sw, gi.offsets, "bf16")
     off = gi.offsets
-    rng = np.random.default_rng(2)
-    rows = []
-    for e in range(gi.E):
-        lo, hi = int(off[e]), int(off[e + 1])
-        if hi > lo:
-            rows += [lo, hi - 1] + list(rng.integers(lo, hi, size=1))
-    rows = np.unique(np.array(rows))
-    log(f"  oracle grouped GEMM on {rows.size} sampled rows ...")
+    rows = expert_tile_rows(off)
+    log(f"  oracle grouped GEMM on {rows.size} rows ...")
     R, found = oracle.grouped_gemm(qa, sa, qw, sw, off, rows)
     assert found.all()
-    from .gpu_util import rel_fro
-    rf = rel_fro(c[rows], R)
-    log(f"  grouped sampled rows: rel_fro={rf:.3e}")
-    assert np.isfinite(c).all()
-    assert rf <= 4e-3
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, "bf16", "grouped workload rows",
+               grouped_error_bound(qa, sa, qw, sw, off, rows))
+
+
+def quantize_grouped_pow2(gi):
+    qa, sa = oracle.quant_act_1x128_pow2(gi.a_bf16)
+    E, N, K = gi.w_bf16.shape
+    qw, sw = oracle.quant_weight_128x128_pow2(gi.w_bf16.reshape(E * N, K))
+    return qa, sa, qw.reshape(E, N, K), sw.reshape(E, N // 128, K // 128)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_grouped_full_depth_fp32_every_row(pow2):
+    # FP32 output at the workload's depth and width (K = 7168: 56 K blocks,
+    # seven activation-scale chunks; N = 4096: 16 N tiles with their own
+    # weight-scale blocks), every routed row: expert 0 spans eight 128-row M
+    # tiles, expert 1 a ragged 300 (three tiles, the last 44 rows), expert 2
+    # is empty, expert 3 has 77 rows.
+    counts = [1024, 300, 0, 77]
+    E, N, K = 4, 4096, 7168
+    T = sum(counts) + 5                                   # 5 unrouted rows
+    gi = I.grouped_inputs(E, T, N, K, seed=1401, counts=counts)
+    qa, sa, qw, sw = quantize_grouped_pow2(gi) if pow2 else quantize_grouped(gi)
+    routed = int(gi.offsets[-1])
+    log(f"  oracle grouped GEMM on all {routed} rows at K={K}, N={N} ...")
+    R, found = oracle.grouped_gemm(qa, sa, qw, sw, gi.offsets)
+    t = torch()
+    c = t.full((T, N), 7.0, dtype=t.float32, device="cuda")
+    fn = B.fp8_block_grouped_gemm_pow2 if pow2 else B.fp8_block_grouped_gemm
+    fn(dev(qa), dev(sa), dev(qw), dev(sw), dev(gi.offsets.astype(np.int32)), out_dtype="f32", c=c)
+    ch = host(c)
+    assert np.all(ch[routed:] == 7.0), "unrouted rows were written"
+    assert found[:routed].all()
+    check_gemm(c[:routed], R[:routed], "f32", f"grouped full depth every row (pow2={pow2})",
+               grouped_error_bound(qa, sa, qw, sw, gi.offsets, np.arange(routed)))
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_grouped_scale_chunks_not_a_multiple(pow2):
+    # K = 2304: G = 18 K blocks, so the last activation-scale chunk (8 blocks
+    # each) holds only two, fetched dword by dword; N = 512 (two N tiles);
+    # every routed row, FP32 output.
+    counts = [0, 1, 129, 300]
+    E, N, K = 4, 512, 2304
+    T = sum(counts)
+    gi = I.grouped_inputs(E, T, N, K, seed=2304, counts=counts)
+    qa, sa, qw, sw = quantize_grouped_pow2(gi) if pow2 else quantize_grouped(gi)
+    R, found = oracle.grouped_gemm(qa, sa, qw, sw, gi.offsets)
+    fn = B.fp8_block_grouped_gemm_pow2 if pow2 else B.fp8_block_grouped_gemm
+    c = fn(dev(qa), dev(sa), dev(qw), dev(sw), dev(gi.offsets.astype(np.int32)), out_dtype="f32")
+    check_gemm(c, R, "f32", f"grouped G=18 (pow2={pow2})",
+               grouped_error_bound(qa, sa, qw, sw, gi.offsets, np.arange(T)))
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 1280), (300, 384, 1280), (4096, 7168, 640)])
+def test_gemm_scale_chunks_not_a_multiple(M, N, K):
+    # G = 10 or 5 K blocks: the last activation-scale chunk is partial (its
+    # scales fetched dword by dword so that nothing past the last row's
+    # scales is read).  Big tiles (4096 x 4096), the two tile widths (4096 x
+    # 7168) and small tiles (300 x 384), rows of every tile incl. the last.
+    g = I.gemm_inputs(M, N, K, seed=M + N + K, outlier_frac=0.01, outlier_mult=20.0)
+    qa, sa, qw, sw = quantize(g)
+    c = run_gemm(qa, sa, qw, sw, "f32")
+    rows = tile_rows(M, 128, per_tile=2)
+    R = oracle.block_gemm(qa, sa, qw, sw, rows)
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, "f32", f"G={K // 128} {M}x{N}x{K}",
+               gemm_error_bound(qa, sa, qw, sw, rows))
 
 
 def test_quant_then_gemm_chain_matches_oracle_chain():
@@ -424,4 +509,4 @@ def test_quant_then_gemm_chain_matches_oracle_chain():
     c = B.fp8_block_gemm(qa_d, sa_d, qw_d, sw_d, out_dtype="f32")
     qa, sa, qw, sw = quantize(g)
     R = oracle.block_gemm(qa, sa, qw, sw)
-    check_gemm(c, R, "f32", "quant->gemm chain")
+    check_gemm(c, R, "f32", "quant->gemm chain", gemm_error_bound(qa, sa, qw, sw))

@@ -14,7 +14,8 @@ import oracle
 from fp8_fine_grained_token_amd import binding as B
 from fp8_fine_grained_token_amd import inputs as I
 
-from .gpu_util import check_gemm, dev, dev_bf16, host, log, rel_fro, torch
+from .gpu_util import (check_gemm, dev, dev_bf16, gemm_error_bound, grouped_error_bound, host,
+                       log, rel_fro, tile_rows, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -107,7 +108,8 @@ def test_pow2_gemm_tiny_fp32_out():
     g = I.config_tiny(seed=0)
     qa, sa, qw, sw = quantize(g)
     R = oracle.block_gemm(qa, sa, qw, sw)
-    check_gemm(run_gemm(qa, sa, qw, sw, "f32"), R, "f32", "pow2 tiny 128x256x512 f32")
+    check_gemm(run_gemm(qa, sa, qw, sw, "f32"), R, "f32", "pow2 tiny 128x256x512 f32",
+               gemm_error_bound(qa, sa, qw, sw))
 
 
 @pytest.mark.parametrize("M", [1, 17, 129, 300])
@@ -117,7 +119,8 @@ def test_pow2_gemm_ragged(M, N, K, out):
     g = I.gemm_inputs(M, N, K, seed=M * 1000 + N + K + 1, outlier_frac=0.01, outlier_mult=20.0)
     qa, sa, qw, sw = quantize(g)
     R = oracle.block_gemm(qa, sa, qw, sw)
-    check_gemm(run_gemm(qa, sa, qw, sw, out), R, out, f"pow2 {M}x{N}x{K} {out}")
+    check_gemm(run_gemm(qa, sa, qw, sw, out), R, out, f"pow2 {M}x{N}x{K} {out}",
+               gemm_error_bound(qa, sa, qw, sw))
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 2048, 7168), (128, 128, 8192)])
@@ -130,10 +133,12 @@ def test_pow2_gemm_split_k(M, N, K):
     nbytes = B.fp8_gemm_workspace_bytes(M, N, K, "bf16")
     assert nbytes > 0
     ws = t.empty(nbytes, dtype=t.uint8, device="cuda")
+    b = gemm_error_bound(qa, sa, qw, sw, splits=nbytes // (M * N * 4))
     for out in ("f32", "bf16"):
         check_gemm(run_gemm(qa, sa, qw, sw, out, workspace=ws), R, out,
-                   f"pow2 split-K {M}x{N}x{K} {out}")
-    check_gemm(run_gemm(qa, sa, qw, sw, "bf16"), R, "bf16", f"pow2 {M}x{N}x{K} no workspace")
+                   f"pow2 split-K {M}x{N}x{K} {out}", b)
+    check_gemm(run_gemm(qa, sa, qw, sw, "bf16"), R, "bf16", f"pow2 {M}x{N}x{K} no workspace",
+               gemm_error_bound(qa, sa, qw, sw))
 
 
 @pytest.mark.parametrize("M,N,K", [(4000, 7040, 384), (4096, 6144, 512), (4096, 7168, 256)])
@@ -143,9 +148,10 @@ def test_pow2_gemm_large_tiles(M, N, K):
     g = I.gemm_inputs(M, N, K, seed=M + N + K + 2, outlier_frac=0.01, outlier_mult=20.0)
     qa, sa, qw, sw = quantize(g)
     c = run_gemm(qa, sa, qw, sw, "f32")
-    rows = np.unique(np.concatenate([np.arange(0, M, 113), [255, 256, M - 1]]))
+    rows = tile_rows(M, 256, per_tile=2, salt=1)
     R = oracle.block_gemm(qa, sa, qw, sw, rows)
-    check_gemm(c[torch().from_numpy(rows).cuda()], R, "f32", f"pow2 {M}x{N}x{K}")
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, "f32", f"pow2 {M}x{N}x{K}",
+               gemm_error_bound(qa, sa, qw, sw, rows))
 
 
 def test_pow2_gemm_dense_workload_sampled_rows_and_plain_path():
@@ -159,10 +165,11 @@ def test_pow2_gemm_dense_workload_sampled_rows_and_plain_path():
     rf = rel_fro(c, c_plain.astype(np.float64))
     log(f"  pow2 vs plain GEMM, 4096x7168x7168 f32: rel_fro={rf:.3e}")
     assert rf <= 1e-5
-    rows = np.array([0, 1, 255, 256, 2047, 2048, 4094, 4095])
-    log("  oracle GEMM on 8 sampled rows of 4096x7168x7168 ...")
+    rows = tile_rows(4096, 256, per_tile=1, salt=2)
+    log(f"  oracle GEMM on {rows.size} rows of 4096x7168x7168 ...")
     R = oracle.block_gemm(qa, sa, qw, sw, rows)
-    check_gemm(torch().from_numpy(c[rows]), R, "f32", "pow2 dense sampled rows")
+    check_gemm(torch().from_numpy(c[rows]), R, "f32", "pow2 dense rows of every tile",
+               gemm_error_bound(qa, sa, qw, sw, rows))
 
 
 def test_pow2_gemm_metamorphic_and_deterministic():
@@ -200,7 +207,8 @@ def test_pow2_grouped_edge_cases(counts, T, out):
                                   dev(gi.offsets.astype(np.int32)), out_dtype=out, c=c)
     routed = int(gi.offsets[-1])
     assert np.all(host(c)[routed:] == 7.0), "unrouted rows were written"
-    check_gemm(c[:routed], R[:routed], out, f"pow2 grouped {counts} {out}")
+    check_gemm(c[:routed], R[:routed], out, f"pow2 grouped {counts} {out}",
+               grouped_error_bound(qa, sa, qw, sw, gi.offsets, np.arange(routed)))
 
 
 def test_pow2_grouped_workload_sampled_rows():
@@ -210,14 +218,14 @@ def test_pow2_grouped_workload_sampled_rows():
     c = B.fp8_block_grouped_gemm_pow2(dev(qa), dev(sa), dev(qw), dev(sw),
                                       dev(gi.offsets.astype(np.int32)), out_dtype="bf16")
     off = gi.offsets
-    rng = np.random.default_rng(3)
     rows = []
     for e in range(gi.E):
         lo, hi = int(off[e]), int(off[e + 1])
         if hi > lo:
-            rows += [lo, hi - 1] + list(rng.integers(lo, hi, size=1))
-    rows = np.unique(np.array(rows))
-    log(f"  oracle grouped GEMM on {rows.size} sampled rows ...")
+            rows += list(lo + tile_rows(hi - lo, 128, 1, 7 + e))
+    rows = np.unique(np.array(rows, dtype=np.int64))
+    log(f"  oracle grouped GEMM on {rows.size} rows (every M tile of every expert) ...")
     R, found = oracle.grouped_gemm(qa, sa, qw, sw, off, rows)
     assert found.all()
-    check_gemm(c[torch().from_numpy(rows).cuda()], R, "bf16", "pow2 grouped workload rows")
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, "bf16", "pow2 grouped workload rows",
+               grouped_error_bound(qa, sa, qw, sw, off, rows))
