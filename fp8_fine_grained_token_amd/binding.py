@@ -52,6 +52,8 @@ _SIGNATURES = {
     "fp8_transpose_weight_128x128": ([_P, _P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "fp8_block_gemm_wgrad": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P],
                              ctypes.c_int),
+    "fp8_block_gemm_noalloc": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P],
+                               ctypes.c_int),
     "fp8_quant_act_1x128_pow2": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "fp8_quant_weight_128x128_pow2": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "fp8_block_gemm_pow2": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P,
@@ -244,6 +246,31 @@ def fp8_block_gemm(a, sa, w, sw, out_dtype="bf16", c=None, workspace=None, strea
     """C[M][N] = block-scaled product of a [M][K] E4M3 (scales [M][K/128]) and
     w [N][K] E4M3 (scales [N/128][K/128]); bf16 or fp32 output."""
     return _block_gemm("fp8_block_gemm", a, sa, w, sw, out_dtype, c, workspace, stream)
+
+
+def fp8_block_gemm_noalloc(a, sa, w, sw, out_dtype="bf16", c=None, stream=None):
+    """fp8_block_gemm whose split-K partials live in the library's static
+    device scratch array (no workspace, no allocation by the library; c is
+    allocated here with torch only when not given).  Calls that overlap on
+    one GPU race on that array."""
+    torch = _torch()
+    _rank(a, "a", 2)
+    _rank(w, "w", 2)
+    M, K = a.shape
+    N = w.shape[0]
+    code, tdt = _out_code(out_dtype)
+    if c is None:
+        c = torch.empty((M, N), dtype=tdt, device=a.device)
+    _shape(w, "w", (N, K))
+    if K % 128 == 0 and N % 128 == 0:
+        _shape(sa, "sa", (M, K // 128))
+        _shape(sw, "sw", (N // 128, K // 128))
+    _shape(c, "c", (M, N))
+    fn = "fp8_block_gemm_noalloc"
+    _check(getattr(lib(), fn)(_dev(a, "a", torch.uint8), _dev(sa, "sa", torch.float32),
+                              _dev(w, "w", torch.uint8), _dev(sw, "sw", torch.float32),
+                              _dev(c, "c", tdt), code, M, N, K, _stream_handle(stream)), fn)
+    return c
 
 
 def fp8_block_gemm_pow2(a, sa, w, sw, out_dtype="bf16", c=None, workspace=None, stream=None):

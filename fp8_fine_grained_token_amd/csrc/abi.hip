@@ -154,6 +154,22 @@ fp8_status fp8_block_gemm(const void *a_e4m3, const float *a_scales, const void 
                       workspace_bytes, false, hip_stream);
 }
 
+fp8_status fp8_block_gemm_noalloc(const void *a_e4m3, const float *a_scales,
+                                  const void *w_e4m3, const float *w_scales, void *c,
+                                  int out_dtype, int64_t M, int64_t N, int64_t K,
+                                  void *hip_stream) {
+    fp8_status st = check_gemm_common(a_e4m3, a_scales, w_e4m3, w_scales, c, out_dtype, M, N, K,
+                                      nullptr, 0);
+    if (st != FP8_OK || M == 0 || N == 0) return st;
+    if (K == 0) return FP8_ERR_SHAPE;
+    if (fp8blk::gemm_workspace_bytes(M, N, K) > fp8blk::noalloc_scratch_bytes())
+        return FP8_ERR_WORKSPACE;
+    clear_last_error();
+    return from_hip(fp8blk::launch_block_gemm_noalloc(a_e4m3, a_scales, w_e4m3, w_scales, c,
+                                                      out_dtype == FP8_OUT_BF16, M, N, K,
+                                                      as_stream(hip_stream)));
+}
+
 fp8_status fp8_block_gemm_pow2(const void *a_e4m3, const float *a_scales, const void *w_e4m3,
                                const float *w_scales, void *c, int out_dtype, int64_t M,
                                int64_t N, int64_t K, void *workspace, size_t workspace_bytes,

@@ -41,6 +41,13 @@ hipError_t launch_block_gemm(const void *a, const float *sa, const void *w, cons
                              void *workspace, size_t workspace_bytes, bool pow2,
                              hipStream_t stream);
 
+// fp8_block_gemm with its split-K partials in the library's static device
+// scratch array (noalloc_scratch_bytes() of it) instead of a workspace.
+size_t noalloc_scratch_bytes();
+hipError_t launch_block_gemm_noalloc(const void *a, const float *sa, const void *w,
+                                     const float *sw, void *c, bool bf16_out, int64_t M,
+                                     int64_t N, int64_t K, hipStream_t stream);
+
 hipError_t launch_grouped_gemm(const void *a, const float *sa, const void *w, const float *sw,
                                const int32_t *offsets, int64_t E, int64_t T, void *c,
                                bool bf16_out, int64_t N, int64_t K, bool pow2,

@@ -27,9 +27,13 @@
  *     next synchronization on that stream.
  *   - Arguments are validated before anything is enqueued; on any error
  *     nothing is written.  No C++ exception crosses this boundary.
- *   - The library keeps no mutable global state: calls are reentrant and
- *     thread-safe (concurrent calls on different streams must not share
- *     output or workspace buffers).
+ *   - Calls are reentrant and thread-safe (concurrent calls on different
+ *     streams must not share output or workspace buffers), with one
+ *     exception: fp8_block_gemm_noalloc.  The library's mutable state is
+ *     small and internal: a per-thread cache of the last Wgrad tile plan
+ *     (fp8_block_gemm_wgrad; the same shapes recur every step), and, for
+ *     fp8_block_gemm_noalloc, a static device scratch array per GPU with a
+ *     mutex-guarded table of its device addresses.
  *   - Sizes of zero (M = 0, T = 0, K = 0 for the quantizers) are valid no-ops.
  *   - Inputs must be finite; NaN/Inf inputs are outside the contract and are
  *     not checked.
@@ -242,6 +246,31 @@ fp8_status fp8_block_gemm_wgrad(const void *dy_t, const float *dy_t_scales,
                                 const void *x_t, const float *x_t_scales,
                                 void *dw, int out_dtype, int64_t N, int64_t K,
                                 int64_t T, void *hip_stream);
+
+/*
+ * fp8_block_gemm for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments, layouts, results and errors are those of fp8_block_gemm with no
+ * workspace argument: where fp8_block_gemm would split K through a
+ * workspace (fp8_gemm_workspace_bytes() > 0), this call puts the split-K
+ * partial sums in a static device array of FP8_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends, and it
+ * gives bitwise the same C as fp8_block_gemm with a workspace of
+ * fp8_gemm_workspace_bytes().  It calls no allocator.
+ *   - Shapes whose split-K partials would exceed FP8_NOALLOC_SCRATCH_BYTES
+ *     are rejected with FP8_ERR_WORKSPACE (with the current tile plans none
+ *     does: a plan splits at most 256 workgroups of 128 x 64 outputs).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (on different streams or host threads) race and give
+ *     undefined results.  Calls on one stream are ordered and safe.
+ *   - The array's device address is looked up (hipGetSymbolAddress) the
+ *     first time a GPU is used; an error there returns FP8_ERR_HIP.
+ */
+#define FP8_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+fp8_status fp8_block_gemm_noalloc(const void *a_e4m3, const float *a_scales,
+                                  const void *w_e4m3, const float *w_scales, void *c,
+                                  int out_dtype, int64_t M, int64_t N, int64_t K,
+                                  void *hip_stream);
 
 /* Workspace bytes that let fp8_block_gemm use its split-K path for this
  * shape (0 when the shape does not use it). */

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         method + [m + "_pow2" for m in method]
         + ["fp8_quant_act_128x1_t", "fp8_transpose_weight_128x128", "fp8_block_gemm_wgrad"]
-        + ["fp8_gemm_workspace_bytes", "fp8_status_string"])
+        + ["fp8_gemm_workspace_bytes", "fp8_status_string", "fp8_block_gemm_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -134,6 +134,28 @@ def test_grouped_argument_errors(suffix):
     assert grouped_(lib, ws=A16, wsb=0) == B.FP8_ERR_WORKSPACE
     # T = 0 is a no-op (E = 0 allowed then)
     assert grouped_(lib, T=0, E=0, a=NUL, sa=NUL, off=NUL, c=NUL) == B.FP8_OK
+
+
+def test_noalloc_gemm_argument_errors():
+    lib = B.lib()
+
+    def na(a=A16, sa=A16, w=A16, sw=A16, c=A16, dt=B.FP8_OUT_BF16, M=128, N=256, K=512):
+        return lib.fp8_block_gemm_noalloc(a, sa, w, sw, c, dt, M, N, K, NUL)
+    assert na(K=500) == B.FP8_ERR_SHAPE
+    assert na(N=200) == B.FP8_ERR_SHAPE
+    assert na(M=-1) == B.FP8_ERR_SHAPE
+    assert na(dt=7) == B.FP8_ERR_DTYPE
+    assert na(a=NUL) == B.FP8_ERR_NULL
+    assert na(c=A8) == B.FP8_ERR_ALIGN
+    assert na(K=0) == B.FP8_ERR_SHAPE
+    assert na(M=0, a=NUL, sa=NUL, c=NUL) == B.FP8_OK
+    # every split-K plan fits the static scratch array: the largest
+    # workspace any shape asks for is 256 workgroups of 128 x 64 FP32
+    worst = max(lib.fp8_gemm_workspace_bytes(m, n, k, B.FP8_OUT_F32)
+                for m in (1, 64, 128, 200, 256, 512, 1024)
+                for n in (128, 256, 1024, 2048, 4096, 8192)
+                for k in (512, 2048, 7168, 65536))
+    assert 0 < worst <= 8 << 20
 
 
 def test_backward_argument_errors():
