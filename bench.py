@@ -7,29 +7,36 @@ One step = one pass of the hot path over one batch of tokens:
 The metric is the step's FP8 GEMM throughput in TFLOP/s (2*M*N*K algorithmic
 flops per step over the measured step time, quantization included).
 
+Order of the run: inputs; the CPU oracle baseline (host only); the
+per-kernel parts (each kernel on its own workload); a fixed untimed pre-roll
+of steps (PREROLL_S seconds, so the timed region starts at the clock the GPU
+sustains on this work); the W warm-up steps; the K timed steps.
+
 Printed as one JSON line, with:
   * roofline: the dominant kernel (the GEMM), its algorithmic flops over its
     average duration measured with HIP events on its stream inside the timed
-    region, against the dense FP8 MFMA peak; traffic = HBM bytes per launch
-    from committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by the
-    copy-kernel calibration, or null if the kernel source changed since;
-  * parts: each kernel on its own workload with the caches flushed before
-    every launch (act quantizer GB/s vs HBM, beside a plain device copy of
-    the same byte count, each also back to back over rotating buffers that
-    exceed the caches; dense / decode / grouped GEMM TFLOP/s vs MFMA and
-    GB/s vs HBM), the power-of-two-scale variants (quantizer, dense and
-    grouped GEMM on the block-scaled MFMA) on the same workloads, and the
-    backward pass of the same linear layer (the 128x1 transposed quantizer
-    on dY and X, the weight transpose, Dgrad on the transposed weights,
-    Wgrad over the 4096 tokens);
-  * cpu_baseline: the CPU oracle timed on this host on a bounded sample of
-    the same step (first 512 tokens, ~11 s of CPU work).
+    region, against the dense FP8 MFMA peak; the shader clock sampled over
+    the last part of a fixed untimed pre-roll of steps and the timed region;
+    the same kernel's flushed per-part fraction beside it;
+    traffic = HBM bytes per launch from committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE counters, scaled by the copy-kernel calibration, or null if
+    the kernel source changed since;
+  * parts: each kernel on its own workload, 5 untimed launches then at least
+    50 timed ones, with a 512 MB read before every timed launch so operands
+    come from HBM (median, p10, p90); the act quantizer and a plain device
+    copy also back to back over rotating buffers that exceed the caches;
+    the tiny GEMM as launch latency; dense / decode / grouped GEMMs (TFLOP/s
+    vs MFMA, GB/s vs HBM); the power-of-two-scale variants; the fused
+    quantize-and-multiply GEMM; the backward pass of the same linear layer;
+  * cpu_baseline: the CPU oracle timed on this host: the step on a bounded
+    sample (first 512 tokens), and per workload (quantizer GB/s single- and
+    multi-threaded, tiny GEMM in full, dense on a sample, decode in full,
+    grouped on a per-expert stratified eighth of the rows).
 
 Usage: python bench.py [--gpus 1] [--steps 500] [--warmup 300]
-       [--no-parts] [--no-cpu-baseline] [--copy-calib]
-The default warmup (~70 ms of steps) lets the GPU reach its sustained clock
-before timing; with a few warmup steps the timed region starts while the
-clock is still ramping up after input generation, and reads ~20% slow.
+       [--no-parts] [--no-cpu-baseline] [--copy-calib] [--part NAME]
+--part NAME runs only that part (for kernel traces of one kernel) and prints
+its JSON.
 """
 from __future__ import annotations
 
@@ -37,7 +44,9 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -50,7 +59,10 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_dense_gemm.json")
 GEMM_SOURCE = os.path.join(ROOT, "fp8_fine_grained_token_amd", "csrc", "gemm.hip")
 
 M, N, K = 4096, 7168, 7168
-CPU_SAMPLE_ROWS = 512  # ~11 s of oracle work on 16 host threads
+CPU_SAMPLE_ROWS = 512   # ~11 s of oracle work on 16 host threads
+PART_WARMUP = 5
+PART_ITERS = 50
+PREROLL_S = 0.4         # untimed steps before the warm-up steps
 
 
 def log(msg):
@@ -98,12 +110,68 @@ class Timer:
         self.ev[self.i][1].record()
         self.i += 1
 
-    def mean_ms(self):
-        return sum(a.elapsed_time(b) for a, b in self.ev[: self.i]) / max(self.i, 1)
+    def times_ms(self):
+        return [a.elapsed_time(b) for a, b in self.ev[: self.i]]
 
-    def median_ms(self):
-        v = sorted(a.elapsed_time(b) for a, b in self.ev[: self.i])
-        return v[len(v) // 2] if v else 0.0
+    def mean_ms(self):
+        v = self.times_ms()
+        return sum(v) / max(len(v), 1)
+
+
+class ClockSampler:
+    """Shader (GFX) clock of GPU 0 sampled every few ms from the SMU through
+    amdsmi while running; reports mean / min / max in MHz."""
+
+    def __init__(self):
+        self.samples, self.error, self.max_mhz = [], None, None
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            info = amdsmi.amdsmi_get_clock_info(self._h, amdsmi.AmdSmiClkType.GFX)
+            self.max_mhz = info.get("max_clk")
+        except Exception as e:  # noqa: BLE001 - reported in the JSON
+            self._amdsmi = None
+            self.error = f"{type(e).__name__}: {e}"
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                info = self._amdsmi.amdsmi_get_clock_info(self._h, self._amdsmi.AmdSmiClkType.GFX)
+                self.samples.append(float(info["clk"]))
+            except Exception as e:  # noqa: BLE001
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(0.002)
+
+    def start(self):
+        if self._amdsmi is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        if not self.samples:
+            return {"mhz_mean": None, "error": self.error or "no samples"}
+        s = self.samples
+        return {"mhz_mean": round(sum(s) / len(s), 1), "mhz_min": min(s), "mhz_max": max(s),
+                "samples": len(s), "max_sclk_mhz": self.max_mhz, "source": "amdsmi GFX clock"}
+
+
+_GROUPED = []
+
+
+def grouped_workload(I):
+    """The grouped workload's inputs, generated once per run."""
+    if not _GROUPED:
+        log("bench: generating the grouped workload ...")
+        _GROUPED.append(I.config_grouped(seed=0))
+    return _GROUPED[0]
 
 
 def to_dev_bf16(torch, bits):
@@ -111,62 +179,49 @@ def to_dev_bf16(torch, bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
-    """Each kernel on its own workload.  Before every launch a 512 MB buffer
-    is read (twice the 256 MB Infinity Cache), so operands come from HBM; a
-    read leaves no dirty lines whose write-back would land in the timed
-    launch."""
-    import numpy as np
-    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
-    parts = {}
+class Parts:
+    """Per-kernel timings.  Before every timed launch a 512 MB buffer is read
+    (twice the 256 MB Infinity Cache), so operands come from HBM; a read
+    leaves no dirty lines whose write-back would land in the timed launch."""
 
-    spread_us = {}  # p10 / p90 of the last measurement, in µs
+    def __init__(self, torch, iters=PART_ITERS):
+        self.torch = torch
+        self.iters = iters
+        self.flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+        self.out = {}
 
-    def set_spread(v_ms):
+    @staticmethod
+    def _spread(v_ms):
         v = sorted(v_ms)
-        spread_us["p10_us"] = v[int(0.1 * (len(v) - 1))] * 1e3
-        spread_us["p90_us"] = v[int(0.9 * (len(v) - 1) + 0.5)] * 1e3
+        return {"p10_us": v[int(0.1 * (len(v) - 1))] * 1e3,
+                "p90_us": v[int(0.9 * (len(v) - 1) + 0.5)] * 1e3}
 
-    def spread():
-        return dict(spread_us)
-
-    def timed(fn, n):
+    def timed(self, fn, n=None):
+        """Median ms of n flushed launches after PART_WARMUP untimed ones."""
+        torch = self.torch
+        n = n or self.iters
+        for _ in range(PART_WARMUP):
+            fn()
         t = Timer(torch, n)
         for _ in range(n):
-            flush.sum()
+            self.flush.sum()
             t.start()
             fn()
             t.stop()
         torch.cuda.synchronize()
-        set_spread([a.elapsed_time(b) for a, b in t.ev[: t.i]])
-        return t.median_ms()
+        v = sorted(t.times_ms())
+        return v[len(v) // 2], self._spread(v)
 
-    # activation quantizer, 4096 x 7168
-    ms = timed(lambda: F.fp8_quant_act_1x128(X, qa, sa), iters)
-    b = quant_bytes(M, K)
-    parts["act_quant_4096x7168"] = {
-        "us": ms * 1e3, **spread(), "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
-        "bytes": b}
-
-    # context: a plain device copy moving the quantizer's byte count
-    # (44.5 MB read + 44.5 MB written), timed the same way
-    src = torch.empty(quant_bytes(M, K) // 2, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    ms = timed(lambda: dst.copy_(src), iters)
-    parts["copy_reference_same_bytes"] = {
-        "us": ms * 1e3, **spread(), "GB/s": 2 * src.numel() / ms / 1e6,
-        "frac_hbm": 2 * src.numel() / ms / 1e6 / PEAK_HBM_GBS}
-    del src, dst
-
-    # The same quantizer and copy back to back, as a model's layers call
-    # them: one event pair around 6 x 8 launches that rotate over six
-    # input/output sets (534 MB, twice the Infinity Cache), so every launch
-    # still reads its input from HBM, while the launch latency that a
-    # single timed launch includes overlaps the previous kernel.
-    def back_to_back(fns, rounds=8, reps=5):
+    def back_to_back(self, fns, rounds=8, reps=10):
+        """Best per-launch ms over reps of (rounds x len(fns)) launches
+        bracketed by one event pair; fns rotate over buffers that exceed the
+        caches, so every launch still reads HBM."""
+        torch = self.torch
+        for fn in fns[:PART_WARMUP]:
+            fn()
         per_rep = []
         for _ in range(reps):
-            flush.sum()
+            self.flush.sum()
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record()
@@ -176,141 +231,181 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, iters=20):
             b.record()
             torch.cuda.synchronize()
             per_rep.append(a.elapsed_time(b) / (rounds * len(fns)))
-        set_spread(per_rep)
-        return min(per_rep)
+        return min(per_rep), self._spread(per_rep)
 
-    sets = [(X.clone(), torch.empty_like(qa), torch.empty_like(sa)) for _ in range(6)]
-    ms = back_to_back([lambda s=s: F.fp8_quant_act_1x128(s[0], s[1], s[2]) for s in sets])
+    def add_bytes(self, name, ms, spread, nbytes, **extra):
+        self.out[name] = {"us": ms * 1e3, **spread, "GB/s": nbytes / ms / 1e6,
+                          "frac_hbm": nbytes / ms / 1e6 / PEAK_HBM_GBS, "bytes": nbytes, **extra}
+
+    def add_flops(self, name, ms, spread, flops, nbytes=None, **extra):
+        d = {"us": ms * 1e3, **spread, "TFLOP/s": flops / ms / 1e9,
+             "frac_mfma": flops / ms / 1e9 / PEAK_FP8_TFLOPS}
+        if nbytes is not None:
+            d.update({"GB/s": nbytes / ms / 1e6, "frac_hbm": nbytes / ms / 1e6 / PEAK_HBM_GBS})
+        self.out[name] = {**d, **extra}
+
+
+def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=None):
+    import numpy as np
+    P = Parts(torch)
+    want = (lambda name: True) if only is None else (lambda name: name == only)
+
     b = quant_bytes(M, K)
-    parts["act_quant_4096x7168_back_to_back"] = {
-        "us": ms * 1e3, **spread(), "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
-        "launches": "6 sets x 8 rounds, best of 5"}
-    del sets
-    pairs = [(torch.empty(b // 2, dtype=torch.uint8, device="cuda"),
-              torch.empty(b // 2, dtype=torch.uint8, device="cuda")) for _ in range(6)]
-    ms = back_to_back([lambda p=p: p[1].copy_(p[0]) for p in pairs])
-    parts["copy_reference_same_bytes_back_to_back"] = {
-        "us": ms * 1e3, **spread(), "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
-    del pairs
+    if want("act_quant_4096x7168"):
+        P.add_bytes("act_quant_4096x7168", *P.timed(lambda: F.fp8_quant_act_1x128(X, qa, sa)), b)
+    if want("copy_reference_same_bytes"):
+        # a plain device copy moving the quantizer's byte count
+        src = torch.empty(b // 2, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        P.add_bytes("copy_reference_same_bytes", *P.timed(lambda: dst.copy_(src)), 2 * src.numel())
+        del src, dst
+    if want("act_quant_4096x7168_back_to_back"):
+        # back to back as a model's layers call it: six input/output sets
+        # (534 MB, twice the Infinity Cache) in rotation
+        sets = [(X.clone(), torch.empty_like(qa), torch.empty_like(sa)) for _ in range(6)]
+        ms, sp = P.back_to_back([lambda s=s: F.fp8_quant_act_1x128(s[0], s[1], s[2])
+                                 for s in sets])
+        P.add_bytes("act_quant_4096x7168_back_to_back", ms, sp, b,
+                    launches="6 sets x 8 rounds, best of 10")
+        del sets
+    if want("copy_reference_same_bytes_back_to_back"):
+        pairs = [(torch.empty(b // 2, dtype=torch.uint8, device="cuda"),
+                  torch.empty(b // 2, dtype=torch.uint8, device="cuda")) for _ in range(6)]
+        ms, sp = P.back_to_back([lambda p=p: p[1].copy_(p[0]) for p in pairs])
+        P.add_bytes("copy_reference_same_bytes_back_to_back", ms, sp, b)
+        del pairs
 
-    # dense GEMM alone, 4096 x 7168 x 7168
-    ms = timed(lambda: F.fp8_block_gemm(qa, sa, qw, sw, out_dtype="bf16", c=C), iters)
     fl = 2 * M * N * K
-    parts["dense_gemm_4096x7168x7168"] = {
-        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
+    if want("dense_gemm_4096x7168x7168"):
+        P.add_flops("dense_gemm_4096x7168x7168",
+                    *P.timed(lambda: F.fp8_block_gemm(qa, sa, qw, sw, out_dtype="bf16", c=C)), fl,
+                    dense_gemm_bytes(M, N, K))
 
-    # power-of-two scales: quantizer and dense GEMM on the same workload
-    pa, psa = F.fp8_quant_act_1x128_pow2(X)
-    pw, psw = F.fp8_quant_weight_128x128_pow2(Wb)
-    ms = timed(lambda: F.fp8_quant_act_1x128_pow2(X, pa, psa), iters)
-    b = quant_bytes(M, K)
-    parts["pow2_act_quant_4096x7168"] = {
-        "us": ms * 1e3, **spread(), "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
-    ms = timed(lambda: F.fp8_block_gemm_pow2(pa, psa, pw, psw, out_dtype="bf16", c=C), iters)
-    parts["pow2_dense_gemm_4096x7168x7168"] = {
-        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
-    del pa, psa, pw, psw
+    if want("tiny_gemm_128x256x512_f32"):
+        g = I.config_tiny(seed=0)
+        ta, tsa = F.fp8_quant_act_1x128(to_dev_bf16(torch, g.a_bf16))
+        tw, tsw = F.fp8_quant_weight_128x128(to_dev_bf16(torch, g.w_bf16))
+        tc = torch.empty((128, 256), dtype=torch.float32, device="cuda")
+        ms, sp = P.timed(lambda: F.fp8_block_gemm(ta, tsa, tw, tsw, out_dtype="f32", c=tc))
+        tfl = 2 * 128 * 256 * 512
+        P.add_flops("tiny_gemm_128x256x512_f32", ms, sp, tfl,
+                    note="launch-latency bound: one launch after a cache flush")
+        del ta, tsa, tw, tsw, tc
+
+    if want("pow2_act_quant_4096x7168") or want("pow2_dense_gemm_4096x7168x7168"):
+        pa, psa = F.fp8_quant_act_1x128_pow2(X)
+        pw, psw = F.fp8_quant_weight_128x128_pow2(Wb)
+        if want("pow2_act_quant_4096x7168"):
+            P.add_bytes("pow2_act_quant_4096x7168",
+                        *P.timed(lambda: F.fp8_quant_act_1x128_pow2(X, pa, psa)), b)
+        if want("pow2_dense_gemm_4096x7168x7168"):
+            P.add_flops("pow2_dense_gemm_4096x7168x7168",
+                        *P.timed(lambda: F.fp8_block_gemm_pow2(pa, psa, pw, psw, out_dtype="bf16",
+                                                               c=C)), fl)
+        del pa, psa, pw, psw
+
+    if hasattr(F, "fp8_block_gemm_fused_quant") and want("fused_quant_gemm_4096x7168x7168"):
+        # bf16 activations quantized inside the GEMM (no E4M3 round trip)
+        P.add_flops("fused_quant_gemm_4096x7168x7168",
+                    *P.timed(lambda: F.fp8_block_gemm_fused_quant(X, qw, sw, out_dtype="bf16",
+                                                                  c=C)), fl)
 
     # backward of the same layer: dY [4096][7168] (same distribution as X
     # without outliers); Dgrad = forward GEMM with the transposed weights,
     # Wgrad = dY^T X from 128x1 tiles
-    dy = to_dev_bf16(torch, I.activations(np.random.default_rng(7), M, N, 0.0, 1.0)[0])
-    ms = timed(lambda: F.fp8_quant_act_128x1_t(dy), iters)
-    b = quant_bytes(M, N)
-    parts["bwd_quant_128x1_t_4096x7168"] = {
-        "us": ms * 1e3, **spread(), "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
-    qdy, sdy = F.fp8_quant_act_1x128(dy)
-    qwt, swt = F.fp8_transpose_weight_128x128(qw, sw)
-    # the weight transpose Dgrad reads, once per weight update
-    ms = timed(lambda: F.fp8_transpose_weight_128x128(qw, sw, qwt, swt), iters)
-    b = 2 * N * K + 2 * 4 * (N // 128) * (K // 128)
-    parts["bwd_transpose_weight_7168x7168"] = {
-        "us": ms * 1e3, **spread(), "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
-    dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
-    ms = timed(lambda: F.fp8_block_gemm(qdy, sdy, qwt, swt, out_dtype="bf16", c=dx), iters)
-    parts["bwd_dgrad_4096x7168x7168"] = {
-        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
-    qdy_t, sdy_t = F.fp8_quant_act_128x1_t(dy)
-    qx_t, sx_t = F.fp8_quant_act_128x1_t(X)
-    dw = torch.empty((N, K), dtype=torch.float32, device="cuda")
-    ms = timed(lambda: F.fp8_block_gemm_wgrad(qdy_t, sdy_t, qx_t, sx_t, out_dtype="f32", dw=dw),
-               iters)
-    parts["bwd_wgrad_7168x7168_over_4096"] = {
-        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS}
-    del dy, qdy, sdy, qwt, swt, dx, qdy_t, sdy_t, qx_t, sx_t, dw
+    bwd = [n for n in ("bwd_quant_128x1_t_4096x7168", "bwd_transpose_weight_7168x7168",
+                       "bwd_dgrad_4096x7168x7168", "bwd_wgrad_7168x7168_over_4096") if want(n)]
+    if bwd:
+        dy = to_dev_bf16(torch, I.activations(np.random.default_rng(7), M, N, 0.0, 1.0)[0])
+        if want("bwd_quant_128x1_t_4096x7168"):
+            P.add_bytes("bwd_quant_128x1_t_4096x7168",
+                        *P.timed(lambda: F.fp8_quant_act_128x1_t(dy)), quant_bytes(M, N))
+        qdy, sdy = F.fp8_quant_act_1x128(dy)
+        qwt, swt = F.fp8_transpose_weight_128x128(qw, sw)
+        if want("bwd_transpose_weight_7168x7168"):
+            P.add_bytes("bwd_transpose_weight_7168x7168",
+                        *P.timed(lambda: F.fp8_transpose_weight_128x128(qw, sw, qwt, swt)),
+                        2 * N * K + 2 * 4 * (N // 128) * (K // 128))
+        if want("bwd_dgrad_4096x7168x7168"):
+            dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+            P.add_flops("bwd_dgrad_4096x7168x7168",
+                        *P.timed(lambda: F.fp8_block_gemm(qdy, sdy, qwt, swt, out_dtype="bf16",
+                                                          c=dx)), fl)
+            del dx
+        if want("bwd_wgrad_7168x7168_over_4096"):
+            qdy_t, sdy_t = F.fp8_quant_act_128x1_t(dy)
+            qx_t, sx_t = F.fp8_quant_act_128x1_t(X)
+            dw = torch.empty((N, K), dtype=torch.float32, device="cuda")
+            P.add_flops("bwd_wgrad_7168x7168_over_4096",
+                        *P.timed(lambda: F.fp8_block_gemm_wgrad(qdy_t, sdy_t, qx_t, sx_t,
+                                                                out_dtype="f32", dw=dw)), fl)
+            del qdy_t, sdy_t, qx_t, sx_t, dw
+        del dy, qdy, sdy, qwt, swt
 
     # decode GEMM, 256 x 2048 x 7168 (split-K with workspace)
-    gd = I.config_decode(seed=0)
-    xa = to_dev_bf16(torch, gd.a_bf16)
-    xw = to_dev_bf16(torch, gd.w_bf16)
-    da, dsa = F.fp8_quant_act_1x128(xa)
-    dw, dsw = F.fp8_quant_weight_128x128(xw)
-    nbytes = F.fp8_gemm_workspace_bytes(256, 2048, 7168, "bf16")
-    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda") if nbytes else None
-    dc = torch.empty((256, 2048), dtype=torch.bfloat16, device="cuda")
-    ms = timed(lambda: F.fp8_block_gemm(da, dsa, dw, dsw, out_dtype="bf16", c=dc, workspace=ws),
-               iters)
-    fl = 2 * 256 * 2048 * 7168
-    b = dense_gemm_bytes(256, 2048, 7168)
-    parts["decode_gemm_256x2048x7168"] = {
-        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
-        "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
-        "split_k_workspace_bytes": nbytes}
-    # back to back, as a decode step calls one layer after another: 40
-    # operand sets (16.5 MB of operands each, 700 MB in all) in rotation
-    sets = [(da.clone(), dsa.clone(), dw.clone(), dsw.clone(), torch.empty_like(dc))
-            for _ in range(40)]
-    ms = back_to_back([lambda s=s: F.fp8_block_gemm(s[0], s[1], s[2], s[3], out_dtype="bf16",
-                                                    c=s[4], workspace=ws) for s in sets],
-                      rounds=2)
-    parts["decode_gemm_256x2048x7168_back_to_back"] = {
-        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
-        "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
-        "launches": "40 sets x 2 rounds, best of 5"}
-    del sets
-    del xa, xw, da, dsa, dw, dsw, ws, dc
+    dec = [n for n in ("decode_gemm_256x2048x7168", "decode_gemm_256x2048x7168_back_to_back")
+           if want(n)]
+    if dec:
+        gd = I.config_decode(seed=0)
+        da, dsa = F.fp8_quant_act_1x128(to_dev_bf16(torch, gd.a_bf16))
+        dw, dsw = F.fp8_quant_weight_128x128(to_dev_bf16(torch, gd.w_bf16))
+        nbytes = F.fp8_gemm_workspace_bytes(256, 2048, 7168, "bf16")
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda") if nbytes else None
+        dc = torch.empty((256, 2048), dtype=torch.bfloat16, device="cuda")
+        dfl = 2 * 256 * 2048 * 7168
+        db = dense_gemm_bytes(256, 2048, 7168)
+        if want("decode_gemm_256x2048x7168"):
+            P.add_flops("decode_gemm_256x2048x7168",
+                        *P.timed(lambda: F.fp8_block_gemm(da, dsa, dw, dsw, out_dtype="bf16",
+                                                          c=dc, workspace=ws)), dfl, db,
+                        split_k_workspace_bytes=nbytes)
+        if want("decode_gemm_256x2048x7168_back_to_back"):
+            # back to back, as a decode step calls one layer after another:
+            # 40 operand sets (16.5 MB each, 700 MB in all) in rotation
+            sets = [(da.clone(), dsa.clone(), dw.clone(), dsw.clone(), torch.empty_like(dc))
+                    for _ in range(40)]
+            ms, sp = P.back_to_back([lambda s=s: F.fp8_block_gemm(s[0], s[1], s[2], s[3],
+                                                                  out_dtype="bf16", c=s[4],
+                                                                  workspace=ws)
+                                     for s in sets], rounds=2)
+            P.add_flops("decode_gemm_256x2048x7168_back_to_back", ms, sp, dfl, db,
+                        launches="40 sets x 2 rounds, best of 10")
+            del sets
+        del da, dsa, dw, dsw, ws, dc
 
     # grouped MoE GEMM, 32 experts / 8192 tokens, N=4096, K=7168
-    log("bench: generating the grouped workload ...")
-    gi = I.config_grouped(seed=0)
-    ga = to_dev_bf16(torch, gi.a_bf16)
-    gq, gsa = F.fp8_quant_act_1x128(ga)
-    del ga
-    gwb = to_dev_bf16(torch, gi.w_bf16.reshape(gi.E * gi.N, gi.K))
-    gw, gsw = F.fp8_quant_weight_128x128(gwb)
-    del gwb
-    gw = gw.view(gi.E, gi.N, gi.K)
-    gsw = gsw.view(gi.E, gi.N // 128, gi.K // 128)
-    off = torch.from_numpy(gi.offsets).cuda()
-    gc = torch.empty((gi.T, gi.N), dtype=torch.bfloat16, device="cuda")
-    ms = timed(lambda: F.fp8_block_grouped_gemm(gq, gsa, gw, gsw, off, out_dtype="bf16", c=gc),
-               iters)
-    fl = 2 * int(gi.counts.sum()) * gi.N * gi.K
-    b = (gi.T * gi.K + gi.E * gi.N * gi.K + gi.T * gi.N * 2 + 4 * gi.T * (gi.K // 128)
-         + 4 * gi.E * (gi.N // 128) * (gi.K // 128))
-    parts["grouped_gemm_e32_t8192_n4096_k7168"] = {
-        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
-        "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS,
-        "counts": [int(c) for c in gi.counts]}
-    del gq, gsa, gw, gsw
-
-    # the same grouped workload with power-of-two scales
-    ga = to_dev_bf16(torch, gi.a_bf16)
-    gq, gsa = F.fp8_quant_act_1x128_pow2(ga)
-    del ga
-    gwb = to_dev_bf16(torch, gi.w_bf16.reshape(gi.E * gi.N, gi.K))
-    gw, gsw = F.fp8_quant_weight_128x128_pow2(gwb)
-    del gwb
-    gw = gw.view(gi.E, gi.N, gi.K)
-    gsw = gsw.view(gi.E, gi.N // 128, gi.K // 128)
-    ms = timed(lambda: F.fp8_block_grouped_gemm_pow2(gq, gsa, gw, gsw, off, out_dtype="bf16",
-                                                     c=gc), iters)
-    parts["pow2_grouped_gemm_e32_t8192_n4096_k7168"] = {
-        "us": ms * 1e3, **spread(), "TFLOP/s": fl / ms / 1e9, "frac_mfma": fl / ms / 1e9 / PEAK_FP8_TFLOPS,
-        "GB/s": b / ms / 1e6, "frac_hbm": b / ms / 1e6 / PEAK_HBM_GBS}
-    del gq, gsa, gw, gsw, gc, flush
+    grp = [n for n in ("grouped_gemm_e32_t8192_n4096_k7168",
+                       "pow2_grouped_gemm_e32_t8192_n4096_k7168") if want(n)]
+    if grp:
+        gi = grouped_workload(I)
+        off = torch.from_numpy(gi.offsets).cuda()
+        gc = torch.empty((gi.T, gi.N), dtype=torch.bfloat16, device="cuda")
+        gfl = 2 * int(gi.counts.sum()) * gi.N * gi.K
+        gb = (gi.T * gi.K + gi.E * gi.N * gi.K + gi.T * gi.N * 2 + 4 * gi.T * (gi.K // 128)
+              + 4 * gi.E * (gi.N // 128) * (gi.K // 128))
+        for name, qa_fn, qw_fn, gemm in (
+                ("grouped_gemm_e32_t8192_n4096_k7168", F.fp8_quant_act_1x128,
+                 F.fp8_quant_weight_128x128, F.fp8_block_grouped_gemm),
+                ("pow2_grouped_gemm_e32_t8192_n4096_k7168", F.fp8_quant_act_1x128_pow2,
+                 F.fp8_quant_weight_128x128_pow2, F.fp8_block_grouped_gemm_pow2)):
+            if not want(name):
+                continue
+            ga = to_dev_bf16(torch, gi.a_bf16)
+            gq, gsa = qa_fn(ga)
+            del ga
+            gwb = to_dev_bf16(torch, gi.w_bf16.reshape(gi.E * gi.N, gi.K))
+            gw, gsw = qw_fn(gwb)
+            del gwb
+            gw = gw.view(gi.E, gi.N, gi.K)
+            gsw = gsw.view(gi.E, gi.N // 128, gi.K // 128)
+            extra = {"counts": [int(c) for c in gi.counts]} if not name.startswith("pow2") else {}
+            P.add_flops(name, *P.timed(lambda: gemm(gq, gsa, gw, gsw, off, out_dtype="bf16",
+                                                    c=gc)), gfl, gb, **extra)
+            del gq, gsa, gw, gsw
+        del gc, off
+    del P.flush
     torch.cuda.empty_cache()
-    return parts
+    return P.out
 
 
 def copy_calibration(torch, nbytes=1 << 30, iters=5):
@@ -323,22 +418,83 @@ def copy_calibration(torch, nbytes=1 << 30, iters=5):
     return {"copy_bytes_each_way": nbytes, "iters": iters}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(I, X_bits, w_bits):
-    """The oracle on the first CPU_SAMPLE_ROWS tokens of the same step."""
+    """The oracle as it stands, on this host's cores: the step on its first
+    CPU_SAMPLE_ROWS tokens (the headline figure), and each workload."""
     import numpy as np
     import oracle
+    cores = oracle.max_threads()    # OMP_NUM_THREADS, else the host's cores
+
+    def clock(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return time.perf_counter() - t0, r
+
     x = np.ascontiguousarray(X_bits[:CPU_SAMPLE_ROWS])
     qw, sw = oracle.quant_weight_128x128(w_bits)      # offline weights, not timed
-    t0 = time.perf_counter()
-    qa, sa = oracle.quant_act_1x128(x)
-    oracle.block_gemm(qa, sa, qw, sw)
-    dt = time.perf_counter() - t0
+
+    def step():
+        qa, sa = oracle.quant_act_1x128(x)
+        return oracle.block_gemm(qa, sa, qw, sw)
+    dt, _ = clock(step)
     flops = 2 * CPU_SAMPLE_ROWS * N * K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
-            "kind": "oracle", "seconds": dt,
-            "sample": f"first {CPU_SAMPLE_ROWS} of {M} tokens: 1x128 quantization of "
-                      f"{CPU_SAMPLE_ROWS}x{K} + binary64 block-scaled GEMM "
-                      f"{CPU_SAMPLE_ROWS}x{N}x{K}"}
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+           "kind": "oracle", "seconds": dt, "cpu_model": cpu_model(),
+           "sample": f"first {CPU_SAMPLE_ROWS} of {M} tokens: 1x128 quantization of "
+                     f"{CPU_SAMPLE_ROWS}x{K} + binary64 block-scaled GEMM "
+                     f"{CPU_SAMPLE_ROWS}x{N}x{K}"}
+    per = {}
+    # quantizer, 4096 x 7168 in full: multi- and single-threaded
+    b = quant_bytes(M, K)
+    dt, _ = clock(lambda: oracle.quant_act_1x128(X_bits))
+    per["act_quant_4096x7168"] = {"GB/s": b / dt / 1e9, "seconds": dt, "threads": cores}
+    oracle.set_threads(1)
+    dt, _ = clock(lambda: oracle.quant_act_1x128(X_bits))
+    per["act_quant_4096x7168_single_thread"] = {"GB/s": b / dt / 1e9, "seconds": dt,
+                                                "threads": 1}
+    oracle.set_threads(cores)
+    # tiny GEMM in full
+    g = I.config_tiny(seed=0)
+    tqa, tsa = oracle.quant_act_1x128(g.a_bf16)
+    tqw, tsw = oracle.quant_weight_128x128(g.w_bf16)
+    dt, _ = clock(lambda: oracle.block_gemm(tqa, tsa, tqw, tsw))
+    per["tiny_gemm_128x256x512"] = {"GFLOP/s": 2 * 128 * 256 * 512 / dt / 1e9, "us": dt * 1e6}
+    # dense: the headline sample above (GEMM part)
+    per["dense_gemm_4096x7168x7168"] = {"GFLOP/s": flops / out["seconds"] / 1e9,
+                                        "sample": f"first {CPU_SAMPLE_ROWS} rows, with their "
+                                                  "quantization"}
+    # decode in full
+    gd = I.config_decode(seed=0)
+    dqa, dsa = oracle.quant_act_1x128(gd.a_bf16)
+    dqw, dsw = oracle.quant_weight_128x128(gd.w_bf16)
+    dt, _ = clock(lambda: oracle.block_gemm(dqa, dsa, dqw, dsw))
+    per["decode_gemm_256x2048x7168"] = {"GFLOP/s": 2 * 256 * 2048 * 7168 / dt / 1e9,
+                                        "seconds": dt}
+    # grouped: every 8th routed row of each expert (stratified eighth)
+    gi = grouped_workload(I)
+    gqa, gsa = oracle.quant_act_1x128(gi.a_bf16)
+    gqw, gsw = oracle.quant_weight_128x128(gi.w_bf16.reshape(gi.E * gi.N, gi.K))
+    gqw = gqw.reshape(gi.E, gi.N, gi.K)
+    gsw = gsw.reshape(gi.E, gi.N // 128, gi.K // 128)
+    rows = np.concatenate([np.arange(gi.offsets[e], gi.offsets[e + 1])[::8]
+                           for e in range(gi.E)]).astype(np.int64)
+    dt, _ = clock(lambda: oracle.grouped_gemm(gqa, gsa, gqw, gsw, gi.offsets, rows))
+    per["grouped_gemm_e32_t8192_n4096_k7168"] = {
+        "GFLOP/s": 2 * rows.size * gi.N * gi.K / dt / 1e9, "seconds": dt,
+        "sample": f"{rows.size} rows: every 8th routed row of each expert"}
+    out["per_workload"] = per
+    return out
 
 
 def main():
@@ -349,6 +505,7 @@ def main():
     ap.add_argument("--no-parts", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--part", default=None, help="run only this part and print it")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the hot path is data-parallel and this "
@@ -372,7 +529,24 @@ def main():
     qa = torch.empty((M, K), dtype=torch.uint8, device="cuda")
     sa = torch.empty((M, K // 128), dtype=torch.float32, device="cuda")
     C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    F.fp8_quant_act_1x128(X, qa, sa)
     torch.cuda.synchronize()
+
+    if args.part:
+        parts = measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=args.part)
+        if not parts:
+            print(f"bench.py: no part named {args.part}", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"parts": parts}), flush=True)
+        return
+
+    result_tail = {}
+    if not args.no_cpu_baseline:
+        log("bench: CPU oracle baseline ...")
+        result_tail["cpu_baseline"] = cpu_baseline(I, X_bits, w_bits)
+    if not args.no_parts:
+        log("bench: per-kernel parts ...")
+        result_tail["parts"] = measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C)
 
     gemm_t = Timer(torch, args.steps)
 
@@ -387,6 +561,25 @@ def main():
         if timed:
             gemm_t.stop()
 
+    # Fixed untimed pre-roll: the step itself for PREROLL_S seconds, so the
+    # timed region starts at the clock the GPU sustains on this work rather
+    # than on the ramp (20 timed steps are only ~5 ms).  The clock is
+    # sampled over the pre-roll's last part and the timed region.
+    log("bench: pre-roll and timed steps ...")
+    clk = ClockSampler()
+    t_pre = time.perf_counter()
+    sampling = False
+    n_pre = 0
+    while time.perf_counter() - t_pre < PREROLL_S:
+        for _ in range(10):
+            step(False)
+        n_pre += 10
+        torch.cuda.synchronize()
+        if not sampling and time.perf_counter() - t_pre > 0.5 * PREROLL_S:
+            clk.start()
+            sampling = True
+    if not sampling:
+        clk.start()
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
@@ -395,6 +588,7 @@ def main():
         step(True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    clock = clk.stop()
 
     ms_per_step = (t1 - t0) / args.steps * 1e3
     flops = 2 * M * N * K
@@ -402,6 +596,13 @@ def main():
     gemm_ms = gemm_t.mean_ms()
     achieved = flops / (gemm_ms * 1e-3) / 1e12
     props = torch.cuda.get_device_properties(0)
+    roof = {"bound": "mfma", "kernel": "dense_gemm_two_kind_kernel",
+            "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic_from_counters(),
+            "gemm_us": round(gemm_ms * 1e3, 2), "sclk_timed_region": clock}
+    dense_part = result_tail.get("parts", {}).get("dense_gemm_4096x7168x7168")
+    if dense_part:
+        roof["frac_flushed_part"] = round(dense_part["frac_mfma"], 4)
     result = {
         "metric": "FP8 block-scaled GEMM TFLOP/s + % FP8 MFMA peak; act-quant GB/s % HBM",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -411,12 +612,10 @@ def main():
         "config": {"workload": "prefill linear: 1x128 act-quant of 4096x7168 bf16 (0.1% outlier "
                                "channels x100) + fp8_block_gemm M=4096 N=7168 K=7168 bf16 out",
                    "M": M, "N": N, "K": K, "weights": "128x128-quantized once before timing",
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "dense_gemm_two_kind_kernel", "achieved": round(achieved, 2),
-                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                     "traffic": traffic_from_counters(),
-                     "gemm_us": round(gemm_ms * 1e3, 2)},
+                   "parallelism": "single GPU",
+                   "preroll": f"CPU baseline, per-kernel parts, then {n_pre} untimed steps "
+                              f"({PREROLL_S} s) before the warm-up steps"},
+        "roofline": roof,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "compute_units": props.multi_processor_count,
                    "memory_bytes": props.total_memory},
@@ -425,12 +624,7 @@ def main():
     }
     if args.copy_calib:
         result["copy_calibration"] = copy_calibration(torch)
-    if not args.no_parts:
-        log("bench: per-kernel parts ...")
-        result["parts"] = measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C)
-    if not args.no_cpu_baseline:
-        log("bench: CPU oracle baseline ...")
-        result["cpu_baseline"] = cpu_baseline(I, X_bits, w_bits)
+    result.update(result_tail)
     print(json.dumps(result), flush=True)
 
 

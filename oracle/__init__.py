@@ -79,6 +79,8 @@ def _load():
         lib.orc_grouped_gemm_rows.restype = None
         lib.orc_max_threads.argtypes = []
         lib.orc_max_threads.restype = ctypes.c_int
+        lib.orc_set_threads.argtypes = [ctypes.c_int]
+        lib.orc_set_threads.restype = None
         _lib = lib
         return lib
 
@@ -97,6 +99,11 @@ def _c(a, dtype):
 def max_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Set the OpenMP thread count of the oracle's parallel loops."""
+    _load().orc_set_threads(int(n))
 
 
 def e4m3_value(code: int) -> float:

@@ -379,3 +379,14 @@ int orc_max_threads(void) {
     return 1;
 #endif
 }
+
+/* Thread count of the OpenMP loops above (the benchmark times the quantizer
+ * single-threaded as well); n <= 0 leaves it unchanged. */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
