@@ -304,11 +304,36 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=None):
                                                                c=C)), fl)
         del pa, psa, pw, psw
 
-    if hasattr(F, "fp8_block_gemm_fused_quant") and want("fused_quant_gemm_4096x7168x7168"):
+    if want("fused_quant_gemm_4096x7168x7168"):
         # bf16 activations quantized inside the GEMM (no E4M3 round trip)
         P.add_flops("fused_quant_gemm_4096x7168x7168",
                     *P.timed(lambda: F.fp8_block_gemm_fused_quant(X, qw, sw, out_dtype="bf16",
                                                                   c=C)), fl)
+    if want("fused_quant_crossover_m4096_k7168"):
+        # The fused GEMM against the two-call path (quantizer, then GEMM),
+        # each timed from a flushed cache, over the output width N: every
+        # 256-column tile re-quantizes its activation rows in the fused
+        # kernel, so it wins only for small N.
+        import numpy as np
+        rows = []
+        for n in (256, 512, 1024, 2048, 4096, 7168):
+            wq, ws = F.fp8_quant_weight_128x128(
+                to_dev_bf16(torch, I.weights(np.random.default_rng(n), (n, K))))
+            cn = torch.empty((M, n), dtype=torch.bfloat16, device="cuda")
+            ms_f, _ = P.timed(lambda: F.fp8_block_gemm_fused_quant(X, wq, ws, out_dtype="bf16",
+                                                                   c=cn))
+
+            def two_call():
+                F.fp8_quant_act_1x128(X, qa, sa)
+                F.fp8_block_gemm(qa, sa, wq, ws, out_dtype="bf16", c=cn)
+            ms_t, _ = P.timed(two_call)
+            rows.append({"N": n, "fused_us": round(ms_f * 1e3, 2),
+                         "two_call_us": round(ms_t * 1e3, 2),
+                         "fused_faster": ms_f < ms_t})
+            del wq, ws, cn
+        P.out["fused_quant_crossover_m4096_k7168"] = {
+            "rows": rows, "note": "M=4096, K=7168, bf16 out; each launch (or pair) after a "
+                                  "512 MB cache flush; median of 50"}
 
     # backward of the same layer: dY [4096][7168] (same distribution as X
     # without outliers); Dgrad = forward GEMM with the transposed weights,

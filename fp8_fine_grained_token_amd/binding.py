@@ -52,6 +52,8 @@ _SIGNATURES = {
     "fp8_transpose_weight_128x128": ([_P, _P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "fp8_block_gemm_wgrad": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P],
                              ctypes.c_int),
+    "fp8_block_gemm_fused_quant": ([_P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, _P,
+                                    _P], ctypes.c_int),
     "fp8_block_gemm_noalloc": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P],
                                ctypes.c_int),
     "fp8_quant_act_1x128_pow2": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
@@ -246,6 +248,42 @@ def fp8_block_gemm(a, sa, w, sw, out_dtype="bf16", c=None, workspace=None, strea
     """C[M][N] = block-scaled product of a [M][K] E4M3 (scales [M][K/128]) and
     w [N][K] E4M3 (scales [N/128][K/128]); bf16 or fp32 output."""
     return _block_gemm("fp8_block_gemm", a, sa, w, sw, out_dtype, c, workspace, stream)
+
+
+def fp8_block_gemm_fused_quant(x, w, sw, out_dtype="bf16", c=None, q_out=None, sa_out=None,
+                               return_quantized=False, stream=None):
+    """C[M][N] = fp8_block_gemm(fp8_quant_act_1x128(x), w, sw) with the 1x128
+    quantization of the bf16 activations x [M][K] done inside the GEMM.
+    With return_quantized (or q_out / sa_out given) the E4M3 bytes [M][K]
+    and scales [M][K/128] are written too and (c, q, sa) is returned."""
+    torch = _torch()
+    _rank(x, "x", 2)
+    _rank(w, "w", 2)
+    M, K = x.shape
+    N = w.shape[0]
+    code, tdt = _out_code(out_dtype)
+    if c is None:
+        c = torch.empty((M, N), dtype=tdt, device=x.device)
+    _shape(w, "w", (N, K))
+    if K % 128 == 0 and N % 128 == 0:
+        _shape(sw, "sw", (N // 128, K // 128))
+    _shape(c, "c", (M, N))
+    want_q = return_quantized or q_out is not None or sa_out is not None
+    if want_q:
+        if q_out is None:
+            q_out = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+        if sa_out is None:
+            sa_out = torch.empty((M, (K + 127) // 128), dtype=torch.float32, device=x.device)
+        _shape(q_out, "q_out", (M, K))
+        _shape(sa_out, "sa_out", (M, (K + 127) // 128))
+        qp, sp = _dev(q_out, "q_out", torch.uint8), _dev(sa_out, "sa_out", torch.float32)
+    else:
+        qp, sp = ctypes.c_void_p(0), ctypes.c_void_p(0)
+    fn = "fp8_block_gemm_fused_quant"
+    _check(getattr(lib(), fn)(_dev(x, "x", torch.bfloat16), _dev(w, "w", torch.uint8),
+                              _dev(sw, "sw", torch.float32), _dev(c, "c", tdt), code, M, N, K,
+                              qp, sp, _stream_handle(stream)), fn)
+    return (c, q_out, sa_out) if want_q else c
 
 
 def fp8_block_gemm_noalloc(a, sa, w, sw, out_dtype="bf16", c=None, stream=None):

@@ -154,6 +154,25 @@ fp8_status fp8_block_gemm(const void *a_e4m3, const float *a_scales, const void 
                       workspace_bytes, false, hip_stream);
 }
 
+fp8_status fp8_block_gemm_fused_quant(const void *x_bf16, const void *w_e4m3,
+                                      const float *w_scales, void *c, int out_dtype, int64_t M,
+                                      int64_t N, int64_t K, void *q_e4m3_out,
+                                      float *a_scales_out, void *hip_stream) {
+    // the activation scales are produced here: pass a valid placeholder for
+    // the common checks (x stands in for a and sa)
+    fp8_status st = check_gemm_common(x_bf16, static_cast<const float *>(x_bf16), w_e4m3,
+                                      w_scales, c, out_dtype, M, N, K, nullptr, 0);
+    if (st != FP8_OK || M == 0 || N == 0) return st;
+    if (K == 0) return FP8_ERR_SHAPE;
+    if ((q_e4m3_out == nullptr) != (a_scales_out == nullptr)) return FP8_ERR_NULL;
+    if (q_e4m3_out && (!aligned(q_e4m3_out, 8) || !aligned(a_scales_out, 4)))
+        return FP8_ERR_ALIGN;
+    clear_last_error();
+    return from_hip(fp8blk::launch_block_gemm_fused_quant(
+        x_bf16, w_e4m3, w_scales, c, out_dtype == FP8_OUT_BF16, M, N, K, q_e4m3_out,
+        a_scales_out, as_stream(hip_stream)));
+}
+
 fp8_status fp8_block_gemm_noalloc(const void *a_e4m3, const float *a_scales,
                                   const void *w_e4m3, const float *w_scales, void *c,
                                   int out_dtype, int64_t M, int64_t N, int64_t K,

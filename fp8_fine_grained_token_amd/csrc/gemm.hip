@@ -89,6 +89,11 @@ struct GemmParams {
     int group_m;             // tile-order grouping height (in M tiles)
     int tn1, tn2;            // two-kind plan: 256-wide and 192-wide N tiles
     int64_t n_split;         // two-kind plan: first column of the 192-wide tiles
+    // quantization fused into the GEMM: bf16 activations in, and optionally
+    // their E4M3 bytes and scales out
+    const uint16_t *x;
+    uint8_t *q_out;
+    float *sa_out;
 };
 
 // SCALE_PIECES: activation scales are staged in chunks of 4 * SCALE_PIECES K
@@ -727,13 +732,13 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 // Final outputs, written once and not read again here, use nontemporal
 // stores; split-K partials (kStream false), read back by the reduction
 // right after, keep the default cache policy.
-template <class C, int OUT, bool kStream = true>
-__device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], TileLds<C> &L,
-                                           void *c, int64_t ldc, int64_t row0, int64_t row_end,
-                                           int64_t n0, int64_t N) {
+template <class C, int OUT, bool kStream, size_t kBufBytes>
+__device__ __forceinline__ void tile_store_buf(const v4f (&acc)[C::kTM][C::kTN], uint8_t *buf,
+                                               void *c, int64_t ldc, int64_t row0,
+                                               int64_t row_end, int64_t n0, int64_t N) {
     constexpr int kOB = OUT == kOutBF16 ? 2 : 4;  // bytes per output element
     constexpr int kRB = C::BN * kOB;              // bytes per tile row
-    constexpr int kFit = (int)(sizeof(L.stages) / kRB) / C::WM * C::WM;
+    constexpr int kFit = (int)(kBufBytes / kRB) / C::WM * C::WM;
     constexpr int kRowsPerPass = kFit < C::BM ? kFit : C::BM;
     static_assert(kRowsPerPass >= C::WM && C::BM % kRowsPerPass == 0, "store passes");
     constexpr int kPieces = kRB / 32;
@@ -751,7 +756,6 @@ __device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], Til
     constexpr int kUnits = kRowsPerPass * kUnitsPerRow;
     static_assert(kUnits % C::kThreads == 0, "store loop");
 
-    uint8_t *buf = reinterpret_cast<uint8_t *>(&L.stages[0]);
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -802,6 +806,16 @@ __device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], Til
             }
         }
     }
+}
+
+// The tile's LDS operand stages are free once the main loop is done and
+// serve as the store buffer.
+template <class C, int OUT, bool kStream = true>
+__device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], TileLds<C> &L,
+                                           void *c, int64_t ldc, int64_t row0, int64_t row_end,
+                                           int64_t n0, int64_t N) {
+    tile_store_buf<C, OUT, kStream, sizeof(L.stages)>(
+        acc, reinterpret_cast<uint8_t *>(&L.stages[0]), c, ldc, row0, row_end, n0, N);
 }
 
 // Tile shapes: 256 x 256 on 8 waves (wave tile 128 x 64, two LDS stages)
@@ -1100,6 +1114,205 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p)
     tile_store<C, OUT>(acc, lds, p.c, p.N, row0, row_end, n0, p.N);
 }
 
+
+// ---- Activation quantization fused into the GEMM ---------------------------
+//
+// The standalone quantizer reads 128 BF16 values per group from HBM, writes
+// the FP8 bytes back, and the GEMM reads them again (page "why-be.co.kr
+// as_center 36949", passage on that round trip and on fusing the FP8 cast
+// with the transfer of activations from global memory).  This kernel takes
+// the bf16 activations itself: each K block's bf16 A tile is copied to LDS,
+// quantized there (the 1x128 rule of the standalone quantizer, with the same
+// arithmetic, so the bytes and scales are identical) into the E4M3 tile the
+// MFMAs read, and the scale goes straight into the promotion.  Optionally
+// the workgroups of the first N tile also write the bytes and scales out.
+//
+// The cost moves from HBM to the VALU: every N tile quantizes its A tile
+// again (N / 256 times in all), and A comes in at 2 bytes per element.  It
+// pays where few N tiles share an A tile; where many do, the standalone
+// quantizer plus the plain GEMM is faster.
+//
+// Tile 32 x 256 on 8 waves (2 x 4, wave tile 16 x 64).  Per K block each
+// wave copies 4 bf16 rows (one 1 KiB copy) and the W tile's 4 rows groups;
+// it quantizes exactly the 4 rows it copied, so the bf16 tile needs no
+// barrier.  Pipeline: W in three stages (copies two blocks ahead), bf16 A in
+// three stages (three blocks ahead, since block kb + 1 is quantized while
+// block kb is multiplied), E4M3 A and its scales double buffered.
+struct FusedCfg {
+    static constexpr int BM = 32, BN = 256;
+    static constexpr int kWavesM = 2, kWavesN = 4, kWaves = 8, kThreads = 512;
+    static constexpr int WM = BM / kWavesM, WN = BN / kWavesN;
+    static constexpr int kTM = WM / 16, kTN = WN / 16;
+    static constexpr int kStagesW = 3, kStagesA = 3;
+    static constexpr int kWLoads = BN / 8 / kWaves;            // 8 rows of 128 B per copy
+    static constexpr int kALoads = BM * 256 / 1024 / kWaves;   // 4 rows of 256 B per copy
+    static constexpr int kCopiesPerBatch = kWLoads + 1 + kALoads;  // + weight scales
+    static_assert(kALoads == 1, "each wave copies the bf16 rows it quantizes");
+    static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns in one weight-scale block");
+};
+
+struct __align__(4096) FusedLds {
+    uint8_t w[FusedCfg::kStagesW][FusedCfg::BN * 128];
+    uint8_t a16[FusedCfg::kStagesA][FusedCfg::BM * 256];
+    uint8_t a8[2][FusedCfg::BM * 128];  // swizzled like Stage::a
+    float sa[2][FusedCfg::BM];
+    float sw[FusedCfg::kStagesW][64];
+};
+
+template <int OUT>
+__global__ __launch_bounds__(FusedCfg::kThreads) void fused_quant_gemm_kernel(GemmParams p) {
+    using C = FusedCfg;
+    __shared__ FusedLds L;
+    const int logical = xcd_logical_tile();
+    if (logical >= p.ntiles) return;
+    int tm, tn;
+    raster(logical, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int64_t K = p.K;
+    const int G = p.G;
+    const int64_t row0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
+    const int64_t ra = p.M - row0 < C::BM ? p.M - row0 : C::BM;
+    const int64_t cw = p.N - n0 < C::BN ? p.N - n0 : C::BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / C::kWavesN, wn = wave % C::kWavesN;
+    const int lr = lane & 15, lk = lane >> 4;
+    const bool write_q = p.q_out != nullptr && tn == 0;
+
+    const v4i rx = make_rsrc(p.x + row0 * K, (uint32_t)(ra * K * 2));
+    const v4i rw = make_rsrc(p.w + n0 * K, (uint32_t)(cw * K));
+    const int64_t nb0 = n0 >> 7, nbs = ((n0 + cw - 1) >> 7) - nb0 + 1;
+    const v4i rsw = make_rsrc(p.sw + nb0 * G, (uint32_t)(nbs * G * 4));
+    v4i rx0 = rx, rw0 = rw, rsw0 = rsw;  // empty views for blocks past the end
+    rx0[2] = rw0[2] = rsw0[2] = 0;
+
+    // W copy t of wave v fills W-stage rows 8 (v + 8 t) .. + 8 (as in
+    // tile_mainloop: lane L -> physical chunk L % 8 of row L / 8, holding
+    // logical chunk (L % 8) ^ key(row)).
+    const uint32_t w_voff = (uint32_t)(8 * wave * K + (lane >> 3) * K +
+                                       (((lane & 7) ^ ((lane >> 3) & 7) ^ (wave & 1)) << 4));
+    const uint32_t w_rowstep = (uint32_t)(64 * K);
+    // bf16 copy of wave v: rows 4 v + L / 16, 16-byte chunk L % 16.
+    const uint32_t a_voff = (uint32_t)((4 * wave + (lane >> 4)) * 2 * K + (lane & 15) * 16);
+    const uint32_t lds_w0 = lds_addr(&L.w[0][1024 * wave]);
+    const uint32_t lds_a0 = lds_addr(&L.a16[0][1024 * wave]);
+    const uint32_t lds_sw0 = lds_addr(&L.sw[0][0]);
+    const uint32_t sw_voff = (uint32_t)(lane * G * 4);
+
+    // one batch: W and weight scales of block kw, bf16 A of block ka
+    auto issue_batch = [&](int kw, int ka) {
+        const bool win = kw < G, ain = ka < G;
+        const v4i &w_r = win ? rw : rw0;
+        const v4i &s_r = win ? rsw : rsw0;
+        const v4i &a_r = ain ? rx : rx0;
+        const int kwc = win ? kw : 0, kac = ain ? ka : 0;
+        const uint32_t sw_st = (uint32_t)((kw % C::kStagesW) * sizeof(L.w[0]));
+#pragma unroll
+        for (int t = 0; t < C::kWLoads; ++t)
+            copy16_nt(w_r, w_voff + t * w_rowstep, (uint32_t)kwc * 128u,
+                      lds_w0 + sw_st + 1024u * C::kWaves * t);
+        copy4(s_r, sw_voff, (uint32_t)kwc * 4u,
+              lds_sw0 + (uint32_t)((kw % C::kStagesW) * sizeof(L.sw[0])));
+        copy16(a_r, a_voff, (uint32_t)kac * 256u,
+               lds_a0 + (uint32_t)((ka % C::kStagesA) * sizeof(L.a16[0])));
+    };
+
+    // Quantize block kb from its bf16 stage (this wave's 4 rows) into E4M3
+    // buffer kb % 2 and its scales; rows past M quantize to zero bytes.
+    auto quant = [&](int kb) {
+        const int r = 4 * wave + (lane >> 4), j = lane & 15;
+        const bool in = row0 + r < p.M;
+        const uint4 v = *reinterpret_cast<const uint4 *>(
+            &L.a16[kb % C::kStagesA][r * 256 + j * 16]);
+        float f[8];
+        unpack8(v, f);
+        const float amax = row16_max(absmax8(f));
+        float y[8], s;
+        if (__all(!in || amax >= 0x1p-60f)) {
+            s = in ? scale_fast(amax) : 1.0f;
+            const float rc = 1.0f / s;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[i] = quot_fast(f[i], s, rc);
+        } else {
+            const QuotientCtx qc(amax, false);
+            s = qc.s;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[i] = qc(f[i]);
+        }
+        if (!in) s = 0.0f;
+        uint32_t lo = 0, hi = 0;
+        lo = cvt_pk_e4m3<false>(y[0], y[1], lo);
+        lo = cvt_pk_e4m3<true>(y[2], y[3], lo);
+        hi = cvt_pk_e4m3<false>(y[4], y[5], hi);
+        hi = cvt_pk_e4m3<true>(y[6], y[7], hi);
+        const int chunk = (j >> 1) ^ swz_key(r);
+        *reinterpret_cast<uint2 *>(&L.a8[kb & 1][r * 128 + chunk * 16 + (j & 1) * 8]) =
+            make_uint2(lo, hi);
+        if (j == 0) L.sa[kb & 1][r] = s;
+        if (write_q && in) {
+            *reinterpret_cast<uint2 *>(p.q_out + (row0 + r) * K + (int64_t)kb * 128 + 8 * j) =
+                make_uint2(lo, hi);
+            if (j == 0) p.sa_out[(row0 + r) * G + kb] = s;
+        }
+    };
+
+    const int frag0 = lr * 128 + (((2 * lk) ^ swz_key(lr)) << 4);
+    const int frag1 = lr * 128 + (((2 * lk + 1) ^ swz_key(lr)) << 4);
+    const int col_off = (int)(n0 & 127) + wn * C::WN;
+    v4f acc[C::kTM][C::kTN];
+#pragma unroll
+    for (int i = 0; i < C::kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Block kb: W stage kb % 3, E4M3 A buffer kb % 2.  The MFMA takes the
+    // weight fragment as its A operand, so lane L holds outputs n = 4 (L /
+    // 16) + e, m = L % 16 of each 16 x 16 tile (see tile_mainloop).
+    auto compute = [&](int kb) {
+        const uint8_t *lw = L.w[kb % C::kStagesW] + wn * C::WN * 128;
+        const uint8_t *la = L.a8[kb & 1] + wm * C::WM * 128;
+        v8i wfr[C::kTN];
+#pragma unroll
+        for (int j = 0; j < C::kTN; ++j)
+            wfr[j] = make_v8i(*reinterpret_cast<const uint4 *>(lw + j * 2048 + frag0),
+                              *reinterpret_cast<const uint4 *>(lw + j * 2048 + frag1));
+        const float swv = L.sw[kb % C::kStagesW][col_off >> 7];
+#pragma unroll
+        for (int i = 0; i < C::kTM; ++i) {
+            const v8i af = make_v8i(*reinterpret_cast<const uint4 *>(la + i * 2048 + frag0),
+                                    *reinterpret_cast<const uint4 *>(la + i * 2048 + frag1));
+            const float f = L.sa[kb & 1][wm * C::WM + 16 * i + lr] * swv;
+            v4f pr[C::kTN];
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j) pr[j] = mfma_e4m3(wfr[j], af);
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(pr[j][e], f, acc[i][j][e]);
+        }
+    };
+
+    // Prologue: block 0's bf16 rows, quantized by each wave (its own rows:
+    // no barrier), then batches for W blocks 0, 1 and bf16 blocks 1, 2.
+    copy16(G > 0 ? rx : rx0, a_voff, 0u, lds_a0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    quant(0);
+    issue_batch(0, 1);
+    issue_batch(1, 2);
+    for (int kb = 0; kb < G; ++kb) {
+        // batch kb - 2 (W block kb, bf16 block kb + 1) has landed; batch
+        // kb - 1 may still be in flight
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::kCopiesPerBatch) : "memory");
+        __syncthreads();
+        // W stage (kb + 2) % 3 was last read by block kb - 1 (every wave is
+        // past it); bf16 stage (kb + 3) % 3 holds block kb, quantized in the
+        // previous iteration by the wave that copies into it
+        issue_batch(kb + 2, kb + 3);
+        compute(kb);
+        if (kb + 1 < G) quant(kb + 1);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    tile_store_buf<C, OUT, true, sizeof(L.w)>(acc, &L.w[0][0], p.c, p.N, row0, p.M, n0, p.N);
+}
+
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 constexpr int kCUs = 256;
@@ -1389,4 +1602,35 @@ hipError_t launch_grouped_gemm(const void *a, const float *sa, const void *w, co
     return hipGetLastError();
 }
 
+hipError_t launch_block_gemm_fused_quant(const void *x, const void *w, const float *sw, void *c,
+                                         bool bf16_out, int64_t M, int64_t N, int64_t K,
+                                         void *q_out, float *sa_out, hipStream_t stream) {
+    using C = FusedCfg;
+    GemmParams p{};
+    p.x = static_cast<const uint16_t *>(x);
+    p.w = static_cast<const uint8_t *>(w);
+    p.sw = sw;
+    p.c = c;
+    p.q_out = static_cast<uint8_t *>(q_out);
+    p.sa_out = sa_out;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.G = (int)(K / 128);
+    p.NB = (int)(N / 128);
+    p.tiles_m = (int)((M + C::BM - 1) / C::BM);
+    p.tiles_n = (int)((N + C::BN - 1) / C::BN);
+    p.ntiles = p.tiles_m * p.tiles_n;
+    p.group_m = 8;
+    const dim3 grid(round_up(p.ntiles, kNumXcd));
+    if (bf16_out)
+        hipLaunchKernelGGL(fused_quant_gemm_kernel<kOutBF16>, grid, dim3(C::kThreads), 0, stream,
+                           p);
+    else
+        hipLaunchKernelGGL(fused_quant_gemm_kernel<kOutF32>, grid, dim3(C::kThreads), 0, stream,
+                           p);
+    return hipGetLastError();
+}
+
 }  // namespace fp8blk
+

@@ -48,6 +48,13 @@ hipError_t launch_block_gemm_noalloc(const void *a, const float *sa, const void 
                                      const float *sw, void *c, bool bf16_out, int64_t M,
                                      int64_t N, int64_t K, hipStream_t stream);
 
+// The block-scaled GEMM on bf16 activations x [M][K], quantized 1x128 inside
+// the GEMM; q_out / sa_out (both or neither) receive the E4M3 bytes and
+// scales the standalone quantizer would write.
+hipError_t launch_block_gemm_fused_quant(const void *x, const void *w, const float *sw, void *c,
+                                         bool bf16_out, int64_t M, int64_t N, int64_t K,
+                                         void *q_out, float *sa_out, hipStream_t stream);
+
 hipError_t launch_grouped_gemm(const void *a, const float *sa, const void *w, const float *sw,
                                const int32_t *offsets, int64_t E, int64_t T, void *c,
                                bool bf16_out, int64_t N, int64_t K, bool pow2,

@@ -144,6 +144,33 @@ fp8_status fp8_block_grouped_gemm(const void *a_e4m3, const float *a_scales,
                                   size_t workspace_bytes, void *hip_stream);
 
 /*
+ * fp8_block_gemm on bf16 activations, with their 1x128 quantization fused
+ * into the GEMM (page "why-be.co.kr as_center 36949", passages on the
+ * quantization round trip through HBM, 128 BF16 values read and FP8 written
+ * back to be read again, and on fusing the FP8 cast with the transfer of
+ * activations from global memory):
+ *   C = fp8_block_gemm(q, s, w_e4m3, w_scales) with (q, s) =
+ *       fp8_quant_act_1x128(x_bf16), without q and s passing through memory.
+ *   x_bf16        [M][K] bf16, 16-byte aligned
+ *   w_e4m3, w_scales, c, out_dtype, M, N, K: as fp8_block_gemm
+ *   q_e4m3_out    [M][K] E4M3 (8-byte aligned) and a_scales_out [M][K/128]
+ *                 fp32: optional outputs (both NULL, or both given), which
+ *                 receive exactly what fp8_quant_act_1x128 writes, e.g. to
+ *                 keep the FP8 activations for the backward pass.
+ * The quantized values, the products and the accumulation are those of the
+ * two-call path, so C is the same up to the FP32 summation order.  Every
+ * 256-column tile of C quantizes its activation rows again, so this call is
+ * the faster one only for small N (see the measured crossover in the
+ * documentation); it uses no workspace.  Errors: as fp8_block_gemm, plus
+ * FP8_ERR_NULL when only one of q_e4m3_out / a_scales_out is given, and
+ * FP8_ERR_ALIGN for x_bf16 not 16-byte or q_e4m3_out not 8-byte aligned.
+ */
+fp8_status fp8_block_gemm_fused_quant(const void *x_bf16, const void *w_e4m3,
+                                      const float *w_scales, void *c, int out_dtype,
+                                      int64_t M, int64_t N, int64_t K, void *q_e4m3_out,
+                                      float *a_scales_out, void *hip_stream);
+
+/*
  * Power-of-two-scale variants for the block-scaled matrix core (page
  * "kailasan.com recruit 147436", passage recommending that matrix units take
  * the per-group scaling factors and do the group-scaled MMA themselves; on

@@ -96,7 +96,13 @@ def gemm_error_bound(qa, sa, qw, sw, rows=None, row_scaled_w=False, splits=1) ->
     and with split-K the partial sums are added once more per split.  Each
     rounding is bounded by U32 times the sum of |scaled products| S.
     W scales: [N/128][G] per 128-row block, or [N][G] per row (row_scaled_w,
-    the Wgrad operands)."""
+    the Wgrad operands).
+
+    The FP32 product of the two scales can underflow: its absolute error is
+    at most 2^-150 (half the smallest subnormal), times the block's sum of
+    |code products| P (this matters only where a group's amax is itself
+    near the bottom of the FP32 range, e.g. a subnormal bf16 amax, whose
+    outputs then flush toward zero)."""
     if rows is None:
         rows = np.arange(qa.shape[0])
     K = qa.shape[1]
@@ -106,7 +112,10 @@ def gemm_error_bound(qa, sa, qw, sw, rows=None, row_scaled_w=False, splits=1) ->
     w_abs, w_max8 = _scaled_abs(qw, sw_rows)
     S = a_abs @ w_abs.T
     T = a_max8 @ w_max8.T
-    return 1.01 * (7.0 * 2.0 ** -13 * T + (16 + G + 2 + splits) * U32 * S) + (G + 20) * 2.0 ** -149
+    lut = e4m3_lut()
+    P = np.abs(lut[qa[rows]]) @ np.abs(lut[qw]).T
+    return (1.01 * (7.0 * 2.0 ** -13 * T + (16 + G + 2 + splits) * U32 * S + 2.0 ** -150 * P)
+            + (G + 20) * 2.0 ** -149)
 
 
 def grouped_error_bound(qa, sa, qw, sw, offsets, rows) -> np.ndarray:

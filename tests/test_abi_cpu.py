@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         method + [m + "_pow2" for m in method]
         + ["fp8_quant_act_128x1_t", "fp8_transpose_weight_128x128", "fp8_block_gemm_wgrad"]
-        + ["fp8_gemm_workspace_bytes", "fp8_status_string", "fp8_block_gemm_noalloc"])
+        + ["fp8_gemm_workspace_bytes", "fp8_status_string", "fp8_block_gemm_noalloc",
+           "fp8_block_gemm_fused_quant"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -134,6 +135,28 @@ def test_grouped_argument_errors(suffix):
     assert grouped_(lib, ws=A16, wsb=0) == B.FP8_ERR_WORKSPACE
     # T = 0 is a no-op (E = 0 allowed then)
     assert grouped_(lib, T=0, E=0, a=NUL, sa=NUL, off=NUL, c=NUL) == B.FP8_OK
+
+
+def test_fused_quant_gemm_argument_errors():
+    lib = B.lib()
+
+    def fq(x=A16, w=A16, sw=A16, c=A16, dt=B.FP8_OUT_BF16, M=128, N=256, K=512, q=NUL, s=NUL):
+        return lib.fp8_block_gemm_fused_quant(x, w, sw, c, dt, M, N, K, q, s, NUL)
+    assert fq(K=500) == B.FP8_ERR_SHAPE
+    assert fq(N=200) == B.FP8_ERR_SHAPE
+    assert fq(M=-1) == B.FP8_ERR_SHAPE
+    assert fq(K=1 << 24) == B.FP8_ERR_SHAPE
+    assert fq(dt=7) == B.FP8_ERR_DTYPE
+    assert fq(x=NUL) == B.FP8_ERR_NULL
+    assert fq(sw=NUL) == B.FP8_ERR_NULL
+    assert fq(q=A16) == B.FP8_ERR_NULL           # bytes out without scales out
+    assert fq(s=A16) == B.FP8_ERR_NULL
+    assert fq(x=A8) == B.FP8_ERR_ALIGN
+    assert fq(c=A8) == B.FP8_ERR_ALIGN
+    assert fq(q=ctypes.c_void_p(0x10004), s=A16) == B.FP8_ERR_ALIGN
+    assert fq(q=A8, s=ctypes.c_void_p(0x10002)) == B.FP8_ERR_ALIGN
+    assert fq(K=0) == B.FP8_ERR_SHAPE
+    assert fq(M=0, x=NUL, c=NUL) == B.FP8_OK
 
 
 def test_noalloc_gemm_argument_errors():

@@ -106,3 +106,21 @@ def test_row_scaled_bound_matches_block_scaled_when_rows_share_scales():
     b1 = gemm_error_bound(qa, sa, qw, sw)
     b2 = gemm_error_bound(qa, sa, qw, np.repeat(sw, 128, axis=0), row_scaled_w=True)
     assert np.array_equal(b1, b2)
+
+
+def test_underflowing_scale_product_is_inside_the_bound():
+    # a row whose groups have amax near the bottom of the FP32 range: its
+    # scale times the weight scale underflows in FP32 (the emulation flushes
+    # those outputs toward zero), which the bound's 2^-150 term covers
+    g = I.gemm_inputs(8, 256, 384, seed=4)
+    a = g.a_bf16.copy()
+    a[0] = I.f32_to_bf16_bits(I.bf16_bits_to_f32(a[0]) * np.float32(2.0 ** -125))
+    a[1, :] = 0
+    a[1, 7] = 0x0001                                   # smallest subnormal bf16
+    qa, sa = oracle.quant_act_1x128(a)
+    qw, sw = oracle.quant_weight_128x128(g.w_bf16)
+    R = oracle.block_gemm(qa, sa, qw, sw)
+    C = emulate(qa, sa, qw, sw)
+    b = gemm_error_bound(qa, sa, qw, sw)
+    assert np.all(np.abs(C - R) <= b)
+    assert np.any((C[:2] == 0) & (R[:2] != 0)), "no output underflowed"

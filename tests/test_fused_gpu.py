@@ -1,0 +1,125 @@
+"""GPU parity of the GEMM with the 1x128 activation quantization fused in
+(fp8_block_gemm_fused_quant), through the C ABI.
+
+The fused kernel quantizes the bf16 activations itself (page "why-be.co.kr
+as_center 36949", passages on the quantization round trip and on fusing the
+FP8 cast with the transfer of activations), so:
+  - its optional E4M3 bytes and scales must equal the oracle's 1x128
+    quantizer bit for bit;
+  - C must meet the per-output bound against the oracle's binary64 GEMM of
+    the oracle's own quantized activations;
+  - with FP32 output C equals the two-call path (GPU quantizer, then the
+    plain GEMM) bit for bit: the same bytes, scales, block products and
+    promotion order per output.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fp8_fine_grained_token_amd import binding as B
+from fp8_fine_grained_token_amd import inputs as I
+
+from .gpu_util import check_gemm, dev, dev_bf16, gemm_error_bound, host, log, tile_rows, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = torch()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    yield
+    t.cuda.synchronize()
+
+
+def assert_bytes_and_scales(qg, sg, qo, so, what):
+    nbad = int((qg != qo).sum())
+    sbad = int((sg.view(np.uint32) != so.view(np.uint32)).sum())
+    log(f"  {what}: byte mismatches={nbad} scale mismatches={sbad}")
+    assert nbad == 0 and sbad == 0
+
+
+def run_case(a_bits, w_bits, out, rows=None, what=""):
+    qw, sw = oracle.quant_weight_128x128(w_bits)
+    qa, sa = oracle.quant_act_1x128(a_bits)
+    x = dev_bf16(a_bits)
+    c, q, s = B.fp8_block_gemm_fused_quant(x, dev(qw), dev(sw), out_dtype=out,
+                                           return_quantized=True)
+    assert_bytes_and_scales(host(q), host(s), qa, sa, f"{what} quantized activations")
+    if rows is None:
+        rows = np.arange(a_bits.shape[0])
+    R = oracle.block_gemm(qa, sa, qw, sw, rows)
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, out, f"fused {what} {out}",
+               gemm_error_bound(qa, sa, qw, sw, rows))
+    return c, x, qw, sw
+
+
+@pytest.mark.parametrize("M", [1, 17, 33, 300])
+@pytest.mark.parametrize("N,K", [(128, 128), (256, 640), (384, 1280)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_fused_ragged(M, N, K, out):
+    # ragged M (partial 32-row tiles), N of one, one or two 256-column tiles
+    # (384: the second tile half full), K of 1, 5 and 10 blocks
+    g = I.gemm_inputs(M, N, K, seed=M * 7 + N + K, outlier_frac=0.01, outlier_mult=50.0)
+    run_case(g.a_bf16, g.w_bf16, out, what=f"{M}x{N}x{K}")
+
+
+def test_fused_special_groups():
+    # all -0, a subnormal amax, the largest bf16, an all-zero group: these
+    # take the general per-group quotient inside the fused kernel.  The
+    # largest bf16 stands in two elements of one group only, so that the
+    # row's products stay inside the FP32 range of the output.
+    K = 512
+    x = np.zeros((40, K), np.uint16)
+    x[1, :] = 0x8000
+    x[2, 5] = 0x0001
+    x[2, 130] = 0x8001
+    x[3, :128] = I.f32_to_bf16_bits(np.linspace(-1, 1, 128, dtype=np.float32))
+    x[4, 130], x[4, 131] = 0x7F7F, 0xFF7F
+    x[5, 256:384] = I.f32_to_bf16_bits(np.float32(448.0 * 2.0 ** -130) * np.ones(128, np.float32))
+    x[6:, :], _ = I.activations(np.random.default_rng(6), 34, K, 0.01, 50.0)
+    w = I.weights(np.random.default_rng(7), (256, K))
+    run_case(x, w, "f32", what="special groups")
+
+
+def test_fused_equals_two_call_path_fp32():
+    # the GPU quantizer then the plain GEMM, against the fused kernel: FP32
+    # outputs bitwise equal, bytes and scales too
+    g = I.gemm_inputs(300, 512, 2304, seed=5, outlier_frac=0.01, outlier_mult=50.0)
+    t = torch()
+    x = dev_bf16(g.a_bf16)
+    qw, sw = B.fp8_quant_weight_128x128(dev_bf16(g.w_bf16))
+    qa, sa = B.fp8_quant_act_1x128(x)
+    c2 = B.fp8_block_gemm(qa, sa, qw, sw, out_dtype="f32")
+    c1, q1, s1 = B.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype="f32", return_quantized=True)
+    t.cuda.synchronize()
+    assert t.equal(q1, qa) and t.equal(s1.view(t.int32), sa.view(t.int32))
+    d = (c1 - c2).abs().max().item()
+    log(f"  fused vs two-call FP32: max |diff| = {d:.3e}")
+    assert t.equal(c1, c2)
+
+
+@pytest.mark.parametrize("N", [256, 7168])
+def test_fused_workload_shapes(N):
+    # M = 4096, K = 7168: N = 256 (one N tile: every activation tile is
+    # quantized once, e.g. a router's 256 experts) and the dense layer's
+    # N = 7168; the quantized activations in full, C on rows of every
+    # 32-row tile, all columns
+    M, K = 4096, 7168
+    x_bits, _ = I.config_quant(seed=0)
+    w_bits = I.weights(np.random.default_rng(N), (N, K))
+    rows = tile_rows(M, 32, per_tile=1)
+    log(f"  fused {M}x{N}x{K}: oracle on {rows.size} rows ...")
+    run_case(x_bits, w_bits, "bf16", rows=rows, what=f"{M}x{N}x{K}")
+
+
+def test_fused_without_quantized_outputs_and_repeatable():
+    g = I.gemm_inputs(64, 256, 1024, seed=9)
+    t = torch()
+    x = dev_bf16(g.a_bf16)
+    qw, sw = B.fp8_quant_weight_128x128(dev_bf16(g.w_bf16))
+    c0 = B.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype="f32")
+    c1, _, _ = B.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype="f32", return_quantized=True)
+    assert t.equal(c0, c1)
