@@ -339,7 +339,8 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=None):
     # without outliers); Dgrad = forward GEMM with the transposed weights,
     # Wgrad = dY^T X from 128x1 tiles
     bwd = [n for n in ("bwd_quant_128x1_t_4096x7168", "bwd_transpose_weight_7168x7168",
-                       "bwd_dgrad_4096x7168x7168", "bwd_wgrad_7168x7168_over_4096") if want(n)]
+                       "bwd_dgrad_4096x7168x7168", "bwd_dgrad_transposed_reads_4096x7168x7168",
+                       "bwd_wgrad_7168x7168_over_4096") if want(n)]
     if bwd:
         dy = to_dev_bf16(torch, I.activations(np.random.default_rng(7), M, N, 0.0, 1.0)[0])
         if want("bwd_quant_128x1_t_4096x7168"):
@@ -356,6 +357,14 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=None):
             P.add_flops("bwd_dgrad_4096x7168x7168",
                         *P.timed(lambda: F.fp8_block_gemm(qdy, sdy, qwt, swt, out_dtype="bf16",
                                                           c=dx)), fl)
+            del dx
+        if want("bwd_dgrad_transposed_reads_4096x7168x7168"):
+            # Dgrad on the forward weights, read transposed inside the GEMM
+            # (no weight transpose)
+            dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+            P.add_flops("bwd_dgrad_transposed_reads_4096x7168x7168",
+                        *P.timed(lambda: F.fp8_block_gemm_dgrad(qdy, sdy, qw, sw,
+                                                                out_dtype="bf16", dx=dx)), fl)
             del dx
         if want("bwd_wgrad_7168x7168_over_4096"):
             qdy_t, sdy_t = F.fp8_quant_act_128x1_t(dy)

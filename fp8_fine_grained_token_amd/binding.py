@@ -52,6 +52,8 @@ _SIGNATURES = {
     "fp8_transpose_weight_128x128": ([_P, _P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "fp8_block_gemm_wgrad": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P],
                              ctypes.c_int),
+    "fp8_block_gemm_dgrad": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P,
+                              ctypes.c_size_t, _P], ctypes.c_int),
     "fp8_block_gemm_fused_quant": ([_P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, _P,
                                     _P], ctypes.c_int),
     "fp8_block_gemm_noalloc": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P],
@@ -248,6 +250,33 @@ def fp8_block_gemm(a, sa, w, sw, out_dtype="bf16", c=None, workspace=None, strea
     """C[M][N] = block-scaled product of a [M][K] E4M3 (scales [M][K/128]) and
     w [N][K] E4M3 (scales [N/128][K/128]); bf16 or fp32 output."""
     return _block_gemm("fp8_block_gemm", a, sa, w, sw, out_dtype, c, workspace, stream)
+
+
+def fp8_block_gemm_dgrad(dy, sdy, w, sw, out_dtype="bf16", dx=None, workspace=None,
+                         stream=None):
+    """dX [M][K] = dY [M][N] W [N][K]: dy E4M3 [M][N] with scales [M][N/128]
+    (1x128 along N), w the forward weights E4M3 [N][K] with 128x128 block
+    scales [N/128][K/128], read transposed inside the GEMM."""
+    torch = _torch()
+    _rank(dy, "dy", 2)
+    _rank(w, "w", 2)
+    M, N = dy.shape
+    K = w.shape[1]
+    code, tdt = _out_code(out_dtype)
+    if dx is None:
+        dx = torch.empty((M, K), dtype=tdt, device=dy.device)
+    _shape(w, "w", (N, K))
+    if K % 128 == 0 and N % 128 == 0:
+        _shape(sdy, "sdy", (M, N // 128))
+        _shape(sw, "sw", (N // 128, K // 128))
+    _shape(dx, "dx", (M, K))
+    wp, wb = _workspace_args(workspace)
+    fn = "fp8_block_gemm_dgrad"
+    _check(getattr(lib(), fn)(_dev(dy, "dy", torch.uint8), _dev(sdy, "sdy", torch.float32),
+                              _dev(w, "w", torch.uint8), _dev(sw, "sw", torch.float32),
+                              _dev(dx, "dx", tdt), code, M, N, K, wp, wb, _stream_handle(stream)),
+           fn)
+    return dx
 
 
 def fp8_block_gemm_fused_quant(x, w, sw, out_dtype="bf16", c=None, q_out=None, sa_out=None,

@@ -94,6 +94,9 @@ struct GemmParams {
     const uint16_t *x;
     uint8_t *q_out;
     float *sa_out;
+    // transposed weights (Dgrad): W is [K][N] (row length ldw = N bytes) and
+    // its block scales [K/128][N/128]; the tiles read it transposed
+    int64_t ldw;
 };
 
 // SCALE_PIECES: activation scales are staged in chunks of 4 * SCALE_PIECES K
@@ -274,6 +277,10 @@ __device__ __forceinline__ void copy4(const v4i &r, uint32_t voff, uint32_t soff
 // other row read as zero, so ragged edges need no clamping.
 struct TileOperands {
     v4i a, w, sa, sw, swr;  // swr: W row scales (row-scaled W only)
+    // weight-scale fetch: lane L of the per-block copy reads byte offset
+    // L sw_lstride + kb sw_kstride of the sw view
+    uint32_t sw_lstride, sw_kstride;
+    uint32_t ldw;           // transposed W only: bytes per row of W [K][N]
 };
 
 template <class C>
@@ -298,7 +305,67 @@ __device__ __forceinline__ TileOperands tile_operands(const uint8_t *a, const fl
         t.sw = make_rsrc(sw + nb0 * G, (uint32_t)(nbs * G * 4));
         t.swr = make_rsrc(sw, 0);
     }
+    t.sw_lstride = (uint32_t)G * 4u;
+    t.sw_kstride = 4u;
+    t.ldw = 0;
     return t;
+}
+
+// Operands of a tile whose weights are stored transposed, W [K][N] with
+// block scales [K/128][N/128] (the forward layer's weights, read for Dgrad):
+// the tile's columns n0 .. n0 + cols of every row of W.  Columns past N read
+// whatever follows in memory (other rows' bytes; zero past the end of W) and
+// feed only outputs that are not stored.
+template <class C>
+__device__ __forceinline__ TileOperands tile_operands_transw(const uint8_t *a, const float *sa,
+                                                             const uint8_t *w, const float *sw,
+                                                             int64_t row0, int64_t rows,
+                                                             int64_t n0, int64_t cols, int64_t K,
+                                                             int G, int64_t ldw, int NB) {
+    TileOperands t;
+    const int64_t ra = rows < C::BM ? rows : C::BM;
+    const int64_t cw = cols < C::BN ? cols : C::BN;
+    t.a = make_rsrc(a + row0 * K, (uint32_t)(ra * K));
+    t.sa = make_rsrc(sa + row0 * G, (uint32_t)(ra * G * 4));
+    t.w = make_rsrc(w + n0, (uint32_t)(K * ldw - n0));
+    const int64_t nb0 = n0 >> 7, nbs = ((n0 + cw - 1) >> 7) - nb0 + 1;
+    // Lane L of the per-block copy reads sw[kb][nb0 + L] at offset 4 L +
+    // kb NB 4 (soffset): the buffer range check covers voffset + soffset,
+    // so the range runs to the end of the scales (lanes past the tile's
+    // blocks read other blocks' scales into LDS words nobody uses; past the
+    // end they read zero).
+    t.sw = make_rsrc(sw + nb0, (uint32_t)(((int64_t)(G - 1) * NB + nbs) * 4));
+    t.swr = make_rsrc(sw, 0);
+    t.sw_lstride = 4u;
+    t.sw_kstride = (uint32_t)NB * 4u;
+    t.ldw = (uint32_t)ldw;
+    return t;
+}
+
+// LDS layout of a transposed W tile: 128 rows (the K block) of BN bytes (the
+// tile's columns); logical 16-byte chunk c of row r sits at physical chunk
+// tw_phys(c, tw_key(r)): c ^ key for a power-of-two chunk count, else
+// (c + key) mod chunks.  The transposed reads (ds_read_b64_tr_b8) of one
+// instruction touch rows 32 lk + 8 q + (0..7) of four lane groups lk at one
+// chunk; with this key the 16 rows of each half wave land on 16 distinct
+// chunks for BN = 256 (256 B, every bank once; two rows per chunk for the
+// 12 chunks of BN = 192).
+__device__ __forceinline__ int tw_key(int r) { return (r & 7) | (((r >> 5) & 1) << 3); }
+template <int BN>
+__device__ __forceinline__ int tw_phys(int c, int key) {
+    constexpr int n = BN / 16;
+    if constexpr ((n & (n - 1)) == 0)
+        return (c ^ key) & (n - 1);
+    else
+        return (c + key) % n;
+}
+template <int BN>
+__device__ __forceinline__ int tw_logical(int p, int key) {
+    constexpr int n = BN / 16;
+    if constexpr ((n & (n - 1)) == 0)
+        return (p ^ key) & (n - 1);
+    else
+        return (p - key % n + n) % n;
 }
 
 // Runs K blocks [kb0, kb1) of one BM x BN tile and leaves the FP32
@@ -327,7 +394,15 @@ __device__ __forceinline__ TileOperands tile_operands(const uint8_t *a, const fl
 // kPow2: the scales are powers of two.  Each MFMA then takes their E8M0 codes
 // and accumulates into the FP32 accumulators itself (acc + sa sw P_kb in one
 // instruction), so there is no promotion FMA.
-template <class C, bool kPow2 = false>
+//
+// kTransW: W is stored transposed (see tile_operands_transw).  Its tile is
+// copied as 128 rows of BN bytes and each MFMA weight fragment is read with
+// four transposed LDS reads (ds_read_b64_tr_b8): in each 16-lane group,
+// result byte b of lane i is byte i % 8 of the 8 bytes at the address of
+// lane 2 b + i / 8, so lane s pointing at row 8 q + s / 2, bytes 8 (s % 2)
+// .. + 8 of the fragment's 16 columns gives lane i the 8 K values 8 q ..
+// 8 q + 7 of column i.
+template <class C, bool kPow2 = false, bool kTransW = false>
 __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K, int G, int kb0,
                                               int kb1, int col_off,
                                               TileLds<C> &L,
@@ -355,22 +430,43 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     const uint32_t wave_voff = (uint32_t)(8 * wave * K) + copy_voff;
     // Scale chunk copy t of wave v fills float4 slots q = 64 (v + kWaves t) + L
     // of a chunk buffer: piece h = q / BM of row r = q % BM.
-    uint32_t sa_voff[C::kScaleLoads];
-#pragma unroll
-    for (int t = 0; t < C::kScaleLoads; ++t) {
-        const int q = 64 * (wave + C::kWaves * t) + lane;
-        sa_voff[t] = (uint32_t)((q % C::BM) * G * 4 + (q / C::BM) * 16);
-    }
+    // Offsets of the rarely issued scale copies are computed at each copy
+    // from the lane index passed through an empty asm statement, so that
+    // they do not occupy registers across the main loop.
+    auto opaque_lane = [&] {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        return ln;
+    };
+    auto sa_voff = [&](int t) {
+        const int q = 64 * (wave + C::kWaves * t) + opaque_lane();
+        return (uint32_t)((q % C::BM) * G * 4 + (q / C::BM) * 16);
+    };
     // Row-scaled W: W chunk copy t of wave v fills float4 slots q = 64 (v +
     // kWaves t) + L of a W chunk buffer, piece q / BN of W row q % BN.
-    uint32_t swr_voff[C::kScaleLoadsW > 0 ? C::kScaleLoadsW : 1];
-#pragma unroll
-    for (int t = 0; t < C::kScaleLoadsW; ++t) {
-        const int q = 64 * (wave + C::kWaves * t) + lane;
-        swr_voff[t] = (uint32_t)((q % C::BN) * G * 4 + (q / C::BN) * 16);
-    }
-    const uint32_t sw_voff = (uint32_t)(lane * G * 4);
+    auto swr_voff = [&](int t) {
+        const int q = 64 * (wave + C::kWaves * t) + opaque_lane();
+        return (uint32_t)((q % C::BN) * G * 4 + (q / C::BN) * 16);
+    };
+    const uint32_t sw_voff = (uint32_t)lane * op.sw_lstride;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // for uniform branches
+    // Transposed W: copy t of wave v fills bytes 1024 (v + kWaves t) .. +
+    // 1024 of the stage's W tile (rows of BN bytes); lane L's 16 bytes at
+    // tile offset pos = 1024 (v + kWaves t) + 16 L are row pos / BN,
+    // physical chunk (pos % BN) / 16, which holds the logical chunk
+    // tw_logical of it.
+    static_assert(!kTransW || C::BN * 128 == C::kBLoads * C::kWaves * 1024,
+                  "transposed W copies");
+    // (computed at each copy from the lane index passed through an empty asm
+    // statement, so these offsets do not occupy registers across the loop)
+    auto wt_voff = [&](int t) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int pos = 1024 * (wave + C::kWaves * t) + 16 * ln;
+        const int r = pos / C::BN;
+        const int c = tw_logical<C::BN>((pos % C::BN) >> 4, tw_key(r));
+        return (uint32_t)r * op.ldw + 16u * (uint32_t)c;
+    };
     // LDS destinations of this wave's copies in stage 0 (stage s is s *
     // sizeof(S) bytes further) and in scale chunk buffer 0.
     const uint32_t lds_a0 = lds_addr(&L.stages[0].a[1024 * wave]);
@@ -396,19 +492,28 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
                 copy16(src.a, wave_voff + t * rowstep, soff, lds_a0 + so + 1024 * C::kWaves * t);
     };
     auto issue_w = [&](const TileOperands &src, int kb, int st) {
-        const uint32_t soff = (uint32_t)kb * 128u;
         const uint32_t so = (uint32_t)(st * sizeof(S));
+        if constexpr (kTransW) {
+            // the K block's offset goes into voffset, which the buffer range
+            // check covers (columns past N of the last rows stop at W's end)
+            const uint32_t koff = (uint32_t)kb * 128u * op.ldw;
 #pragma unroll
-        for (int t = 0; t < C::kBLoads; ++t)
-            copy16_nt(src.w, wave_voff + t * rowstep, soff, lds_b0 + so + 1024 * C::kWaves * t);
+            for (int t = 0; t < C::kBLoads; ++t)
+                copy16_nt(src.w, wt_voff(t) + koff, 0u, lds_b0 + so + 1024 * C::kWaves * t);
+        } else {
+            const uint32_t soff = (uint32_t)kb * 128u;
+#pragma unroll
+            for (int t = 0; t < C::kBLoads; ++t)
+                copy16_nt(src.w, wave_voff + t * rowstep, soff,
+                          lds_b0 + so + 1024 * C::kWaves * t);
+        }
     };
     // A chunk that runs past the last K block (G not a multiple of
-    // kScaleChunk) is fetched one dword per lane instead: the buffer range
-    // check covers the lane's voffset only (not soffset), and it may treat a
-    // 16-byte access that straddles the end as wholly out of range, so a
-    // 16-byte piece of the last row would either read past the buffer or lose
-    // its valid scales.  Here every lane's offset includes the chunk's K
-    // offset, and each dword is checked on its own.  Dword copy u of a
+    // kScaleChunk) is fetched one dword per lane instead: a 16-byte piece of
+    // the tile's last row would straddle the end of the scales, and the
+    // buffer range check may treat such an access as wholly out of range
+    // (losing the valid scales in it).  Here every lane's offset (voffset,
+    // with the chunk's K offset in it) is checked on its own dword.  Dword copy u of a
     // chunk buffer fills its dwords 64 u .. + 63: dword d is block j = d % 4
     // of piece h = d / (4 ROWS) of row r = (d / 4) % ROWS.  More copies in a
     // block only make the pipeline's waits stricter.
@@ -444,7 +549,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 #pragma unroll
                 for (int t = 0; t < C::kScaleLoads; ++t)
                     if (wave_u + C::kWaves * t < C::kScaleCopies)
-                        copy16(src.sa, sa_voff[t], (uint32_t)c * (4u * C::kScaleChunk),
+                        copy16(src.sa, sa_voff(t), (uint32_t)c * (4u * C::kScaleChunk),
                                lds_sc0 + so + 1024 * C::kWaves * t);
             } else {
                 issue_chunk_dwords(src.sa, C::BM, c, lds_addr(&L.chunks.v[0][0][0][0]) + so);
@@ -455,7 +560,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 #pragma unroll
                     for (int t = 0; t < C::kScaleLoadsW; ++t)
                         if (wave_u + C::kWaves * t < C::kScaleCopiesW)
-                            copy16(src.swr, swr_voff[t], (uint32_t)c * (4u * C::kScaleChunk),
+                            copy16(src.swr, swr_voff(t), (uint32_t)c * (4u * C::kScaleChunk),
                                    lds_wc0 + sow + 1024 * C::kWaves * t);
                 } else {
                     issue_chunk_dwords(src.swr, C::BN, c,
@@ -465,7 +570,8 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         }
         // every wave fetches the (one or two) weight scales of the block to
         // the same LDS words; the duplicates carry identical values
-        copy4(src.sw, sw_voff, (uint32_t)kb * 4u, lds_sw0 + (uint32_t)st * sizeof(L.sw[0]));
+        copy4(src.sw, sw_voff, (uint32_t)kb * op.sw_kstride,
+              lds_sw0 + (uint32_t)st * sizeof(L.sw[0]));
     };
     // all of block kb
     auto issue = [&](const TileOperands &src, int kb, int st) {
@@ -487,10 +593,34 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     // The activation scale is then one value per lane per M tile and the
     // weight scale one value per wave (or per fragment, see kWaveInOneBlock).
     auto wfrag = [&](int s, int j) {
-        const uint8_t *lb = L.stages[s].b + b_base;
-        const uint4 lo = *reinterpret_cast<const uint4 *>(lb + j * 2048 + frag0);
-        const uint4 hi = *reinterpret_cast<const uint4 *>(lb + j * 2048 + frag1);
-        return make_v8i(lo, hi);
+        if constexpr (kTransW) {
+            typedef int v2i_t __attribute__((ext_vector_type(2)));
+            typedef __attribute__((address_space(3))) v2i_t *lds_v2i;
+            // rows 32 lk + 8 q + lr / 2 all have tw_key = (lr / 2) | (lk & 1) << 3,
+            // so the four reads differ by immediate offsets 8 q BN
+            // (the key passes through an empty asm statement so that the four
+            // fragments' offsets are recomputed here instead of being hoisted
+            // into registers held across the loop)
+            const int c = (wn * C::WN + 16 * j) >> 4;
+            int key = (lr >> 1) | ((lk & 1) << 3);
+            asm volatile("" : "+v"(key));
+            const uint8_t *p = L.stages[s].b + (32 * lk + (lr >> 1)) * C::BN + 8 * (lr & 1) +
+                               (tw_phys<C::BN>(c, key) << 4);
+            v2i_t r[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                r[q] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (lds_v2i)(lds_ptr_t)(const_cast<uint8_t *>(p + 8 * q * C::BN)));
+            v8i v;
+            v[0] = r[0][0]; v[1] = r[0][1]; v[2] = r[1][0]; v[3] = r[1][1];
+            v[4] = r[2][0]; v[5] = r[2][1]; v[6] = r[3][0]; v[7] = r[3][1];
+            return v;
+        } else {
+            const uint8_t *lb = L.stages[s].b + b_base;
+            const uint4 lo = *reinterpret_cast<const uint4 *>(lb + j * 2048 + frag0);
+            const uint4 hi = *reinterpret_cast<const uint4 *>(lb + j * 2048 + frag1);
+            return make_v8i(lo, hi);
+        }
     };
     // Scales of block kb (stage s): sc[i] = sa(i) * sw for waves inside one
     // weight-scale block, else sc[i] = sa(i) and swj[j] = sw(fragment j);
@@ -851,7 +981,7 @@ __device__ __forceinline__ int xcd_logical_tile() {
     return (blockIdx.x % kNumXcd) * per + blockIdx.x / kNumXcd;
 }
 
-template <class C, int OUT, bool kPow2>
+template <class C, int OUT, bool kPow2, bool kTransW = false>
 __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
     __shared__ TileLds<C> lds;
     const int logical = xcd_logical_tile();
@@ -876,9 +1006,13 @@ __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
 
     v4f acc[C::kTM][C::kTN];
     const TileOperands op =
-        tile_operands<C>(p.a, p.sa, p.w, p.sw, row0, p.M - row0, n0, p.N - n0, p.K, p.G);
+        kTransW ? tile_operands_transw<C>(p.a, p.sa, p.w, p.sw, row0, p.M - row0, n0, p.N - n0,
+                                          p.K, p.G, p.ldw, p.NB)
+                : tile_operands<C>(p.a, p.sa, p.w, p.sw, row0, p.M - row0, n0, p.N - n0, p.K,
+                                   p.G);
     const int wn = (threadIdx.x >> 6) % C::kWavesN;
-    tile_mainloop<C, kPow2>(op, p.K, p.G, kb0, kb1, (int)(n0 & 127) + wn * C::WN, lds, acc);
+    tile_mainloop<C, kPow2, kTransW>(op, p.K, p.G, kb0, kb1, (int)(n0 & 127) + wn * C::WN, lds,
+                                     acc);
     if (OUT == kOutPartial)
         tile_store<C, kOutF32, false>(acc, lds, p.partial + (int64_t)ks * p.M * p.N, p.N, row0,
                                       p.M, n0, p.N);
@@ -887,14 +1021,18 @@ __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
 }
 
 // One 256-row tile of the dense GEMM at (row0, n0), full K.
-template <class C, int OUT, bool kPow2>
+template <class C, int OUT, bool kPow2, bool kTransW = false>
 __device__ __forceinline__ void dense_tile(const GemmParams &p, TileLds<C> &lds, int64_t row0,
                                            int64_t n0) {
     v4f acc[C::kTM][C::kTN];
     const TileOperands op =
-        tile_operands<C>(p.a, p.sa, p.w, p.sw, row0, p.M - row0, n0, p.N - n0, p.K, p.G);
+        kTransW ? tile_operands_transw<C>(p.a, p.sa, p.w, p.sw, row0, p.M - row0, n0, p.N - n0,
+                                          p.K, p.G, p.ldw, p.NB)
+                : tile_operands<C>(p.a, p.sa, p.w, p.sw, row0, p.M - row0, n0, p.N - n0, p.K,
+                                   p.G);
     const int wn = (threadIdx.x >> 6) % C::kWavesN;
-    tile_mainloop<C, kPow2>(op, p.K, p.G, 0, p.G, (int)(n0 & 127) + wn * C::WN, lds, acc);
+    tile_mainloop<C, kPow2, kTransW>(op, p.K, p.G, 0, p.G, (int)(n0 & 127) + wn * C::WN, lds,
+                                     acc);
     tile_store<C, OUT>(acc, lds, p.c, p.N, row0, p.M, n0, p.N);
 }
 
@@ -915,7 +1053,7 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int grou
 // share of the CB tiles (columns [0, n_split)), the rest its share of the CN
 // tiles (columns [n_split, N)).  The wide tiles are dispatched first; the
 // LDS union holds either layout.
-template <class CB, class CN, int OUT, bool kPow2>
+template <class CB, class CN, int OUT, bool kPow2, bool kTransW = false>
 __device__ __forceinline__ void two_kind_tile(const GemmParams &p, TileLds<CB> &lds_b,
                                               TileLds<CN> &lds_n) {
     static_assert(CB::kThreads == CN::kThreads && CB::BM == CN::BM, "two-kind tiles");
@@ -928,13 +1066,14 @@ __device__ __forceinline__ void two_kind_tile(const GemmParams &p, TileLds<CB> &
         const int t = xcd * per1 + slot;
         if (t >= t1) return;
         raster(t, p.tiles_m, p.tn1, p.group_m, tm, tn);
-        dense_tile<CB, OUT, kPow2>(p, lds_b, (int64_t)tm * CB::BM, (int64_t)tn * CB::BN);
+        dense_tile<CB, OUT, kPow2, kTransW>(p, lds_b, (int64_t)tm * CB::BM,
+                                            (int64_t)tn * CB::BN);
     } else {
         const int t = xcd * per2 + (slot - per1);
         if (slot - per1 >= per2 || t >= t2) return;
         raster(t, p.tiles_m, p.tn2, p.group_m, tm, tn);
-        dense_tile<CN, OUT, kPow2>(p, lds_n, (int64_t)tm * CN::BM,
-                                   p.n_split + (int64_t)tn * CN::BN);
+        dense_tile<CN, OUT, kPow2, kTransW>(p, lds_n, (int64_t)tm * CN::BM,
+                                            p.n_split + (int64_t)tn * CN::BN);
     }
 }
 
@@ -945,13 +1084,13 @@ __device__ __forceinline__ void two_kind_tile(const GemmParams &p, TileLds<CB> &
 // each per CU instead of two 256 x 256 tiles on 192 CUs and one on the
 // rest).  Each XCD takes a contiguous share of each kind, the wide tiles
 // first; the LDS holds either layout.
-template <int OUT, bool kPow2>
+template <int OUT, bool kPow2, bool kTransW = false>
 __global__ __launch_bounds__(BigTile::kThreads) void dense_gemm_two_kind_kernel(GemmParams p) {
     __shared__ union DenseLds {
         TileLds<BigTile> big;
         TileLds<NarrowTile> narrow;
     } lds;
-    two_kind_tile<BigTile, NarrowTile, OUT, kPow2>(p, lds.big, lds.narrow);
+    two_kind_tile<BigTile, NarrowTile, OUT, kPow2, kTransW>(p, lds.big, lds.narrow);
 }
 
 // Wgrad with 128 x 256 tiles on columns [0, n_split) and 128 x 192 tiles on
@@ -1444,15 +1583,15 @@ Plan plan_dense(int64_t M, int64_t N, int64_t K) {
     return {false, s, per};
 }
 
-template <class C, int OUT, bool kPow2>
+template <class C, int OUT, bool kPow2, bool kTransW = false>
 hipError_t launch_dense(const GemmParams &p0, hipStream_t stream) {
     GemmParams p = p0;
     p.tiles_m = (int)((p.M + C::BM - 1) / C::BM);
     p.tiles_n = (int)((p.N + C::BN - 1) / C::BN);
     p.ntiles = p.tiles_m * p.tiles_n * p.ksplit;
     const int grid = round_up(p.ntiles, kNumXcd);
-    hipLaunchKernelGGL((dense_gemm_kernel<C, OUT, kPow2>), dim3(grid), dim3(C::kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((dense_gemm_kernel<C, OUT, kPow2, kTransW>), dim3(grid),
+                       dim3(C::kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -1632,5 +1771,70 @@ hipError_t launch_block_gemm_fused_quant(const void *x, const void *w, const flo
     return hipGetLastError();
 }
 
+// Dgrad, dX [M][Kx] = dY [M][N] W [N][Kx]: the block GEMM with dY as the
+// activations (inner dimension N) and W read transposed from its forward
+// layout; the same plan as fp8_block_gemm for an M x Kx output over N
+// (256 x 256 tiles, or 128 x 64 tiles with split-K for small M).
+hipError_t launch_block_gemm_dgrad(const void *dy, const float *sdy, const void *w,
+                                   const float *sw, void *dx, bool bf16_out, int64_t M,
+                                   int64_t N, int64_t Kx, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    GemmParams p{};
+    p.a = static_cast<const uint8_t *>(dy);
+    p.sa = sdy;
+    p.w = static_cast<const uint8_t *>(w);
+    p.sw = sw;
+    p.c = dx;
+    p.M = M;
+    p.N = Kx;
+    p.K = N;
+    p.G = (int)(N / 128);
+    p.NB = (int)(Kx / 128);
+    p.ldw = Kx;
+    p.group_m = 8;
+    Plan pl = plan_dense(M, Kx, N);
+    const size_t need = gemm_workspace_bytes(M, Kx, N);
+    if (pl.ksplit > 1 && (workspace == nullptr || workspace_bytes < need)) pl = {false, 1, p.G};
+    p.ksplit = pl.ksplit;
+    p.kb_per_split = pl.kb_per_split;
+    p.partial = static_cast<float *>(workspace);
+    if (pl.big && pl.tn2 > 0) {
+        // the forward GEMM's two tile widths (see block_gemm)
+        p.tiles_m = (int)((p.M + 255) / 256);
+        p.tn1 = pl.tn1;
+        p.tn2 = pl.tn2;
+        p.n_split = (int64_t)pl.tn1 * BigTile::BN;
+        const int per1 = (p.tiles_m * p.tn1 + kNumXcd - 1) / kNumXcd;
+        const int per2 = (p.tiles_m * p.tn2 + kNumXcd - 1) / kNumXcd;
+        const int grid = kNumXcd * (per1 + per2);
+        if (bf16_out)
+            hipLaunchKernelGGL((dense_gemm_two_kind_kernel<kOutBF16, false, true>), dim3(grid),
+                               dim3(BigTile::kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((dense_gemm_two_kind_kernel<kOutF32, false, true>), dim3(grid),
+                               dim3(BigTile::kThreads), 0, stream, p);
+        return hipGetLastError();
+    }
+    if (pl.big)
+        return bf16_out ? launch_dense<BigTile, kOutBF16, false, true>(p, stream)
+                        : launch_dense<BigTile, kOutF32, false, true>(p, stream);
+    if (p.ksplit > 1) {
+        hipError_t e = launch_dense<SmallTile, kOutPartial, false, true>(p, stream);
+        if (e != hipSuccess) return e;
+        const int64_t MN = p.M * p.N;
+        const int64_t blocks = (MN / 4 + 255) / 256;
+        if (bf16_out)
+            hipLaunchKernelGGL(splitk_reduce_kernel<kOutBF16>, dim3((unsigned)blocks), dim3(256),
+                               0, stream, p.partial, dx, MN, p.ksplit);
+        else
+            hipLaunchKernelGGL(splitk_reduce_kernel<kOutF32>, dim3((unsigned)blocks), dim3(256),
+                               0, stream, p.partial, dx, MN, p.ksplit);
+        return hipGetLastError();
+    }
+    return bf16_out ? launch_dense<SmallTile, kOutBF16, false, true>(p, stream)
+                    : launch_dense<SmallTile, kOutF32, false, true>(p, stream);
+}
+
 }  // namespace fp8blk
+
 

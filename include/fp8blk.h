@@ -299,6 +299,31 @@ fp8_status fp8_block_gemm_noalloc(const void *a_e4m3, const float *a_scales,
                                   int out_dtype, int64_t M, int64_t N, int64_t K,
                                   void *hip_stream);
 
+/*
+ * Dgrad on the forward layout of the weights, read transposed inside the
+ * GEMM (page "why-be.co.kr as_center 36949", passage recommending that
+ * matrices be read transposed from shared memory before the MMA; gfx950's
+ * ds_read_b64_tr_b8 does that): no transposed copy of W is needed.
+ *   dX[m][k] = sum_nb dy_scales[m][nb] * w_scales[nb][k/128]
+ *                    * sum_{n in block nb} dy[m][n] * w[n][k]
+ *   dy_e4m3 [M][N] E4M3 with dy_scales [M][N/128] (fp8_quant_act_1x128 of dY)
+ *   w_e4m3  [N][K] E4M3 with w_scales [N/128][K/128]: the forward weights as
+ *           fp8_quant_weight_128x128 wrote them (row n = output channel of
+ *           the forward layer); a 128x128 block's scale serves both
+ *           orientations
+ *   dx      [M][K] fp32 or bf16 (RNE)
+ * N % 128 == 0, K % 128 == 0, N < 2^24 and N * K < 2^32 are required
+ * (FP8_ERR_SHAPE); dy_e4m3, w_e4m3 and dx 16-byte aligned (FP8_ERR_ALIGN).
+ * workspace: as fp8_block_gemm for an M x K output over N, i.e. of
+ * fp8_gemm_workspace_bytes(M, K, N, out_dtype) bytes for the split-K path.
+ * Results equal fp8_block_gemm(dy, W^T) with W^T from
+ * fp8_transpose_weight_128x128 up to the FP32 summation order.
+ */
+fp8_status fp8_block_gemm_dgrad(const void *dy_e4m3, const float *dy_scales,
+                                const void *w_e4m3, const float *w_scales, void *dx,
+                                int out_dtype, int64_t M, int64_t N, int64_t K,
+                                void *workspace, size_t workspace_bytes, void *hip_stream);
+
 /* Workspace bytes that let fp8_block_gemm use its split-K path for this
  * shape (0 when the shape does not use it). */
 size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int out_dtype);

@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
         method + [m + "_pow2" for m in method]
         + ["fp8_quant_act_128x1_t", "fp8_transpose_weight_128x128", "fp8_block_gemm_wgrad"]
         + ["fp8_gemm_workspace_bytes", "fp8_status_string", "fp8_block_gemm_noalloc",
-           "fp8_block_gemm_fused_quant"])
+           "fp8_block_gemm_fused_quant", "fp8_block_gemm_dgrad"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -135,6 +135,26 @@ def test_grouped_argument_errors(suffix):
     assert grouped_(lib, ws=A16, wsb=0) == B.FP8_ERR_WORKSPACE
     # T = 0 is a no-op (E = 0 allowed then)
     assert grouped_(lib, T=0, E=0, a=NUL, sa=NUL, off=NUL, c=NUL) == B.FP8_OK
+
+
+def test_dgrad_argument_errors():
+    lib = B.lib()
+
+    def dg(dy=A16, sdy=A16, w=A16, sw=A16, dx=A16, dt=B.FP8_OUT_BF16, M=128, N=256, K=512,
+           ws=NUL, wsb=0):
+        return lib.fp8_block_gemm_dgrad(dy, sdy, w, sw, dx, dt, M, N, K, ws, wsb, NUL)
+    assert dg(N=200) == B.FP8_ERR_SHAPE          # inner dimension
+    assert dg(K=500) == B.FP8_ERR_SHAPE          # output columns
+    assert dg(M=-1) == B.FP8_ERR_SHAPE
+    assert dg(N=0) == B.FP8_ERR_SHAPE
+    assert dg(N=1 << 24) == B.FP8_ERR_SHAPE
+    assert dg(N=1 << 17, K=1 << 15) == B.FP8_ERR_SHAPE   # W of 2^32 bytes
+    assert dg(dt=5) == B.FP8_ERR_DTYPE
+    assert dg(w=NUL) == B.FP8_ERR_NULL
+    assert dg(w=A8) == B.FP8_ERR_ALIGN
+    assert dg(dx=A8) == B.FP8_ERR_ALIGN
+    assert dg(ws=A16, wsb=0) == B.FP8_ERR_WORKSPACE
+    assert dg(M=0, dy=NUL, dx=NUL) == B.FP8_OK
 
 
 def test_fused_quant_gemm_argument_errors():

@@ -161,3 +161,63 @@ def test_wgrad_workload_chain_sampled_rows_and_deterministic():
     R = oracle.rowscaled_gemm(qdy_o, sdy_o, qx_o, sx_o, rows)
     check_gemm(c0[torch().from_numpy(rows).cuda()], R, "f32", "wgrad workload rows",
                gemm_error_bound(qdy_o, sdy_o, qx_o, sx_o, rows, row_scaled_w=True))
+
+
+# ---- Dgrad with W read transposed inside the GEMM -------------------------------
+
+@pytest.mark.parametrize("M,N,K", [
+    (64, 256, 384),      # small tiles, one output tile row
+    (300, 384, 640),     # small tiles, ragged M
+    (256, 7168, 2048),   # small tiles with split-K through a workspace
+    (4000, 1280, 7040),  # 256 x 256 tiles, ragged M, the last 128 output columns
+                         # of a 256-wide tile past K (read, never stored)
+    (4096, 512, 6144),   # 256 x 192 tiles only (12 chunks per LDS row, rotated)
+    (4096, 384, 7168),   # both tile widths (256 x 256 and 256 x 192)
+])
+def test_dgrad_transposed_reads(M, N, K):
+    # dX [M][K] = dY [M][N] W [N][K] with W in its forward layout: against
+    # the oracle (every row up to 300, else rows of every tile) within the
+    # per-output bound, and FP32 bitwise equal to the forward GEMM on the
+    # transposed copy of W (the same bytes and block products per output)
+    rng = np.random.default_rng(M + 3 * N + 7 * K)
+    dy, _ = I.activations(rng, M, N, 0.01, 20.0)
+    w = I.weights(rng, (N, K))
+    qw, sw = oracle.quant_weight_128x128(w)
+    qdy, sdy = oracle.quant_act_1x128(dy)
+    qwt, swt = oracle.transpose_weight(qw, sw)
+    t = torch()
+    nbytes = B.fp8_gemm_workspace_bytes(M, K, N, "f32")
+    ws = t.empty(nbytes, dtype=t.uint8, device="cuda") if nbytes else None
+    d = [dev(qdy), dev(sdy), dev(qw), dev(sw)]
+    c32 = B.fp8_block_gemm_dgrad(*d, out_dtype="f32", workspace=ws)
+    c16 = B.fp8_block_gemm_dgrad(*d, out_dtype="bf16", workspace=ws)
+    ref = B.fp8_block_gemm(dev(qdy), dev(sdy), dev(qwt), dev(swt), out_dtype="f32", workspace=ws)
+    rows = np.arange(M) if M <= 300 else tile_rows(M, 256, per_tile=2)
+    log(f"  dgrad {M}x{N}x{K} (split-K workspace {nbytes} B): oracle on {rows.size} rows ...")
+    R = oracle.block_gemm(qdy, sdy, qwt, swt, rows)
+    splits = max(1, nbytes // (M * K * 4))
+    b = gemm_error_bound(qdy, sdy, qwt, swt, rows, splits=splits)
+    ri = t.from_numpy(rows).cuda()
+    check_gemm(c32[ri], R, "f32", f"dgrad transposed reads {M}x{N}x{K} f32", b)
+    check_gemm(c16[ri], R, "bf16", f"dgrad transposed reads {M}x{N}x{K} bf16", b)
+    assert t.equal(c32, ref), "transposed-read Dgrad differs from the GEMM on W^T"
+
+
+def test_dgrad_transposed_reads_workload():
+    # the 4096 x 7168 x 7168 layer: GPU chain (1x128 quantizer on dY, Dgrad
+    # on the forward weights), rows of every 256-row tile against the oracle
+    M, N, K = 4096, 7168, 7168
+    rng = np.random.default_rng(17)
+    dy, _ = I.activations(rng, M, N, 0.0, 1.0)
+    w = I.weights(rng, (N, K))
+    qw, sw = oracle.quant_weight_128x128(w)
+    qdy_o, sdy_o = oracle.quant_act_1x128(dy)
+    qdy, sdy = B.fp8_quant_act_1x128(dev_bf16(dy))
+    assert_bytes_and_scales(host(qdy), host(sdy), qdy_o, sdy_o, "dY 1x128")
+    c = B.fp8_block_gemm_dgrad(qdy, sdy, dev(qw), dev(sw), out_dtype="bf16")
+    qwt, swt = oracle.transpose_weight(qw, sw)
+    rows = tile_rows(M, 256, per_tile=1)
+    log(f"  oracle Dgrad on {rows.size} rows of {M}x{K} over {N} ...")
+    R = oracle.block_gemm(qdy_o, sdy_o, qwt, swt, rows)
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, "bf16", "dgrad workload rows",
+               gemm_error_bound(qdy_o, sdy_o, qwt, swt, rows))
