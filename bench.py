@@ -35,6 +35,7 @@ Printed as one JSON line, with:
 
 Usage: python bench.py [--gpus 1] [--steps 500] [--warmup 300]
        [--no-parts] [--no-cpu-baseline] [--copy-calib] [--part NAME]
+       [--preroll SECONDS]
 --part NAME runs only that part (for kernel traces of one kernel) and prints
 its JSON.
 """
@@ -540,6 +541,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--part", default=None, help="run only this part and print it")
+    ap.add_argument("--preroll", type=float, default=PREROLL_S,
+                    help="seconds of untimed steps before the warm-up (default %(default)s)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the hot path is data-parallel and this "
@@ -604,12 +607,12 @@ def main():
     t_pre = time.perf_counter()
     sampling = False
     n_pre = 0
-    while time.perf_counter() - t_pre < PREROLL_S:
+    while time.perf_counter() - t_pre < args.preroll:
         for _ in range(10):
             step(False)
         n_pre += 10
         torch.cuda.synchronize()
-        if not sampling and time.perf_counter() - t_pre > 0.5 * PREROLL_S:
+        if not sampling and time.perf_counter() - t_pre > 0.5 * args.preroll:
             clk.start()
             sampling = True
     if not sampling:
@@ -648,7 +651,7 @@ def main():
                    "M": M, "N": N, "K": K, "weights": "128x128-quantized once before timing",
                    "parallelism": "single GPU",
                    "preroll": f"CPU baseline, per-kernel parts, then {n_pre} untimed steps "
-                              f"({PREROLL_S} s) before the warm-up steps"},
+                              f"({args.preroll} s) before the warm-up steps"},
         "roofline": roof,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "compute_units": props.multi_processor_count,
