@@ -13,10 +13,16 @@
  *   - fp8_transpose_weight_128x128 (equal to the transposed oracle bytes and
  *     scales);
  *   - fp8_block_gemm_wgrad, dW = X^T X over the whole 128-token blocks of
- *     the activations (sampled rows, at most 1e-3).
+ *     the activations (sampled rows, at most 1e-3);
+ *   - fp8_block_gemm_fused_quant on the bf16 activations (its E4M3 bytes and
+ *     scales equal the oracle's, C within 1e-3);
+ *   - fp8_block_gemm_noalloc (bitwise equal to fp8_block_gemm's C);
+ *   - fp8_block_gemm_dgrad, dX = dY W for a seeded dY [M][N] on the forward
+ *     weights (within 1e-3 of the oracle on the transposed weights).
  * The argument checks are exercised too (a K that is not a multiple of 128,
  * NULL pointers, an unknown output type, a token count that is not a
- * multiple of 128 for Wgrad, no experts for routed tokens).
+ * multiple of 128 for Wgrad, no experts for routed tokens, fused bytes out
+ * without scales out, a Dgrad inner size that is not a multiple of 128).
  *
  * Usage: c_abi_check [M N K]   (defaults 200 384 2688: two M tiles, the
  * second ragged, and K split four ways through the workspace).  Prints one
@@ -266,12 +272,76 @@ int main(int argc, char **argv) {
                                                    stream) == FP8_ERR_SHAPE;
     fails += !err_tokens + !err_experts;
 
+    /* ---- quantization fused into the GEMM, on the bf16 activations ---- */
+    void *dqf = dev_alloc(M * K);
+    float *dsf = dev_alloc(4 * M * G), *dcf = dev_alloc(4 * M * N), *dcn = dev_alloc(4 * M * N);
+    st = fp8_block_gemm_fused_quant(dx, dqw, dsw, dcf, FP8_OUT_F32, M, N, K, dqf, dsf, stream);
+    /* ---- the no-allocation GEMM: its own static scratch for split-K ---- */
+    if (st == FP8_OK)
+        st = fp8_block_gemm_noalloc(dqa, dsa, dqw, dsw, dcn, FP8_OUT_F32, M, N, K, stream);
+    if (st != FP8_OK) {
+        printf("c-abi FAIL (fused / noalloc): %s\n", fp8_status_string(st));
+        return 1;
+    }
+    HIP_OK(hipStreamSynchronize(stream));
+    uint8_t *qf = malloc(M * K);
+    float *sf = malloc(4 * M * G), *cf = malloc(4 * M * N), *cn = malloc(4 * M * N);
+    HIP_OK(hipMemcpy(qf, dqf, M * K, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(sf, dsf, 4 * M * G, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(cf, dcf, 4 * M * N, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(cn, dcn, 4 * M * N, hipMemcpyDeviceToHost));
+    const int fused_q_equal = !memcmp(qf, qa_o, M * K) && !memcmp(sf, sa_o, 4 * M * G);
+    const double fused_rel_fro = rel_fro_of(cf, R, M * N);
+    const int noalloc_equal = !memcmp(cn, c, 4 * M * N);
+    fails += !fused_q_equal + !(fused_rel_fro <= 1e-3) + !noalloc_equal;
+
+    /* ---- Dgrad on the forward weights: dX [M][K] = dY [M][N] W [N][K] ---- */
+    uint16_t *dyb = malloc(sizeof(uint16_t) * M * N);
+    for (int64_t i = 0; i < M * N; ++i) dyb[i] = to_bf16((float)(2.0 * uniform01() - 1.0));
+    void *ddy = dev_alloc(2 * M * N), *dqdy = dev_alloc(M * N);
+    float *dsdy = dev_alloc(4 * M * NB), *ddx = dev_alloc(4 * M * K);
+    HIP_OK(hipMemcpy(ddy, dyb, 2 * M * N, hipMemcpyHostToDevice));
+    const size_t ws_dg = fp8_gemm_workspace_bytes(M, K, N, FP8_OUT_F32);
+    void *wsd = ws_dg ? dev_alloc(ws_dg) : NULL;
+    st = fp8_quant_act_1x128(ddy, M, N, dqdy, dsdy, stream);
+    if (st == FP8_OK)
+        st = fp8_block_gemm_dgrad(dqdy, dsdy, dqw, dsw, ddx, FP8_OUT_F32, M, N, K, wsd, ws_dg,
+                                  stream);
+    if (st != FP8_OK) {
+        printf("c-abi FAIL (dgrad): %s\n", fp8_status_string(st));
+        return 1;
+    }
+    HIP_OK(hipStreamSynchronize(stream));
+    uint8_t *qdy_o = malloc(M * N), *qwt_o = malloc(K * N);
+    float *sdy_o = malloc(4 * M * NB), *swt_o = malloc(4 * G * NB), *dxh = malloc(4 * M * K);
+    double *Rd = malloc(sizeof(double) * M * K);
+    HIP_OK(hipMemcpy(dxh, ddx, 4 * M * K, hipMemcpyDeviceToHost));
+    orc_quant_act_1x128(dyb, M, N, qdy_o, sdy_o);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) qwt_o[k * N + n] = qw_o[n * K + k];
+    for (int64_t nb = 0; nb < NB; ++nb)
+        for (int64_t g = 0; g < G; ++g) swt_o[g * NB + nb] = sw_o[nb * G + g];
+    orc_block_gemm_rows(qdy_o, sdy_o, qwt_o, swt_o, M, K, N, rows, M, Rd);
+    const double dgrad_rel_fro = rel_fro_of(dxh, Rd, M * K);
+    fails += !(dgrad_rel_fro <= 1e-3);
+    const int err_fused = fp8_block_gemm_fused_quant(dx, dqw, dsw, dcf, FP8_OUT_F32, M, N, K, dqf,
+                                                     NULL, stream) == FP8_ERR_NULL;
+    const int err_dgrad = fp8_block_gemm_dgrad(dqdy, dsdy, dqw, dsw, ddx, FP8_OUT_F32, M, 200, K,
+                                               NULL, 0, stream) == FP8_ERR_SHAPE;
+    fails += !err_fused + !err_dgrad;
+
     printf("c-abi %s: M=%lld N=%lld K=%lld workspace=%zu bytes_equal=%d scales_equal=%d "
            "rel_fro=%.3e grouped_rel_fro=%.3e q128x1_t_equal=%d transpose_equal=%d "
-           "wgrad_tokens=%lld wgrad_rel_fro=%.3e error_codes=%d%d%d%d%d\n",
+           "wgrad_tokens=%lld wgrad_rel_fro=%.3e fused_q_equal=%d fused_rel_fro=%.3e "
+           "noalloc_equal=%d dgrad_rel_fro=%.3e error_codes=%d%d%d%d%d%d%d\n",
            fails ? "FAIL" : "ok", (long long)M, (long long)N, (long long)K, ws_bytes, bytes_equal,
            scales_equal, rel_fro, grouped_rel_fro, t_equal, tr_equal, (long long)T, wgrad_rel_fro,
-           err_shape, err_null, err_dtype, err_tokens, err_experts);
+           fused_q_equal, fused_rel_fro, noalloc_equal, dgrad_rel_fro, err_shape, err_null,
+           err_dtype, err_tokens, err_experts, err_fused, err_dgrad);
+    hipFree(dqf); hipFree(dsf); hipFree(dcf); hipFree(dcn); hipFree(ddy); hipFree(dqdy);
+    hipFree(dsdy); hipFree(ddx); if (wsd) hipFree(wsd);
+    free(qf); free(sf); free(cf); free(cn); free(dyb); free(qdy_o); free(qwt_o); free(sdy_o);
+    free(swt_o); free(dxh); free(Rd);
     hipFree(dwe); hipFree(dqwe); hipFree(dswe); hipFree(doff); hipFree(dcg);
     hipFree(dqt); hipFree(dqwt); hipFree(dst); hipFree(dswt);
     free(we); free(qwe_o); free(swe_o); free(cg16); free(cg); free(Rg); free(found);

@@ -2,10 +2,12 @@
 (tests/c_abi/c_abi_check.c, built by tests/c_abi/build.py and by
 __graft_entry__.build()): quantization and the block GEMM through
 include/fp8blk.h on its own HIP stream, then the grouped GEMM, the 128x1
-transposed quantizer, the weight transpose and Wgrad, each checked inside
-the program against the oracle's C functions (bytes and scale bits equal;
-rel. Frobenius error <= 1e-3 for FP32 output, <= 8e-3 for BF16), plus the
-documented error codes."""
+transposed quantizer, the weight transpose, Wgrad, the GEMM with the
+quantization fused in, the no-allocation GEMM and Dgrad on the forward
+weights, each checked inside the program against the oracle's C functions
+(bytes and scale bits equal; rel. Frobenius error <= 1e-3 for FP32 output,
+<= 8e-3 for BF16; the no-allocation GEMM bitwise equal to fp8_block_gemm),
+plus the documented error codes."""
 import subprocess
 
 import pytest
