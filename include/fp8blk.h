@@ -26,7 +26,11 @@
  *     stream) and runs asynchronously.  Device faults surface at the caller's
  *     next synchronization on that stream.
  *   - Arguments are validated before anything is enqueued; on any error
- *     nothing is written.  No C++ exception crosses this boundary.
+ *     nothing is written.  One exception: a split-K GEMM is two launches,
+ *     and if the second (the reduction into C) fails with FP8_ERR_HIP the
+ *     first may already be enqueued and write its partial sums into the
+ *     workspace; C is then not written.  No C++ exception crosses this
+ *     boundary.
  *   - Calls are reentrant and thread-safe (concurrent calls on different
  *     streams must not share output or workspace buffers), with one
  *     exception: fp8_block_gemm_noalloc.  The library's mutable state is
