@@ -323,18 +323,24 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=None):
             cn = torch.empty((M, n), dtype=torch.bfloat16, device="cuda")
             ms_f, _ = P.timed(lambda: F.fp8_block_gemm_fused_quant(X, wq, ws, out_dtype="bf16",
                                                                    c=cn))
+            # the two-call path in its best configuration: with the split-K
+            # workspace its GEMM asks for (small N)
+            nb = F.fp8_gemm_workspace_bytes(M, n, K, "bf16")
+            gws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
 
             def two_call():
                 F.fp8_quant_act_1x128(X, qa, sa)
-                F.fp8_block_gemm(qa, sa, wq, ws, out_dtype="bf16", c=cn)
+                F.fp8_block_gemm(qa, sa, wq, ws, out_dtype="bf16", c=cn, workspace=gws)
             ms_t, _ = P.timed(two_call)
             rows.append({"N": n, "fused_us": round(ms_f * 1e3, 2),
                          "two_call_us": round(ms_t * 1e3, 2),
+                         "two_call_split_k_workspace_bytes": nb,
                          "fused_faster": ms_f < ms_t})
-            del wq, ws, cn
+            del wq, ws, cn, gws
         P.out["fused_quant_crossover_m4096_k7168"] = {
             "rows": rows, "note": "M=4096, K=7168, bf16 out; each launch (or pair) after a "
-                                  "512 MB cache flush; median of 50"}
+                                  "512 MB cache flush; median of 50; the two-call GEMM "
+                                  "gets the split-K workspace it asks for"}
 
     # backward of the same layer: dY [4096][7168] (same distribution as X
     # without outliers); Dgrad = forward GEMM with the transposed weights,
