@@ -3,9 +3,12 @@
 Quantization and the GEMMs allocate nothing, and none of them issues a
 memset, so a serving loop can capture them once and replay them: the
 split-K path takes its partials from the caller's workspace and reduces
-them with a kernel.  Each test captures 1x128 activation quantization
-followed by a GEMM into one graph (torch.cuda.CUDAGraph over the library's
-launches on the capture stream) and replays it several times.  Between
+them with a kernel (the no-allocation GEMM from the library's static
+scratch array instead).  Each test captures 1x128 activation quantization
+followed by a GEMM (plain, split-K, grouped, no-allocation, Dgrad on the
+forward weights), or the GEMM with the quantization fused in, into one
+graph (torch.cuda.CUDAGraph over the library's launches on the capture
+stream) and replays it several times.  Between
 replays the program's own eager work changes the bf16 input in place and
 synchronizes, and every replay must equal, bit for bit, the eager chain on
 the same input: the same kernels run on the same bytes, in a fixed
@@ -143,3 +146,80 @@ def test_graph_quant_and_grouped_gemm():
         return q2, s2, c2
 
     replay_and_check(capture, eager, x, fresh, "quant + grouped GEMM, 6 experts")
+
+
+def test_graph_quant_and_noalloc_split_k_gemm():
+    # the no-allocation GEMM is meant for capture: 64 x 2048 x 7168 splits K
+    # through the library's static scratch array; every replay equals the
+    # eager chain through the workspace GEMM (same plan, same order)
+    t = torch()
+    M, N, K = 64, 2048, 7168
+    x = activations(5, M, K)
+    fresh = [activations(40 + r, M, K) for r in range(REPLAYS)]
+    qw, sw = B.fp8_quant_weight_128x128(dev_bf16(I.weights(np.random.default_rng(6), (N, K))))
+    assert B.fp8_gemm_workspace_bytes(M, N, K, "bf16") > 0
+    q = t.empty((M, K), dtype=t.uint8, device="cuda")
+    s = t.empty((M, K // 128), dtype=t.float32, device="cuda")
+    c = t.empty((M, N), dtype=t.bfloat16, device="cuda")
+
+    def capture():
+        B.fp8_quant_act_1x128(x, q, s)
+        B.fp8_block_gemm_noalloc(q, s, qw, sw, out_dtype="bf16", c=c)
+        return q, s, c
+
+    def eager():
+        q2, s2 = B.fp8_quant_act_1x128(x)
+        ws = t.empty(B.fp8_gemm_workspace_bytes(M, N, K, "bf16"), dtype=t.uint8, device="cuda")
+        return q2, s2, B.fp8_block_gemm(q2, s2, qw, sw, out_dtype="bf16", workspace=ws)
+
+    replay_and_check(capture, eager, x, fresh, "quant + no-allocation split-K GEMM 64x2048x7168")
+
+
+def test_graph_fused_quant_gemm():
+    # the quantization fused into the GEMM, with its quantized outputs
+    t = torch()
+    M, N, K = 96, 512, 1280
+    x = activations(7, M, K)
+    fresh = [activations(50 + r, M, K) for r in range(REPLAYS)]
+    qw, sw = B.fp8_quant_weight_128x128(dev_bf16(I.weights(np.random.default_rng(8), (N, K))))
+    q = t.empty((M, K), dtype=t.uint8, device="cuda")
+    s = t.empty((M, K // 128), dtype=t.float32, device="cuda")
+    c = t.empty((M, N), dtype=t.float32, device="cuda")
+
+    def capture():
+        B.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype="f32", c=c, q_out=q, sa_out=s)
+        return q, s, c
+
+    def eager():
+        c2, q2, s2 = B.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype="f32",
+                                                   return_quantized=True)
+        return q2, s2, c2
+
+    replay_and_check(capture, eager, x, fresh, "fused quantization + GEMM 96x512x1280 f32")
+
+
+def test_graph_dgrad_transposed_split_k():
+    # Dgrad on the forward weights (read transposed), small M: split-K
+    # through the workspace
+    t = torch()
+    M, N, Kx = 64, 1024, 2048  # dY [M][N], W [N][Kx], dX [M][Kx]
+    dy = activations(9, M, N)
+    fresh = [activations(60 + r, M, N) for r in range(REPLAYS)]
+    qw, sw = B.fp8_quant_weight_128x128(dev_bf16(I.weights(np.random.default_rng(10), (N, Kx))))
+    q = t.empty((M, N), dtype=t.uint8, device="cuda")
+    s = t.empty((M, N // 128), dtype=t.float32, device="cuda")
+    dx = t.empty((M, Kx), dtype=t.float32, device="cuda")
+    nbytes = B.fp8_gemm_workspace_bytes(M, Kx, N, "f32")
+    ws = t.empty(max(nbytes, 256), dtype=t.uint8, device="cuda") if nbytes else None
+
+    def capture():
+        B.fp8_quant_act_1x128(dy, q, s)
+        B.fp8_block_gemm_dgrad(q, s, qw, sw, out_dtype="f32", dx=dx, workspace=ws)
+        return q, s, dx
+
+    def eager():
+        q2, s2 = B.fp8_quant_act_1x128(dy)
+        ws2 = t.empty_like(ws) if ws is not None else None
+        return q2, s2, B.fp8_block_gemm_dgrad(q2, s2, qw, sw, out_dtype="f32", workspace=ws2)
+
+    replay_and_check(capture, eager, dy, fresh, "quant + Dgrad (W read transposed) 64x2048 over 1024")
