@@ -32,6 +32,9 @@
 //   - The output tile leaves through LDS in whole 128-byte lines.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -1583,6 +1586,49 @@ Plan plan_dense(int64_t M, int64_t N, int64_t K) {
     return {false, s, per};
 }
 
+// With FP8BLK_LOG set in the environment (to anything but "" or "0"), every
+// GEMM call prints the plan it launches, one line on stderr: the entry, the
+// output and inner sizes, the tile shapes, the K splits and the grid.
+bool plan_log_on() {
+    static const bool on = [] {
+        const char *v = getenv("FP8BLK_LOG");
+        return v != nullptr && *v != 0 && strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+void log_plan(const char *entry, int64_t M, int64_t N, int64_t K, const char *tiles, int tn1,
+              int tn2, int ksplit, int grid) {
+    if (!plan_log_on()) return;
+    if (tn2 > 0)
+        fprintf(stderr,
+                "fp8blk: %s M=%lld N=%lld K=%lld tiles=%s (%d + %d column tiles) ksplit=%d "
+                "grid=%d\n",
+                entry, (long long)M, (long long)N, (long long)K, tiles, tn1, tn2, ksplit, grid);
+    else
+        fprintf(stderr, "fp8blk: %s M=%lld N=%lld K=%lld tiles=%s ksplit=%d grid=%d\n", entry,
+                (long long)M, (long long)N, (long long)K, tiles, ksplit, grid);
+}
+
+// Plan of the dense GEMM family (forward and Dgrad) for the log line.
+void log_dense_plan(const char *entry, const GemmParams &p, const Plan &pl) {
+    if (!plan_log_on()) return;
+    if (pl.big && pl.tn2 > 0) {
+        const int tm = (int)((p.M + 255) / 256);
+        const int grid = kNumXcd * ((tm * pl.tn1 + kNumXcd - 1) / kNumXcd +
+                                    (tm * pl.tn2 + kNumXcd - 1) / kNumXcd);
+        log_plan(entry, p.M, p.N, p.K, "256x256+256x192", pl.tn1, pl.tn2, 1, grid);
+    } else if (pl.big) {
+        const int t = (int)(((p.M + 255) / 256) * ((p.N + 255) / 256));
+        log_plan(entry, p.M, p.N, p.K, "256x256", 0, 0, 1, round_up(t, kNumXcd));
+    } else {
+        const int t = (int)(((p.M + SmallTile::BM - 1) / SmallTile::BM) *
+                            ((p.N + SmallTile::BN - 1) / SmallTile::BN));
+        log_plan(entry, p.M, p.N, p.K, pl.ksplit > 1 ? "128x64 split-K + reduction" : "128x64", 0,
+                 0, pl.ksplit, round_up(t * pl.ksplit, kNumXcd));
+    }
+}
+
 template <class C, int OUT, bool kPow2, bool kTransW = false>
 hipError_t launch_dense(const GemmParams &p0, hipStream_t stream) {
     GemmParams p = p0;
@@ -1654,6 +1700,7 @@ hipError_t launch_block_gemm(const void *a, const float *sa, const void *w, cons
     p.ksplit = pl.ksplit;
     p.kb_per_split = pl.kb_per_split;
     p.partial = static_cast<float *>(workspace);
+    log_dense_plan(pow2 ? "block_gemm_pow2" : "block_gemm", p, pl);
     if (pow2)
         return bf16_out ? block_gemm<kOutBF16, true>(p, pl, c, stream)
                         : block_gemm<kOutF32, true>(p, pl, c, stream);
@@ -1687,6 +1734,7 @@ hipError_t launch_block_gemm_wgrad(const void *a, const float *sa, const void *b
         const int per1 = (p.tiles_m * tn1 + kNumXcd - 1) / kNumXcd;
         const int per2 = (p.tiles_m * tn2 + kNumXcd - 1) / kNumXcd;
         const dim3 grid((unsigned)(kNumXcd * (per1 + per2)));
+        log_plan("block_gemm_wgrad", M, N, K, "128x256+128x192", tn1, tn2, 1, (int)grid.x);
         if (bf16_out)
             hipLaunchKernelGGL((wgrad_two_kind_kernel<kOutBF16>), grid, dim3(WgradTile::kThreads),
                                0, stream, p);
@@ -1695,6 +1743,10 @@ hipError_t launch_block_gemm_wgrad(const void *a, const float *sa, const void *b
                                0, stream, p);
         return hipGetLastError();
     }
+    log_plan("block_gemm_wgrad", M, N, K, "128x256", 0, 0, 1,
+             round_up((int)(((M + WgradTile::BM - 1) / WgradTile::BM) *
+                            ((N + WgradTile::BN - 1) / WgradTile::BN)),
+                      kNumXcd));
     return bf16_out ? launch_dense<WgradTile, kOutBF16, false>(p, stream)
                     : launch_dense<WgradTile, kOutF32, false>(p, stream);
 }
@@ -1723,6 +1775,9 @@ hipError_t launch_grouped_gemm(const void *a, const float *sa, const void *w, co
     p.ksplit = 1;
     p.kb_per_split = p.G;
     const dim3 grid(round_up(p.ntiles, kNumXcd));
+    log_plan(pow2 ? "block_grouped_gemm_pow2" : "block_grouped_gemm", T, N, K,
+             "128x256 (tiles found on the device; grid sized for the worst case)", 0, 0, 1,
+             (int)grid.x);
     if (pow2) {
         if (bf16_out)
             hipLaunchKernelGGL((grouped_gemm_kernel<C, kOutBF16, true>), grid, dim3(C::kThreads),
@@ -1762,6 +1817,7 @@ hipError_t launch_block_gemm_fused_quant(const void *x, const void *w, const flo
     p.ntiles = p.tiles_m * p.tiles_n;
     p.group_m = 8;
     const dim3 grid(round_up(p.ntiles, kNumXcd));
+    log_plan("block_gemm_fused_quant", M, N, K, "32x256", 0, 0, 1, (int)grid.x);
     if (bf16_out)
         hipLaunchKernelGGL(fused_quant_gemm_kernel<kOutBF16>, grid, dim3(C::kThreads), 0, stream,
                            p);
@@ -1798,6 +1854,7 @@ hipError_t launch_block_gemm_dgrad(const void *dy, const float *sdy, const void 
     p.ksplit = pl.ksplit;
     p.kb_per_split = pl.kb_per_split;
     p.partial = static_cast<float *>(workspace);
+    log_dense_plan("block_gemm_dgrad (W read transposed)", p, pl);
     if (pl.big && pl.tn2 > 0) {
         // the forward GEMM's two tile widths (see block_gemm)
         p.tiles_m = (int)((p.M + 255) / 256);

@@ -41,6 +41,10 @@
  *   - Sizes of zero (M = 0, T = 0, K = 0 for the quantizers) are valid no-ops.
  *   - Inputs must be finite; NaN/Inf inputs are outside the contract and are
  *     not checked.
+ *   - Diagnostics: with the environment variable FP8BLK_LOG set (to anything
+ *     but "" or "0") when the library first launches a GEMM, every GEMM call
+ *     prints the plan it launches on stderr (entry, sizes, tile shapes, K
+ *     splits, grid).  The variable is read once per process.
  */
 #ifndef FP8BLK_H_
 #define FP8BLK_H_
