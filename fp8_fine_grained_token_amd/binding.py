@@ -24,7 +24,9 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "_build", "libfp8blk.so")
+# FP8BLK_LIB may name another build of the same library (the race-check
+# build _build/libfp8blk_poison.so); by default the released one loads.
+LIB_PATH = os.environ.get("FP8BLK_LIB") or os.path.join(HERE, "_build", "libfp8blk.so")
 
 FP8_OK = 0
 FP8_ERR_NULL = 1

@@ -4,6 +4,11 @@
 
 hipcc cross-compiles for gfx950 without a GPU.  Flags: -O3, C++17, no fast
 math, explicit FMAs only (-ffp-contract=off), packed-FP32 instructions off.
+
+It also builds _build/libfp8blk_poison.so, the same sources with
+FP8BLK_POISON_LDS defined (every LDS-DMA copy first poisons its destination):
+a race-check build that tests load through FP8BLK_LIB; the product path loads
+libfp8blk.so.
 """
 from __future__ import annotations
 
@@ -16,6 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(BUILD_DIR, "libfp8blk.so")
+POISON_LIB_PATH = os.path.join(BUILD_DIR, "libfp8blk_poison.so")
 ARCH = "gfx950"
 
 
@@ -28,22 +34,35 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libfp8blk.so (always rebuilds)."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [
+def _command(out: str, defines) -> list:
+    return [
         hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
         "-ffp-contract=off", "-fno-gpu-rdc", "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",
         "-I" + os.path.join(os.path.dirname(HERE), "include"),
-        "-o", tmp,
-    ] + sources()
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
+    ] + ["-D" + d for d in defines] + ["-o", out] + sources()
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libfp8blk.so and the race-check
+    libfp8blk_poison.so (always rebuilds; the two compile in parallel)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = []
+    for path, defines in ((LIB_PATH, []), (POISON_LIB_PATH, ["FP8BLK_POISON_LDS"])):
+        tmp = path + ".tmp%d" % os.getpid()
+        cmd = _command(tmp, defines)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((subprocess.Popen(cmd), tmp, path, cmd))
+    failed = None
+    for proc, tmp, path, cmd in jobs:
+        if proc.wait() != 0 and failed is None:
+            failed = subprocess.CalledProcessError(proc.returncode, cmd)
+    if failed is not None:
+        raise failed
+    for proc, tmp, path, cmd in jobs:
+        os.replace(tmp, path)
     return LIB_PATH
 
 

@@ -241,7 +241,27 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) {
 // sets the LDS address, issues the load (which takes M0 at issue: copies
 // back to back with different addresses land where they should) and puts
 // the old value back.
+//
+// Race-check builds (FP8BLK_POISON_LDS defined): before each copy the wave
+// first fills the LDS bytes the copy will write with 0x7F (an E4M3 NaN;
+// 3.4e38 as an fp32 scale) and waits for those writes.  A wave that still
+// read a stage after another wave began to refill it would then see poison
+// at once, instead of the old data that a copy still in flight has not yet
+// overwritten, and its outputs would be wrong.  Released builds leave this
+// out.
+#ifdef FP8BLK_POISON_LDS
+__device__ __forceinline__ void poison_lds(uint32_t lds, int bytes_per_lane) {
+    typedef __attribute__((address_space(3))) uint32_t *lds_u32_t;
+    lds_u32_t p = (lds_u32_t)(uintptr_t)(lds + (uint32_t)(bytes_per_lane * (threadIdx.x & 63)));
+    for (int i = 0; i < bytes_per_lane / 4; ++i) p[i] = 0x7F7F7F7Fu;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+#define FP8BLK_POISON(lds, bytes) poison_lds(lds, bytes)
+#else
+#define FP8BLK_POISON(lds, bytes) ((void)0)
+#endif
 __device__ __forceinline__ void copy16(const v4i &r, uint32_t voff, uint32_t soff, uint32_t lds) {
+    FP8BLK_POISON(lds, 16);
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\t"
@@ -257,6 +277,7 @@ __device__ __forceinline__ void copy16(const v4i &r, uint32_t voff, uint32_t sof
 // the default policy.
 __device__ __forceinline__ void copy16_nt(const v4i &r, uint32_t voff, uint32_t soff,
                                           uint32_t lds) {
+    FP8BLK_POISON(lds, 16);
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\t"
@@ -266,6 +287,7 @@ __device__ __forceinline__ void copy16_nt(const v4i &r, uint32_t voff, uint32_t 
         : "memory");
 }
 __device__ __forceinline__ void copy4(const v4i &r, uint32_t voff, uint32_t soff, uint32_t lds) {
+    FP8BLK_POISON(lds, 4);
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\t"
