@@ -70,9 +70,16 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def code_hash(path):
+    """sha256 of a C/C++/HIP source with its comments removed and its blank
+    space collapsed: it changes when the code changes, not when only its
+    comments do."""
+    import re
+    with open(path, encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
 def dense_gemm_bytes(m, n, k, out_bytes=2):
@@ -85,13 +92,13 @@ def quant_bytes(m, k):
 
 def traffic_from_counters():
     """HBM bytes per GEMM launch from the committed counter summary, or None
-    when it is missing or was taken on a different gemm.hip."""
+    when it is missing or was taken on different gemm.hip code."""
     try:
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("gemm_source_sha256") != source_hash(GEMM_SOURCE):
+    if c.get("gemm_code_sha256") != code_hash(GEMM_SOURCE):
         return None
     return c.get("hbm_bytes_per_launch")
 
