@@ -328,10 +328,12 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=None):
             wq, ws = F.fp8_quant_weight_128x128(
                 to_dev_bf16(torch, I.weights(np.random.default_rng(n), (n, K))))
             cn = torch.empty((M, n), dtype=torch.bfloat16, device="cuda")
+            # each path in its best configuration: with the split-K
+            # workspace it asks for (small N)
+            nf = F.fp8_fused_quant_workspace_bytes(M, n, K, "bf16")
+            fws = torch.empty(nf, dtype=torch.uint8, device="cuda") if nf else None
             ms_f, _ = P.timed(lambda: F.fp8_block_gemm_fused_quant(X, wq, ws, out_dtype="bf16",
-                                                                   c=cn))
-            # the two-call path in its best configuration: with the split-K
-            # workspace its GEMM asks for (small N)
+                                                                   c=cn, workspace=fws))
             nb = F.fp8_gemm_workspace_bytes(M, n, K, "bf16")
             gws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
 
@@ -341,13 +343,14 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=None):
             ms_t, _ = P.timed(two_call)
             rows.append({"N": n, "fused_us": round(ms_f * 1e3, 2),
                          "two_call_us": round(ms_t * 1e3, 2),
+                         "fused_split_k_workspace_bytes": nf,
                          "two_call_split_k_workspace_bytes": nb,
                          "fused_faster": ms_f < ms_t})
-            del wq, ws, cn, gws
+            del wq, ws, cn, gws, fws
         P.out["fused_quant_crossover_m4096_k7168"] = {
             "rows": rows, "note": "M=4096, K=7168, bf16 out; each launch (or pair) after a "
-                                  "512 MB cache flush; median of 50; the two-call GEMM "
-                                  "gets the split-K workspace it asks for"}
+                                  "512 MB cache flush; median of 50; both paths get the "
+                                  "split-K workspaces they ask for"}
 
     # backward of the same layer: dY [4096][7168] (same distribution as X
     # without outliers); Dgrad = forward GEMM with the transposed weights,

@@ -57,7 +57,8 @@ _SIGNATURES = {
     "fp8_block_gemm_dgrad": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P,
                               ctypes.c_size_t, _P], ctypes.c_int),
     "fp8_block_gemm_fused_quant": ([_P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, _P,
-                                    _P], ctypes.c_int),
+                                    _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "fp8_fused_quant_workspace_bytes": ([_I64, _I64, _I64, ctypes.c_int], ctypes.c_size_t),
     "fp8_block_gemm_noalloc": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P],
                                ctypes.c_int),
     "fp8_quant_act_1x128_pow2": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
@@ -217,6 +218,11 @@ def fp8_gemm_workspace_bytes(M: int, N: int, K: int, out_dtype="bf16") -> int:
     return int(lib().fp8_gemm_workspace_bytes(M, N, K, code))
 
 
+def fp8_fused_quant_workspace_bytes(M: int, N: int, K: int, out_dtype="bf16") -> int:
+    code, _ = _out_code(out_dtype)
+    return int(lib().fp8_fused_quant_workspace_bytes(M, N, K, code))
+
+
 def _workspace_args(workspace):
     if workspace is None:
         return ctypes.c_void_p(0), 0
@@ -282,11 +288,13 @@ def fp8_block_gemm_dgrad(dy, sdy, w, sw, out_dtype="bf16", dx=None, workspace=No
 
 
 def fp8_block_gemm_fused_quant(x, w, sw, out_dtype="bf16", c=None, q_out=None, sa_out=None,
-                               return_quantized=False, stream=None):
+                               return_quantized=False, workspace=None, stream=None):
     """C[M][N] = fp8_block_gemm(fp8_quant_act_1x128(x), w, sw) with the 1x128
     quantization of the bf16 activations x [M][K] done inside the GEMM.
     With return_quantized (or q_out / sa_out given) the E4M3 bytes [M][K]
-    and scales [M][K/128] are written too and (c, q, sa) is returned."""
+    and scales [M][K/128] are written too and (c, q, sa) is returned.  A
+    workspace of fp8_fused_quant_workspace_bytes(M, N, K) bytes enables the
+    split-K path for small M x N."""
     torch = _torch()
     _rank(x, "x", 2)
     _rank(w, "w", 2)
@@ -310,10 +318,11 @@ def fp8_block_gemm_fused_quant(x, w, sw, out_dtype="bf16", c=None, q_out=None, s
         qp, sp = _dev(q_out, "q_out", torch.uint8), _dev(sa_out, "sa_out", torch.float32)
     else:
         qp, sp = ctypes.c_void_p(0), ctypes.c_void_p(0)
+    wp, wb = _workspace_args(workspace)
     fn = "fp8_block_gemm_fused_quant"
     _check(getattr(lib(), fn)(_dev(x, "x", torch.bfloat16), _dev(w, "w", torch.uint8),
                               _dev(sw, "sw", torch.float32), _dev(c, "c", tdt), code, M, N, K,
-                              qp, sp, _stream_handle(stream)), fn)
+                              qp, sp, wp, wb, _stream_handle(stream)), fn)
     return (c, q_out, sa_out) if want_q else c
 
 

@@ -174,11 +174,13 @@ fp8_status fp8_block_gemm_dgrad(const void *dy_e4m3, const float *dy_scales,
 fp8_status fp8_block_gemm_fused_quant(const void *x_bf16, const void *w_e4m3,
                                       const float *w_scales, void *c, int out_dtype, int64_t M,
                                       int64_t N, int64_t K, void *q_e4m3_out,
-                                      float *a_scales_out, void *hip_stream) {
+                                      float *a_scales_out, void *workspace,
+                                      size_t workspace_bytes, void *hip_stream) {
     // the activation scales are produced here: pass a valid placeholder for
     // the common checks (x stands in for a and sa)
     fp8_status st = check_gemm_common(x_bf16, static_cast<const float *>(x_bf16), w_e4m3,
-                                      w_scales, c, out_dtype, M, N, K, nullptr, 0);
+                                      w_scales, c, out_dtype, M, N, K, workspace,
+                                      workspace_bytes);
     if (st != FP8_OK || M == 0 || N == 0) return st;
     if (K == 0) return FP8_ERR_SHAPE;
     if ((q_e4m3_out == nullptr) != (a_scales_out == nullptr)) return FP8_ERR_NULL;
@@ -187,7 +189,7 @@ fp8_status fp8_block_gemm_fused_quant(const void *x_bf16, const void *w_e4m3,
     clear_last_error();
     return from_hip(fp8blk::launch_block_gemm_fused_quant(
         x_bf16, w_e4m3, w_scales, c, out_dtype == FP8_OUT_BF16, M, N, K, q_e4m3_out,
-        a_scales_out, as_stream(hip_stream)));
+        a_scales_out, workspace, workspace_bytes, as_stream(hip_stream)));
 }
 
 fp8_status fp8_block_gemm_noalloc(const void *a_e4m3, const float *a_scales,
@@ -275,6 +277,12 @@ size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int out_dtype) 
     if (out_dtype != FP8_OUT_F32 && out_dtype != FP8_OUT_BF16) return 0;
     if (M <= 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return 0;
     return fp8blk::gemm_workspace_bytes(M, N, K);
+}
+
+size_t fp8_fused_quant_workspace_bytes(int64_t M, int64_t N, int64_t K, int out_dtype) {
+    if (out_dtype != FP8_OUT_F32 && out_dtype != FP8_OUT_BF16) return 0;
+    if (M <= 0 || N <= 0 || K <= 0 || N % 128 != 0 || K % 128 != 0) return 0;
+    return fp8blk::fused_quant_workspace_bytes(M, N, K);
 }
 
 const char *fp8_status_string(fp8_status s) {

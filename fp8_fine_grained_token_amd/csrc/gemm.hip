@@ -1298,22 +1298,25 @@ __global__ __launch_bounds__(C::kThreads) void grouped_gemm_kernel(GemmParams p)
 // pays where few N tiles share an A tile; where many do, the standalone
 // quantizer plus the plain GEMM is faster.
 //
-// Tile 32 x 256 on 8 waves (2 x 4, wave tile 16 x 64).  Per K block each
-// wave copies 4 bf16 rows (one 1 KiB copy) and the W tile's 4 rows groups;
-// it quantizes exactly the 4 rows it copied, so the bf16 tile needs no
-// barrier.  Pipeline: W in three stages (copies two blocks ahead), bf16 A in
-// three stages (three blocks ahead, since block kb + 1 is quantized while
-// block kb is multiplied), E4M3 A and its scales double buffered.
+// Tile 64 x 256 on 8 waves (2 x 4, wave tile 32 x 64).  Per K block each
+// wave copies 8 bf16 rows (two 1 KiB copies) and a quarter of the W tile; it
+// quantizes exactly the 8 rows it copied, so the bf16 tile needs no barrier.
+// Pipeline: bf16 A, streamed from HBM, in three stages (copies two blocks
+// ahead of their quantization, which runs one block ahead of the MFMAs); W,
+// re-read by every M tile and mostly an L2 hit, in two stages (one block
+// ahead); E4M3 A and its scales double buffered.
+// When the tiles alone would not fill the CUs, K is split over workgroups
+// as in the plain GEMM (partials in the caller's workspace, then the fixed-
+// order reduction).
 struct FusedCfg {
-    static constexpr int BM = 32, BN = 256;
+    static constexpr int BM = 64, BN = 256;
     static constexpr int kWavesM = 2, kWavesN = 4, kWaves = 8, kThreads = 512;
     static constexpr int WM = BM / kWavesM, WN = BN / kWavesN;
     static constexpr int kTM = WM / 16, kTN = WN / 16;
-    static constexpr int kStagesW = 3, kStagesA = 3;
+    static constexpr int kStagesW = 2, kStagesA = 3;
     static constexpr int kWLoads = BN / 8 / kWaves;            // 8 rows of 128 B per copy
     static constexpr int kALoads = BM * 256 / 1024 / kWaves;   // 4 rows of 256 B per copy
-    static constexpr int kCopiesPerBatch = kWLoads + 1 + kALoads;  // + weight scales
-    static_assert(kALoads == 1, "each wave copies the bf16 rows it quantizes");
+    static_assert(kALoads == 2, "each wave copies the 8 bf16 rows it quantizes");
     static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns in one weight-scale block");
 };
 
@@ -1331,10 +1334,14 @@ __global__ __launch_bounds__(FusedCfg::kThreads) void fused_quant_gemm_kernel(Ge
     __shared__ FusedLds L;
     const int logical = xcd_logical_tile();
     if (logical >= p.ntiles) return;
+    const int per_split = p.tiles_m * p.tiles_n;
+    const int ks = logical / per_split;
     int tm, tn;
-    raster(logical, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+    raster(logical - ks * per_split, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int64_t K = p.K;
     const int G = p.G;
+    const int kb0 = ks * p.kb_per_split;
+    const int kb1 = min(kb0 + p.kb_per_split, G);
     const int64_t row0 = (int64_t)tm * C::BM, n0 = (int64_t)tn * C::BN;
     const int64_t ra = p.M - row0 < C::BM ? p.M - row0 : C::BM;
     const int64_t cw = p.N - n0 < C::BN ? p.N - n0 : C::BN;
@@ -1356,67 +1363,81 @@ __global__ __launch_bounds__(FusedCfg::kThreads) void fused_quant_gemm_kernel(Ge
     const uint32_t w_voff = (uint32_t)(8 * wave * K + (lane >> 3) * K +
                                        (((lane & 7) ^ ((lane >> 3) & 7) ^ (wave & 1)) << 4));
     const uint32_t w_rowstep = (uint32_t)(64 * K);
-    // bf16 copy of wave v: rows 4 v + L / 16, 16-byte chunk L % 16.
+    // bf16 copy t of wave v: rows 4 (v + 8 t) + L / 16, 16-byte chunk L % 16
+    // (1 KiB of the stage from byte 1024 (v + 8 t)).
     const uint32_t a_voff = (uint32_t)((4 * wave + (lane >> 4)) * 2 * K + (lane & 15) * 16);
+    const uint32_t a_rowstep = (uint32_t)(32 * 2 * K);
     const uint32_t lds_w0 = lds_addr(&L.w[0][1024 * wave]);
     const uint32_t lds_a0 = lds_addr(&L.a16[0][1024 * wave]);
     const uint32_t lds_sw0 = lds_addr(&L.sw[0][0]);
     const uint32_t sw_voff = (uint32_t)(lane * G * 4);
 
-    // one batch: W and weight scales of block kw, bf16 A of block ka
-    auto issue_batch = [&](int kw, int ka) {
-        const bool win = kw < G, ain = ka < G;
-        const v4i &w_r = win ? rw : rw0;
-        const v4i &s_r = win ? rsw : rsw0;
-        const v4i &a_r = ain ? rx : rx0;
-        const int kwc = win ? kw : 0, kac = ain ? ka : 0;
-        const uint32_t sw_st = (uint32_t)((kw % C::kStagesW) * sizeof(L.w[0]));
+    // bf16 A of block k (this wave's 8 rows); the W tile and weight scales
+    // of block k.  Blocks past the split read from empty views, so every
+    // iteration issues the same copies.
+    auto issue_a = [&](int k) {
+        const bool in = k < kb1;
+        const v4i &a_r = in ? rx : rx0;
+        const int kc = in ? k : kb0;
+        const uint32_t a_st = (uint32_t)((k % C::kStagesA) * sizeof(L.a16[0]));
+#pragma unroll
+        for (int t = 0; t < C::kALoads; ++t)
+            copy16(a_r, a_voff + t * a_rowstep, (uint32_t)kc * 256u,
+                   lds_a0 + a_st + 1024u * C::kWaves * t);
+    };
+    auto issue_w = [&](int k) {
+        const bool in = k < kb1;
+        const v4i &w_r = in ? rw : rw0;
+        const v4i &s_r = in ? rsw : rsw0;
+        const int kc = in ? k : kb0;
+        const uint32_t w_st = (uint32_t)((k % C::kStagesW) * sizeof(L.w[0]));
 #pragma unroll
         for (int t = 0; t < C::kWLoads; ++t)
-            copy16_nt(w_r, w_voff + t * w_rowstep, (uint32_t)kwc * 128u,
-                      lds_w0 + sw_st + 1024u * C::kWaves * t);
-        copy4(s_r, sw_voff, (uint32_t)kwc * 4u,
-              lds_sw0 + (uint32_t)((kw % C::kStagesW) * sizeof(L.sw[0])));
-        copy16(a_r, a_voff, (uint32_t)kac * 256u,
-               lds_a0 + (uint32_t)((ka % C::kStagesA) * sizeof(L.a16[0])));
+            copy16_nt(w_r, w_voff + t * w_rowstep, (uint32_t)kc * 128u,
+                      lds_w0 + w_st + 1024u * C::kWaves * t);
+        copy4(s_r, sw_voff, (uint32_t)kc * 4u,
+              lds_sw0 + (uint32_t)((k % C::kStagesW) * sizeof(L.sw[0])));
     };
 
-    // Quantize block kb from its bf16 stage (this wave's 4 rows) into E4M3
+    // Quantize block kb from its bf16 stage (this wave's 8 rows) into E4M3
     // buffer kb % 2 and its scales; rows past M quantize to zero bytes.
     auto quant = [&](int kb) {
-        const int r = 4 * wave + (lane >> 4), j = lane & 15;
-        const bool in = row0 + r < p.M;
-        const uint4 v = *reinterpret_cast<const uint4 *>(
-            &L.a16[kb % C::kStagesA][r * 256 + j * 16]);
-        float f[8];
-        unpack8(v, f);
-        const float amax = row16_max(absmax8(f));
-        float y[8], s;
-        if (__all(!in || amax >= 0x1p-60f)) {
-            s = in ? scale_fast(amax) : 1.0f;
-            const float rc = 1.0f / s;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) y[i] = quot_fast(f[i], s, rc);
-        } else {
-            const QuotientCtx qc(amax, false);
-            s = qc.s;
+        for (int t = 0; t < C::kALoads; ++t) {
+            const int r = 4 * (wave + C::kWaves * t) + (lane >> 4), j = lane & 15;
+            const bool in = row0 + r < p.M;
+            const uint4 v = *reinterpret_cast<const uint4 *>(
+                &L.a16[kb % C::kStagesA][r * 256 + j * 16]);
+            float f[8];
+            unpack8(v, f);
+            const float amax = row16_max(absmax8(f));
+            float y[8], s;
+            if (__all(!in || amax >= 0x1p-60f)) {
+                s = in ? scale_fast(amax) : 1.0f;
+                const float rc = 1.0f / s;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) y[i] = qc(f[i]);
-        }
-        if (!in) s = 0.0f;
-        uint32_t lo = 0, hi = 0;
-        lo = cvt_pk_e4m3<false>(y[0], y[1], lo);
-        lo = cvt_pk_e4m3<true>(y[2], y[3], lo);
-        hi = cvt_pk_e4m3<false>(y[4], y[5], hi);
-        hi = cvt_pk_e4m3<true>(y[6], y[7], hi);
-        const int chunk = (j >> 1) ^ swz_key(r);
-        *reinterpret_cast<uint2 *>(&L.a8[kb & 1][r * 128 + chunk * 16 + (j & 1) * 8]) =
-            make_uint2(lo, hi);
-        if (j == 0) L.sa[kb & 1][r] = s;
-        if (write_q && in) {
-            *reinterpret_cast<uint2 *>(p.q_out + (row0 + r) * K + (int64_t)kb * 128 + 8 * j) =
+                for (int i = 0; i < 8; ++i) y[i] = quot_fast(f[i], s, rc);
+            } else {
+                const QuotientCtx qc(amax, false);
+                s = qc.s;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] = qc(f[i]);
+            }
+            if (!in) s = 0.0f;
+            uint32_t lo = 0, hi = 0;
+            lo = cvt_pk_e4m3<false>(y[0], y[1], lo);
+            lo = cvt_pk_e4m3<true>(y[2], y[3], lo);
+            hi = cvt_pk_e4m3<false>(y[4], y[5], hi);
+            hi = cvt_pk_e4m3<true>(y[6], y[7], hi);
+            const int chunk = (j >> 1) ^ swz_key(r);
+            *reinterpret_cast<uint2 *>(&L.a8[kb & 1][r * 128 + chunk * 16 + (j & 1) * 8]) =
                 make_uint2(lo, hi);
-            if (j == 0) p.sa_out[(row0 + r) * G + kb] = s;
+            if (j == 0) L.sa[kb & 1][r] = s;
+            if (write_q && in) {
+                *reinterpret_cast<uint2 *>(p.q_out + (row0 + r) * K + (int64_t)kb * 128 + 8 * j) =
+                    make_uint2(lo, hi);
+                if (j == 0) p.sa_out[(row0 + r) * G + kb] = s;
+            }
         }
     };
 
@@ -1429,7 +1450,7 @@ __global__ __launch_bounds__(FusedCfg::kThreads) void fused_quant_gemm_kernel(Ge
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Block kb: W stage kb % 3, E4M3 A buffer kb % 2.  The MFMA takes the
+    // Block kb: W stage kb % 2, E4M3 A buffer kb % 2.  The MFMA takes the
     // weight fragment as its A operand, so lane L holds outputs n = 4 (L /
     // 16) + e, m = L % 16 of each 16 x 16 tile (see tile_mainloop).
     auto compute = [&](int kb) {
@@ -1456,27 +1477,36 @@ __global__ __launch_bounds__(FusedCfg::kThreads) void fused_quant_gemm_kernel(Ge
         }
     };
 
-    // Prologue: block 0's bf16 rows, quantized by each wave (its own rows:
-    // no barrier), then batches for W blocks 0, 1 and bf16 blocks 1, 2.
-    copy16(G > 0 ? rx : rx0, a_voff, 0u, lds_a0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    quant(0);
-    issue_batch(0, 1);
-    issue_batch(1, 2);
-    for (int kb = 0; kb < G; ++kb) {
-        // batch kb - 2 (W block kb, bf16 block kb + 1) has landed; batch
-        // kb - 1 may still be in flight
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::kCopiesPerBatch) : "memory");
+    // Prologue: bf16 A of block kb0, W and scales of block kb0, bf16 A of
+    // blocks kb0 + 1 and kb0 + 2; block kb0's rows are quantized by the wave
+    // that copied them (no barrier needed) once its two copies have landed.
+    issue_a(kb0);
+    issue_w(kb0);
+    issue_a(kb0 + 1);
+    issue_a(kb0 + 2);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::kWLoads + 1 + 2 * C::kALoads) : "memory");
+    quant(kb0);
+    for (int kb = kb0; kb < kb1; ++kb) {
+        // Iteration kb - 1 issued W(kb), its scales, then bf16 A(kb + 2):
+        // with only A(kb + 2) outstanding, W(kb) and the older A(kb + 1)
+        // have landed.
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::kALoads) : "memory");
         __syncthreads();
-        // W stage (kb + 2) % 3 was last read by block kb - 1 (every wave is
-        // past it); bf16 stage (kb + 3) % 3 holds block kb, quantized in the
-        // previous iteration by the wave that copies into it
-        issue_batch(kb + 2, kb + 3);
+        // W stage (kb + 1) % 2 was last read by block kb - 1 and bf16 stage
+        // (kb + 3) % 3 held block kb's rows, quantized in the previous
+        // iteration (every wave is past both)
+        issue_w(kb + 1);
+        issue_a(kb + 3);
         compute(kb);
-        if (kb + 1 < G) quant(kb + 1);
+        if (kb + 1 < kb1) quant(kb + 1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    tile_store_buf<C, OUT, true, sizeof(L.w)>(acc, &L.w[0][0], p.c, p.N, row0, p.M, n0, p.N);
+    if (p.ksplit > 1)
+        tile_store_buf<C, kOutF32, false, sizeof(L.w)>(acc, &L.w[0][0],
+                                                       p.partial + (int64_t)ks * p.M * p.N, p.N,
+                                                       row0, p.M, n0, p.N);
+    else
+        tile_store_buf<C, OUT, true, sizeof(L.w)>(acc, &L.w[0][0], p.c, p.N, row0, p.M, n0, p.N);
 }
 
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -1820,9 +1850,34 @@ hipError_t launch_grouped_gemm(const void *a, const float *sa, const void *w, co
     return hipGetLastError();
 }
 
+namespace {
+
+// K splits of the fused GEMM: as for the plain GEMM's small tiles, doubled
+// while the tiles times the splits still fit in the CUs and each split keeps
+// at least 4 K blocks.
+int fused_ksplit(int64_t M, int64_t N, int64_t K) {
+    using C = FusedCfg;
+    const int G = (int)(K / 128);
+    const int64_t tiles = ((M + C::BM - 1) / C::BM) * ((N + C::BN - 1) / C::BN);
+    int s = 1;
+    while (tiles * s * 2 <= kCUs && G / (s * 2) >= 4) s *= 2;
+    const int per = (G + s - 1) / s;
+    return (G + per - 1) / per;
+}
+
+}  // namespace
+
+size_t fused_quant_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0 || K <= 0) return 0;
+    const int s = fused_ksplit(M, N, K);
+    if (s <= 1) return 0;
+    return (size_t)s * (size_t)M * (size_t)N * sizeof(float);
+}
+
 hipError_t launch_block_gemm_fused_quant(const void *x, const void *w, const float *sw, void *c,
                                          bool bf16_out, int64_t M, int64_t N, int64_t K,
-                                         void *q_out, float *sa_out, hipStream_t stream) {
+                                         void *q_out, float *sa_out, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream) {
     using C = FusedCfg;
     GemmParams p{};
     p.x = static_cast<const uint16_t *>(x);
@@ -1838,16 +1893,35 @@ hipError_t launch_block_gemm_fused_quant(const void *x, const void *w, const flo
     p.NB = (int)(N / 128);
     p.tiles_m = (int)((M + C::BM - 1) / C::BM);
     p.tiles_n = (int)((N + C::BN - 1) / C::BN);
-    p.ntiles = p.tiles_m * p.tiles_n;
+    int s = fused_ksplit(M, N, K);
+    if (s > 1 && (workspace == nullptr || workspace_bytes < fused_quant_workspace_bytes(M, N, K)))
+        s = 1;
+    p.ksplit = s;
+    p.kb_per_split = (p.G + s - 1) / s;
+    p.partial = static_cast<float *>(workspace);
+    p.ntiles = p.tiles_m * p.tiles_n * s;
     p.group_m = 8;
     const dim3 grid(round_up(p.ntiles, kNumXcd));
-    log_plan("block_gemm_fused_quant", M, N, K, "32x256", 0, 0, 1, (int)grid.x);
+    log_plan("block_gemm_fused_quant", M, N, K,
+             s > 1 ? "64x256 split-K + reduction" : "64x256", 0, 0, s, (int)grid.x);
     if (bf16_out)
         hipLaunchKernelGGL(fused_quant_gemm_kernel<kOutBF16>, grid, dim3(C::kThreads), 0, stream,
                            p);
     else
         hipLaunchKernelGGL(fused_quant_gemm_kernel<kOutF32>, grid, dim3(C::kThreads), 0, stream,
                            p);
+    if (s > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t MN = M * N;
+        const int64_t blocks = (MN / 4 + 255) / 256;
+        if (bf16_out)
+            hipLaunchKernelGGL(splitk_reduce_kernel<kOutBF16>, dim3((unsigned)blocks), dim3(256),
+                               0, stream, p.partial, c, MN, s);
+        else
+            hipLaunchKernelGGL(splitk_reduce_kernel<kOutF32>, dim3((unsigned)blocks), dim3(256),
+                               0, stream, p.partial, c, MN, s);
+    }
     return hipGetLastError();
 }
 

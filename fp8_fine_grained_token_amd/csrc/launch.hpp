@@ -50,10 +50,14 @@ hipError_t launch_block_gemm_noalloc(const void *a, const float *sa, const void 
 
 // The block-scaled GEMM on bf16 activations x [M][K], quantized 1x128 inside
 // the GEMM; q_out / sa_out (both or neither) receive the E4M3 bytes and
-// scales the standalone quantizer would write.
+// scales the standalone quantizer would write.  K is split over workgroups
+// (partials in the workspace) when the workspace holds
+// fused_quant_workspace_bytes(M, N, K).
+size_t fused_quant_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_block_gemm_fused_quant(const void *x, const void *w, const float *sw, void *c,
                                          bool bf16_out, int64_t M, int64_t N, int64_t K,
-                                         void *q_out, float *sa_out, hipStream_t stream);
+                                         void *q_out, float *sa_out, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
 
 // Dgrad dX [M][Kx] = dY [M][N] W [N][Kx], W E4M3 with 128x128 block scales
 // [N/128][Kx/128] in its forward layout, read transposed in LDS.

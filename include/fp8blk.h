@@ -165,18 +165,24 @@ fp8_status fp8_block_grouped_gemm(const void *a_e4m3, const float *a_scales,
  *                 fp32: optional outputs (both NULL, or both given), which
  *                 receive exactly what fp8_quant_act_1x128 writes, e.g. to
  *                 keep the FP8 activations for the backward pass.
+ *   workspace / workspace_bytes: optional, as for fp8_block_gemm, with the
+ *                 size from fp8_fused_quant_workspace_bytes(); with it, K is
+ *                 split over workgroups when the output tiles alone would
+ *                 not fill the GPU.
  * The quantized values, the products and the accumulation are those of the
- * two-call path, so C is the same up to the FP32 summation order.  Every
- * 256-column tile of C quantizes its activation rows again, so this call is
- * the faster one only for small N (see the measured crossover in the
- * documentation); it uses no workspace.  Errors: as fp8_block_gemm, plus
- * FP8_ERR_NULL when only one of q_e4m3_out / a_scales_out is given, and
+ * two-call path, so C is the same up to the FP32 summation order (bitwise
+ * the same where both calls run the same K splits, e.g. both without a
+ * workspace).  Every 256-column tile of C quantizes its activation rows
+ * again, so this call is the faster one only for small and medium N (see
+ * the measured crossover in the documentation).  Errors: as fp8_block_gemm,
+ * plus FP8_ERR_NULL when only one of q_e4m3_out / a_scales_out is given, and
  * FP8_ERR_ALIGN for x_bf16 not 16-byte or q_e4m3_out not 8-byte aligned.
  */
 fp8_status fp8_block_gemm_fused_quant(const void *x_bf16, const void *w_e4m3,
                                       const float *w_scales, void *c, int out_dtype,
                                       int64_t M, int64_t N, int64_t K, void *q_e4m3_out,
-                                      float *a_scales_out, void *hip_stream);
+                                      float *a_scales_out, void *workspace,
+                                      size_t workspace_bytes, void *hip_stream);
 
 /*
  * Power-of-two-scale variants for the block-scaled matrix core (page
@@ -335,6 +341,10 @@ fp8_status fp8_block_gemm_dgrad(const void *dy_e4m3, const float *dy_scales,
 /* Workspace bytes that let fp8_block_gemm use its split-K path for this
  * shape (0 when the shape does not use it). */
 size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int out_dtype);
+
+/* The same for fp8_block_gemm_fused_quant (whose tiles, and so its splits,
+ * differ from fp8_block_gemm's). */
+size_t fp8_fused_quant_workspace_bytes(int64_t M, int64_t N, int64_t K, int out_dtype);
 
 /* Static, human-readable name of a status code. */
 const char *fp8_status_string(fp8_status s);

@@ -275,7 +275,8 @@ int main(int argc, char **argv) {
     /* ---- quantization fused into the GEMM, on the bf16 activations ---- */
     void *dqf = dev_alloc(M * K);
     float *dsf = dev_alloc(4 * M * G), *dcf = dev_alloc(4 * M * N), *dcn = dev_alloc(4 * M * N);
-    st = fp8_block_gemm_fused_quant(dx, dqw, dsw, dcf, FP8_OUT_F32, M, N, K, dqf, dsf, stream);
+    st = fp8_block_gemm_fused_quant(dx, dqw, dsw, dcf, FP8_OUT_F32, M, N, K, dqf, dsf, NULL, 0,
+                                    stream);
     /* ---- the no-allocation GEMM: its own static scratch for split-K ---- */
     if (st == FP8_OK)
         st = fp8_block_gemm_noalloc(dqa, dsa, dqw, dsw, dcn, FP8_OUT_F32, M, N, K, stream);
@@ -325,7 +326,7 @@ int main(int argc, char **argv) {
     const double dgrad_rel_fro = rel_fro_of(dxh, Rd, M * K);
     fails += !(dgrad_rel_fro <= 1e-3);
     const int err_fused = fp8_block_gemm_fused_quant(dx, dqw, dsw, dcf, FP8_OUT_F32, M, N, K, dqf,
-                                                     NULL, stream) == FP8_ERR_NULL;
+                                                     NULL, NULL, 0, stream) == FP8_ERR_NULL;
     const int err_dgrad = fp8_block_gemm_dgrad(dqdy, dsdy, dqw, dsw, ddx, FP8_OUT_F32, M, 200, K,
                                                NULL, 0, stream) == FP8_ERR_SHAPE;
     fails += !err_fused + !err_dgrad;

@@ -82,6 +82,16 @@ def run_cases():
     keep("fused", c)
     keep("fused_q", q)
     keep("fused_s", s)
+    # ... and with its split-K workspace (4 splits of 1024 x 256 x 2304)
+    x = act(12, 1024, 2304)
+    qw, sw = F.fp8_quant_weight_128x128(wts(13, 256, 2304))
+    nf = F.fp8_fused_quant_workspace_bytes(1024, 256, 2304, "f32")
+    assert nf > 0
+    fws = torch.empty(nf, dtype=torch.uint8, device="cuda")
+    c, q, s = F.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype="f32", return_quantized=True,
+                                           workspace=fws)
+    keep("fused_split_k", c)
+    keep("fused_split_k_q", q)
     # Dgrad on the forward weights: two tile widths, and split-K for small M
     for name, (m, n, kx), split in [("dgrad_two_kind", (4096, 512, 7168), False),
                                     ("dgrad_split_k", (64, 1024, 2048), True)]:

@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
         method + [m + "_pow2" for m in method]
         + ["fp8_quant_act_128x1_t", "fp8_transpose_weight_128x128", "fp8_block_gemm_wgrad"]
         + ["fp8_gemm_workspace_bytes", "fp8_status_string", "fp8_block_gemm_noalloc",
-           "fp8_block_gemm_fused_quant", "fp8_block_gemm_dgrad"])
+           "fp8_block_gemm_fused_quant", "fp8_fused_quant_workspace_bytes",
+           "fp8_block_gemm_dgrad"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -160,8 +161,9 @@ def test_dgrad_argument_errors():
 def test_fused_quant_gemm_argument_errors():
     lib = B.lib()
 
-    def fq(x=A16, w=A16, sw=A16, c=A16, dt=B.FP8_OUT_BF16, M=128, N=256, K=512, q=NUL, s=NUL):
-        return lib.fp8_block_gemm_fused_quant(x, w, sw, c, dt, M, N, K, q, s, NUL)
+    def fq(x=A16, w=A16, sw=A16, c=A16, dt=B.FP8_OUT_BF16, M=128, N=256, K=512, q=NUL, s=NUL,
+           ws=NUL, wsb=0):
+        return lib.fp8_block_gemm_fused_quant(x, w, sw, c, dt, M, N, K, q, s, ws, wsb, NUL)
     assert fq(K=500) == B.FP8_ERR_SHAPE
     assert fq(N=200) == B.FP8_ERR_SHAPE
     assert fq(M=-1) == B.FP8_ERR_SHAPE
@@ -176,7 +178,25 @@ def test_fused_quant_gemm_argument_errors():
     assert fq(q=ctypes.c_void_p(0x10004), s=A16) == B.FP8_ERR_ALIGN
     assert fq(q=A8, s=ctypes.c_void_p(0x10002)) == B.FP8_ERR_ALIGN
     assert fq(K=0) == B.FP8_ERR_SHAPE
+    assert fq(ws=A16, wsb=0) == B.FP8_ERR_WORKSPACE      # pointer without a size
+    assert fq(ws=NUL, wsb=256) == B.FP8_ERR_WORKSPACE    # size without a pointer
+    assert fq(ws=ctypes.c_void_p(0x10010), wsb=256) == B.FP8_ERR_WORKSPACE  # not 256-aligned
     assert fq(M=0, x=NUL, c=NUL) == B.FP8_OK
+
+
+def test_fused_quant_workspace_bytes():
+    # the fused GEMM's 64 x 256 tiles split K while tiles x splits fit in 256
+    # CUs and every split keeps 4 K blocks; its partials are FP32 [S][M][N]
+    lib = B.lib()
+    ws = lib.fp8_fused_quant_workspace_bytes
+    assert ws(4096, 256, 7168, B.FP8_OUT_BF16) == 4 * 4096 * 256 * 4   # 64 tiles -> 4 splits
+    assert ws(4096, 512, 7168, B.FP8_OUT_F32) == 2 * 4096 * 512 * 4    # 128 tiles -> 2 splits
+    assert ws(4096, 1024, 7168, B.FP8_OUT_BF16) == 0                   # 256 tiles fill the CUs
+    assert ws(64, 256, 512, B.FP8_OUT_BF16) == 0                       # K too short to split
+    assert ws(64, 256, 1024, B.FP8_OUT_BF16) == 2 * 64 * 256 * 4
+    assert ws(0, 256, 1024, B.FP8_OUT_BF16) == 0
+    assert ws(64, 200, 1024, B.FP8_OUT_BF16) == 0
+    assert ws(64, 256, 1024, 7) == 0
 
 
 def test_noalloc_gemm_argument_errors():

@@ -41,12 +41,21 @@ def assert_bytes_and_scales(qg, sg, qo, so, what):
     assert nbad == 0 and sbad == 0
 
 
-def run_case(a_bits, w_bits, out, rows=None, what=""):
+def fused_workspace(M, N, K):
+    nb = B.fp8_fused_quant_workspace_bytes(M, N, K, "f32")
+    return torch().empty(nb, dtype=torch().uint8, device="cuda") if nb else None
+
+
+def run_case(a_bits, w_bits, out, rows=None, what="", split=False):
     qw, sw = oracle.quant_weight_128x128(w_bits)
     qa, sa = oracle.quant_act_1x128(a_bits)
     x = dev_bf16(a_bits)
+    M, K = a_bits.shape
+    ws = fused_workspace(M, w_bits.shape[0], K) if split else None
+    if split:
+        assert ws is not None, "shape has no split-K plan"
     c, q, s = B.fp8_block_gemm_fused_quant(x, dev(qw), dev(sw), out_dtype=out,
-                                           return_quantized=True)
+                                           return_quantized=True, workspace=ws)
     assert_bytes_and_scales(host(q), host(s), qa, sa, f"{what} quantized activations")
     if rows is None:
         rows = np.arange(a_bits.shape[0])
@@ -60,7 +69,7 @@ def run_case(a_bits, w_bits, out, rows=None, what=""):
 @pytest.mark.parametrize("N,K", [(128, 128), (256, 640), (384, 1280)])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_fused_ragged(M, N, K, out):
-    # ragged M (partial 32-row tiles), N of one, one or two 256-column tiles
+    # ragged M (partial 64-row tiles), N of one, one or two 256-column tiles
     # (384: the second tile half full), K of 1, 5 and 10 blocks
     g = I.gemm_inputs(M, N, K, seed=M * 7 + N + K, outlier_frac=0.01, outlier_mult=50.0)
     run_case(g.a_bf16, g.w_bf16, out, what=f"{M}x{N}x{K}")
@@ -106,13 +115,60 @@ def test_fused_workload_shapes(N):
     # M = 4096, K = 7168: N = 256 (one N tile: every activation tile is
     # quantized once, e.g. a router's 256 experts) and the dense layer's
     # N = 7168; the quantized activations in full, C on rows of every
-    # 32-row tile, all columns
+    # 64-row tile, all columns
     M, K = 4096, 7168
     x_bits, _ = I.config_quant(seed=0)
     w_bits = I.weights(np.random.default_rng(N), (N, K))
-    rows = tile_rows(M, 32, per_tile=1)
+    rows = tile_rows(M, 64, per_tile=1)
     log(f"  fused {M}x{N}x{K}: oracle on {rows.size} rows ...")
     run_case(x_bits, w_bits, "bf16", rows=rows, what=f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,splits", [(300, 512, 2304, 4), (64, 256, 1024, 2)])
+def test_fused_split_k_equals_two_call_split_k_fp32(M, N, K, splits):
+    # with their workspaces both calls split K the same way here (same
+    # number of splits and K blocks per split), so the FP32 outputs agree
+    # bit for bit: the same bytes, block products, promotion and reduction
+    # order
+    g = I.gemm_inputs(M, N, K, seed=M + N, outlier_frac=0.01, outlier_mult=50.0)
+    t = torch()
+    x = dev_bf16(g.a_bf16)
+    qw, sw = B.fp8_quant_weight_128x128(dev_bf16(g.w_bf16))
+    qa, sa = B.fp8_quant_act_1x128(x)
+    nb = B.fp8_gemm_workspace_bytes(M, N, K, "f32")
+    nf = B.fp8_fused_quant_workspace_bytes(M, N, K, "f32")
+    assert nb == nf == splits * M * N * 4
+    c2 = B.fp8_block_gemm(qa, sa, qw, sw, out_dtype="f32",
+                          workspace=t.empty(nb, dtype=t.uint8, device="cuda"))
+    c1, q1, s1 = B.fp8_block_gemm_fused_quant(
+        x, qw, sw, out_dtype="f32", return_quantized=True,
+        workspace=t.empty(nf, dtype=t.uint8, device="cuda"))
+    t.cuda.synchronize()
+    assert t.equal(q1, qa) and t.equal(s1.view(t.int32), sa.view(t.int32))
+    log(f"  fused split-K ({splits}) vs two-call split-K FP32: max |diff| = "
+        f"{(c1 - c2).abs().max().item():.3e}")
+    assert t.equal(c1, c2)
+
+
+@pytest.mark.parametrize("N", [256, 512])
+def test_fused_split_k_workload_rows_of_every_tile(N):
+    # M = 4096, K = 7168 with the workspace: 4 splits for N = 256, 2 for
+    # N = 512; bytes and scales in full against the oracle, C (bf16) on a
+    # row of every 64-row tile, all columns, within the per-output bound
+    M, K = 4096, 7168
+    x_bits, _ = I.config_quant(seed=1)
+    w_bits = I.weights(np.random.default_rng(N + 1), (N, K))
+    rows = tile_rows(M, 64, per_tile=1)
+    log(f"  fused split-K {M}x{N}x{K}: oracle on {rows.size} rows ...")
+    run_case(x_bits, w_bits, "bf16", rows=rows, what=f"split-K {M}x{N}x{K}", split=True)
+
+
+@pytest.mark.parametrize("M", [1, 63, 65, 200])
+def test_fused_split_k_ragged_fp32(M):
+    # ragged 64-row tiles with K split (G = 18: splits of 5, 5, 5 and 3 K
+    # blocks), FP32 out, every row
+    g = I.gemm_inputs(M, 256, 2304, seed=M + 11, outlier_frac=0.01, outlier_mult=50.0)
+    run_case(g.a_bf16, g.w_bf16, "f32", what=f"split-K {M}x256x2304", split=True)
 
 
 def test_fused_without_quantized_outputs_and_repeatable():
