@@ -67,7 +67,7 @@ def test_plan_log_lines():
         "block_gemm M=4096 N=7168 K=1024 tiles=256x256+256x192",
         "block_gemm M=64 N=1024 K=2048 tiles=128x64 split-K + reduction",
         "block_gemm M=64 N=1024 K=2048 tiles=128x64 ksplit=1",
-        "block_gemm_fused_quant M=64 N=1024 K=2048 tiles=32x256",
+        "block_gemm_fused_quant M=64 N=1024 K=2048 tiles=64x256",
         "block_grouped_gemm M=300 N=256 K=256 tiles=128x256",
         "block_gemm_dgrad (W read transposed) M=64 N=2048 K=1024",
         "block_gemm_wgrad M=512 N=384 K=256",
