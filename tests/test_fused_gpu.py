@@ -163,12 +163,15 @@ def test_fused_split_k_workload_rows_of_every_tile(N):
     run_case(x_bits, w_bits, "bf16", rows=rows, what=f"split-K {M}x{N}x{K}", split=True)
 
 
-@pytest.mark.parametrize("M", [1, 63, 65, 200])
-def test_fused_split_k_ragged_fp32(M):
+@pytest.mark.parametrize("M,N,K", [(1, 256, 2304), (63, 256, 2304), (65, 256, 2304),
+                                   (200, 256, 2304), (130, 384, 1280)])
+def test_fused_split_k_ragged_fp32(M, N, K):
     # ragged 64-row tiles with K split (G = 18: splits of 5, 5, 5 and 3 K
-    # blocks), FP32 out, every row
-    g = I.gemm_inputs(M, 256, 2304, seed=M + 11, outlier_frac=0.01, outlier_mult=50.0)
-    run_case(g.a_bf16, g.w_bf16, "f32", what=f"split-K {M}x256x2304", split=True)
+    # blocks; G = 10 over a half-filled second N tile: 2 splits of 5, with
+    # only the first N tile writing the quantized outputs), FP32 out, every
+    # row
+    g = I.gemm_inputs(M, N, K, seed=M + N + 11, outlier_frac=0.01, outlier_mult=50.0)
+    run_case(g.a_bf16, g.w_bf16, "f32", what=f"split-K {M}x{N}x{K}", split=True)
 
 
 def test_fused_without_quantized_outputs_and_repeatable():
