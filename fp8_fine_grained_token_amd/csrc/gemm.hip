@@ -1040,9 +1040,11 @@ __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
     const int wn = (threadIdx.x >> 6) % C::kWavesN;
     tile_mainloop<C, kPow2, kTransW>(op, p.K, p.G, kb0, kb1, (int)(n0 & 127) + wn * C::WN, lds,
                                      acc);
+    // Partial sums are written and read back once, both with the
+    // nontemporal policy (see splitk_reduce_kernel).
     if (OUT == kOutPartial)
-        tile_store<C, kOutF32, false>(acc, lds, p.partial + (int64_t)ks * p.M * p.N, p.N, row0,
-                                      p.M, n0, p.N);
+        tile_store<C, kOutF32, true>(acc, lds, p.partial + (int64_t)ks * p.M * p.N, p.N, row0,
+                                     p.M, n0, p.N);
     else
         tile_store<C, OUT>(acc, lds, p.c, p.N, row0, p.M, n0, p.N);
 }
@@ -1135,14 +1137,22 @@ __global__ __launch_bounds__(WgradTile::kThreads) void wgrad_two_kind_kernel(Gem
 // output conversion.  Four elements per thread (M*N is a multiple of 128).
 // The partials are loaded eight splits at a time before any is added, so
 // their latencies overlap instead of adding up (indexes past S - 1 re-read
-// split S - 1 and are not added).
+// split S - 1 and are not added).  The partials are stored and loaded with
+// the nontemporal policy: on back-to-back decode-sized calls (256 x 2048 x
+// 7168 over rotating operand sets) that took a call from 18.2 to 16.2 us,
+// the streamed partials no longer displacing the next call's operands in the
+// caches; either half alone gained at most 1.5%.
 template <int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ partial,
                                                             void *__restrict__ c, int64_t MN,
                                                             int S) {
     const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= MN) return;
-    auto load = [&](int k) { return *reinterpret_cast<const float4 *>(partial + (int64_t)k * MN + i); };
+    auto load = [&](int k) {
+        const v4f t =
+            __builtin_nontemporal_load(reinterpret_cast<const v4f *>(partial + (int64_t)k * MN + i));
+        return make_float4(t[0], t[1], t[2], t[3]);
+    };
     float4 s = load(0);
     for (int k0 = 1; k0 < S; k0 += 8) {
         float4 v[8];
@@ -1502,7 +1512,7 @@ __global__ __launch_bounds__(FusedCfg::kThreads) void fused_quant_gemm_kernel(Ge
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (p.ksplit > 1)
-        tile_store_buf<C, kOutF32, false, sizeof(L.w)>(acc, &L.w[0][0],
+        tile_store_buf<C, kOutF32, true, sizeof(L.w)>(acc, &L.w[0][0],
                                                        p.partial + (int64_t)ks * p.M * p.N, p.N,
                                                        row0, p.M, n0, p.N);
     else
