@@ -886,9 +886,9 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 // for rows that are not a power of two long), which spreads the 16 rows a
 // wave writes at once over the banks.
 //
-// Final outputs, written once and not read again here, use nontemporal
-// stores; split-K partials (kStream false), read back by the reduction
-// right after, keep the default cache policy.
+// Final outputs and split-K partials are each written once; kStream selects
+// nontemporal stores for them (the reduction reads the partials back with
+// nontemporal loads).
 template <class C, int OUT, bool kStream, size_t kBufBytes>
 __device__ __forceinline__ void tile_store_buf(const v4f (&acc)[C::kTM][C::kTN], uint8_t *buf,
                                                void *c, int64_t ldc, int64_t row0,
