@@ -151,9 +151,9 @@ struct TileCfg {
     // barrier that every wave passes only once it finished the block before,
     // that user is done once D <= kScaleChunk
     static_assert(STAGES - 1 <= kScaleChunk, "scale chunk double buffer");
-    // copy instructions each wave issues per K block (A, W, weight scales);
-    // a scale chunk adds kScaleLoads more every kScaleChunk blocks
-    static constexpr int kCopiesPerBlock = kALoads + kBLoads + 1;
+    // copy instructions each wave issues per K block (A, W); a scale chunk
+    // adds kScaleLoads (+ kScaleLoadsW) + 1 more every kScaleChunk blocks
+    static constexpr int kCopiesPerBlock = kALoads + kBLoads;
     static_assert((STAGES - 2) * kCopiesPerBlock <= 63, "vmcnt range");  // wait count in the loop
 };
 
@@ -179,13 +179,15 @@ struct ScaleChunks {
 };
 
 // Everything a workgroup keeps in LDS: the operand stages, the activation
-// scale chunks and, per stage, the weight scales of the tile's (one or two)
-// 128-column blocks for that stage's K block.
+// scale chunks and the weight scales of the tile's 128-column blocks, chunked
+// like the activation scales: buffer b holds at word nb kScaleChunk + j the
+// scale of the tile's column block nb for K block kScaleChunk c + j (one
+// copy instruction per wave per chunk instead of one per K block).
 template <class C>
 struct TileLds {
     Stage<C::BM, C::BN> stages[C::kStages];
     ScaleChunks<C::BM, C::kScalePieces> chunks;
-    float sw[C::kStages][64];
+    float swc[2][64];
     // row-scaled W only: its rows' scales, chunked like the activation scales
     ScaleChunks<(C::kRowScaledW ? C::BN : 4), C::kScalePieces> wchunks;
 };
@@ -304,8 +306,11 @@ __device__ __forceinline__ void copy4(const v4i &r, uint32_t voff, uint32_t soff
 // other row read as zero, so ragged edges need no clamping.
 struct TileOperands {
     v4i a, w, sa, sw, swr;  // swr: W row scales (row-scaled W only)
-    // weight-scale fetch: lane L of the per-block copy reads byte offset
-    // L sw_lstride + kb sw_kstride of the sw view
+    // weight-scale fetch: lane L of a chunk copy reads the scale of the
+    // tile's 128-column block L / kScaleChunk for K block kScaleChunk c + L %
+    // kScaleChunk, at byte offset (L / kScaleChunk) sw_lstride + (L %
+    // kScaleChunk) sw_kstride (voffset) + kScaleChunk c sw_kstride (soffset)
+    // of the sw view
     uint32_t sw_lstride, sw_kstride;
     uint32_t ldw;           // transposed W only: bytes per row of W [K][N]
 };
@@ -322,9 +327,9 @@ __device__ __forceinline__ TileOperands tile_operands(const uint8_t *a, const fl
     t.w = make_rsrc(w + n0 * K, (uint32_t)(cw * K));
     t.sa = make_rsrc(sa + row0 * G, (uint32_t)(ra * G * 4));
     if constexpr (C::kRowScaledW) {
-        // sw is [cols][G]: rows n0 .. n0 + cw of it.  The per-block weight
-        // scale copy still runs (from an empty buffer) so the wait counts
-        // stay those of the block-scaled layout.
+        // sw is [cols][G]: rows n0 .. n0 + cw of it.  The weight-scale chunk
+        // copy still runs (from an empty buffer) so the wait counts stay
+        // those of the block-scaled layout.
         t.swr = make_rsrc(sw + n0 * G, (uint32_t)(cw * G * 4));
         t.sw = make_rsrc(sw, 0);
     } else {
@@ -356,11 +361,11 @@ __device__ __forceinline__ TileOperands tile_operands_transw(const uint8_t *a, c
     t.sa = make_rsrc(sa + row0 * G, (uint32_t)(ra * G * 4));
     t.w = make_rsrc(w + n0, (uint32_t)(K * ldw - n0));
     const int64_t nb0 = n0 >> 7, nbs = ((n0 + cw - 1) >> 7) - nb0 + 1;
-    // Lane L of the per-block copy reads sw[kb][nb0 + L] at offset 4 L +
-    // kb NB 4 (soffset): the buffer range check covers voffset + soffset,
-    // so the range runs to the end of the scales (lanes past the tile's
-    // blocks read other blocks' scales into LDS words nobody uses; past the
-    // end they read zero).
+    // A chunk copy's lane reads sw[kb][nb0 + nb] at offset 4 nb + kb NB 4
+    // (the chunk's first K block in soffset): the buffer range check covers
+    // voffset + soffset, so the range runs to the end of the scales (lanes
+    // past the tile's blocks read other blocks' scales into LDS words nobody
+    // uses; past the end they read zero).
     t.sw = make_rsrc(sw + nb0, (uint32_t)(((int64_t)(G - 1) * NB + nbs) * 4));
     t.swr = make_rsrc(sw, 0);
     t.sw_lstride = 4u;
@@ -475,7 +480,11 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         const int q = 64 * (wave + C::kWaves * t) + opaque_lane();
         return (uint32_t)((q % C::BN) * G * 4 + (q / C::BN) * 16);
     };
-    const uint32_t sw_voff = (uint32_t)lane * op.sw_lstride;
+    auto sw_voff = [&] {
+        const int ln = opaque_lane();
+        return (uint32_t)(ln / C::kScaleChunk) * op.sw_lstride +
+               (uint32_t)(ln % C::kScaleChunk) * op.sw_kstride;
+    };
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // for uniform branches
     // Transposed W: copy t of wave v fills bytes 1024 (v + kWaves t) .. +
     // 1024 of the stage's W tile (rows of BN bytes); lane L's 16 bytes at
@@ -498,7 +507,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     // sizeof(S) bytes further) and in scale chunk buffer 0.
     const uint32_t lds_a0 = lds_addr(&L.stages[0].a[1024 * wave]);
     const uint32_t lds_b0 = lds_addr(&L.stages[0].b[1024 * wave]);
-    const uint32_t lds_sw0 = lds_addr(&L.sw[0][0]);
+    const uint32_t lds_sw0 = lds_addr(&L.swc[0][0]);
     const uint32_t lds_sc0 =
         lds_addr(reinterpret_cast<const uint8_t *>(&L.chunks.v[0][0][0][0]) + 1024 * wave);
     const uint32_t lds_wc0 =
@@ -565,9 +574,9 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             }
         }
     };
-    // block kb's scales: its activation-scale chunk if one starts there, and
-    // its weight scales
-    auto issue_scales = [&](const TileOperands &src, int kb, int st) {
+    // block kb's scales: the activation- and weight-scale chunks if one
+    // starts there
+    auto issue_scales = [&](const TileOperands &src, int kb) {
         if (kb == kb0 || (kb & (C::kScaleChunk - 1)) == 0) {
             const int c = kb / C::kScaleChunk;
             const bool whole = (c + 1) * C::kScaleChunk <= G;
@@ -594,15 +603,16 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
                                        lds_addr(&L.wchunks.v[0][0][0][0]) + sow);
                 }
             }
+            // every wave fetches the chunk's weight scales to the same LDS
+            // words (the duplicates carry identical values), so that every
+            // wave issues the same number of copies
+            copy4(src.sw, sw_voff(), (uint32_t)(c * C::kScaleChunk) * op.sw_kstride,
+                  lds_sw0 + (uint32_t)((c & 1) * sizeof(L.swc[0])));
         }
-        // every wave fetches the (one or two) weight scales of the block to
-        // the same LDS words; the duplicates carry identical values
-        copy4(src.sw, sw_voff, (uint32_t)kb * op.sw_kstride,
-              lds_sw0 + (uint32_t)st * sizeof(L.sw[0]));
     };
     // all of block kb
     auto issue = [&](const TileOperands &src, int kb, int st) {
-        issue_scales(src, kb, st);
+        issue_scales(src, kb);
         issue_a(src, kb, st, -1);
         issue_w(src, kb, st);
     };
@@ -657,8 +667,10 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     // outputs of fragment j).
     static_assert(!(kPow2 && C::kRowScaledW), "row-scaled W runs with FP32 scales");
     float swr[C::kTN][4];
-    auto load_scales = [&](int s, int kb, float (&sc)[C::kTM], float (&swj)[C::kTN]) {
+    auto load_scales = [&](int kb, float (&sc)[C::kTM], float (&swj)[C::kTN]) {
         const int cb = (kb / C::kScaleChunk) & 1, piece = (kb >> 2) & (C::kScalePieces - 1);
+        // weight scale of the tile's 128-column block nb for block kb
+        auto wsc = [&](int nb) { return L.swc[cb][nb * C::kScaleChunk + (kb & (C::kScaleChunk - 1))]; };
         const float *sa_lane = &L.chunks.v[cb][piece][wm * C::WM + lr][kb & 3];
         if constexpr (C::kRowScaledW) {
             const float *sw_lane = &L.wchunks.v[cb][piece][wn * C::WN + 4 * lk][kb & 3];
@@ -672,16 +684,16 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 #pragma unroll
             for (int i = 0; i < C::kTM; ++i) sc[i] = e8m0_code(sa_lane[64 * i]);
 #pragma unroll
-            for (int j = 0; j < C::kTN; ++j) swj[j] = e8m0_code(L.sw[s][(col_off + 16 * j) >> 7]);
+            for (int j = 0; j < C::kTN; ++j) swj[j] = e8m0_code(wsc((col_off + 16 * j) >> 7));
         } else if constexpr (C::kWaveInOneBlock) {
-            const float swv = L.sw[s][col_off >> 7];
+            const float swv = wsc(col_off >> 7);
 #pragma unroll
             for (int i = 0; i < C::kTM; ++i) sc[i] = sa_lane[64 * i] * swv;
         } else {
 #pragma unroll
             for (int i = 0; i < C::kTM; ++i) sc[i] = sa_lane[64 * i];
 #pragma unroll
-            for (int j = 0; j < C::kTN; ++j) swj[j] = L.sw[s][(col_off + 16 * j) >> 7];
+            for (int j = 0; j < C::kTN; ++j) swj[j] = wsc((col_off + 16 * j) >> 7);
         }
     };
     // Weight fragments and scales of the block being computed.  With two
@@ -704,7 +716,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j) wfr[j] = wfrag(s, j);
         }
-        if constexpr (!kSplit) load_scales(s, kb, sc, swj);
+        if constexpr (!kSplit) load_scales(kb, sc, swj);
         float sc_next[C::kTM], swj_next[C::kTN];
         // combined scale of M tile i and N fragment j: sa(i) * sw(j)
         auto scale = [&](int i, int j) {
@@ -756,7 +768,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
                 af_next = afrag_at(s ^ 1, 0);
             else
                 af_next = af;
-            if (kSplit && i == C::kTM - 1) load_scales(s ^ 1, kb + 1, sc_next, swj_next);
+            if (kSplit && i == C::kTM - 1) load_scales(kb + 1, sc_next, swj_next);
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j) {
                 if constexpr (kPow2) {
@@ -788,8 +800,8 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         // Two stages, each block's copies in two groups so that the copy pipe
         // never drains at a barrier:
         //   G1(j): the A rows of every wave's first kTM / 2 M tiles of block j;
-        //   G2(j): the other A rows of block j + 1, and the W tile and the
-        //          scales of block j + 2.
+        //   G2(j): the other A rows of block j + 1, the W tile of block j + 2
+        //          and the scale chunks that start at block j + 2.
         // Block kb (stage st) runs as: rows 0 .. kTM/2 - 2; wait for G2(kb - 1)
         // (only the kG1 newer copies may stay outstanding), barrier, issue
         // G2(kb); rows kTM/2 - 1 .. kTM - 2; wait for G1(kb + 1) (kG2 newer
@@ -800,13 +812,15 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         // reloaded right after its last MFMA in block kb, and block kb + 1's
         // scales and first token fragment are read.  Reuse is safe: G2(kb)
         // overwrites the other stage's second-half A rows (block kb - 1 was
-        // finished before the last barrier) and this stage's W tile and
-        // scales (read into registers during block kb - 1's last row); G1(kb
+        // finished before the last barrier) and this stage's W tile (read
+        // into registers during block kb - 1's last row); G1(kb
         // + 2) overwrites this stage's first-half A rows (rows 0 .. kTM/2 - 1
         // of block kb are done).  Each group has one block of compute to land.
         constexpr int kAHalf = C::kALoads / 2;
         constexpr int kG1 = kAHalf;
-        constexpr int kG2 = C::kALoads - kAHalf + C::kBLoads + 1;  // without a scale chunk
+        // G2 without a scale chunk; a chunk's copies come after the A and W
+        // copies of G2, which only makes the wait for G1 stricter
+        constexpr int kG2 = C::kALoads - kAHalf + C::kBLoads;
         static_assert((C::WM / 2) % (8 * C::kWaves) == 0 && C::kTM % 2 == 0, "split block");
         // Blocks past the end are copied from empty buffers (every lane out of
         // bounds: nothing is read, zeros land in regions no block uses) so
@@ -825,13 +839,13 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         };
         issue(op, kb0, 0);
         issue_w(src_for(kb0 + 1), kb0 + 1, 1);
-        issue_scales(src_for(kb0 + 1), kb0 + 1, 1);
+        issue_scales(src_for(kb0 + 1), kb0 + 1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         issue_a(src_for(kb0 + 1), kb0 + 1, 1, 0);  // G1(kb0 + 1)
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) wfr[j] = wfrag(0, j);
-        load_scales(0, kb0, sc, swj);
+        load_scales(kb0, sc, swj);
         af_carry = afrag_at(0, 0);
         for (int kb = kb0; kb < kb1; ++kb) {
             const int st = (kb - kb0) & 1;
@@ -843,7 +857,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
                     issue_a(src_for(kb + 1), kb + 1, st ^ 1, 1);
                     const TileOperands next2 = src_for(kb + 2);
                     issue_w(next2, kb + 2, st);
-                    issue_scales(next2, kb + 2, st);
+                    issue_scales(next2, kb + 2);
                 },
                 [&] {
                     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kG2) : "memory");
