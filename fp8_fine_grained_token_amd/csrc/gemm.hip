@@ -151,8 +151,9 @@ struct TileCfg {
     // barrier that every wave passes only once it finished the block before,
     // that user is done once D <= kScaleChunk
     static_assert(STAGES - 1 <= kScaleChunk, "scale chunk double buffer");
-    // copy instructions each wave issues per K block (A, W); a scale chunk
-    // adds kScaleLoads (+ kScaleLoadsW) + 1 more every kScaleChunk blocks
+    // copy instructions each wave issues per K block (A, W; tiles that read W
+    // transposed add their weight-scale copy); a scale chunk adds kScaleLoads
+    // (+ kScaleLoadsW) + 1 more every kScaleChunk blocks
     static constexpr int kCopiesPerBlock = kALoads + kBLoads;
     static_assert((STAGES - 2) * kCopiesPerBlock <= 63, "vmcnt range");  // wait count in the loop
 };
@@ -179,15 +180,18 @@ struct ScaleChunks {
 };
 
 // Everything a workgroup keeps in LDS: the operand stages, the activation
-// scale chunks and the weight scales of the tile's 128-column blocks, chunked
-// like the activation scales: buffer b holds at word nb kScaleChunk + j the
-// scale of the tile's column block nb for K block kScaleChunk c + j (one
-// copy instruction per wave per chunk instead of one per K block).
+// scale chunks and the weight scales of the tile's 128-column blocks.  The
+// weight scales are chunked like the activation scales: buffer b holds at
+// word nb kScaleChunk + j the scale of the tile's column block nb for K block
+// kScaleChunk c + j (one copy instruction per wave per chunk instead of one
+// per K block).  Tiles that read W transposed keep one slot per stage
+// instead, holding the stage's block scales at word nb (fetched per K block:
+// chunked, that kernel measured ~3% slower).
 template <class C>
 struct TileLds {
     Stage<C::BM, C::BN> stages[C::kStages];
     ScaleChunks<C::BM, C::kScalePieces> chunks;
-    float swc[2][64];
+    float swc[C::kStages > 2 ? C::kStages : 2][64];
     // row-scaled W only: its rows' scales, chunked like the activation scales
     ScaleChunks<(C::kRowScaledW ? C::BN : 4), C::kScalePieces> wchunks;
 };
@@ -480,10 +484,18 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         const int q = 64 * (wave + C::kWaves * t) + opaque_lane();
         return (uint32_t)((q % C::BN) * G * 4 + (q / C::BN) * 16);
     };
+    // weight-scale copies: per K block (transposed W; the lane's offset is
+    // kept in a register) or per chunk (the offset is computed at each copy)
+    constexpr bool kSwPerBlock = kTransW;
+    const uint32_t sw_voff_blk = kSwPerBlock ? (uint32_t)lane * op.sw_lstride : 0u;
     auto sw_voff = [&] {
-        const int ln = opaque_lane();
-        return (uint32_t)(ln / C::kScaleChunk) * op.sw_lstride +
-               (uint32_t)(ln % C::kScaleChunk) * op.sw_kstride;
+        if constexpr (kSwPerBlock) {
+            return sw_voff_blk;
+        } else {
+            const int ln = opaque_lane();
+            return (uint32_t)(ln / C::kScaleChunk) * op.sw_lstride +
+                   (uint32_t)(ln % C::kScaleChunk) * op.sw_kstride;
+        }
     };
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // for uniform branches
     // Transposed W: copy t of wave v fills bytes 1024 (v + kWaves t) .. +
@@ -576,7 +588,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     };
     // block kb's scales: the activation- and weight-scale chunks if one
     // starts there
-    auto issue_scales = [&](const TileOperands &src, int kb) {
+    auto issue_scales = [&](const TileOperands &src, int kb, int st) {
         if (kb == kb0 || (kb & (C::kScaleChunk - 1)) == 0) {
             const int c = kb / C::kScaleChunk;
             const bool whole = (c + 1) * C::kScaleChunk <= G;
@@ -606,13 +618,17 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             // every wave fetches the chunk's weight scales to the same LDS
             // words (the duplicates carry identical values), so that every
             // wave issues the same number of copies
-            copy4(src.sw, sw_voff(), (uint32_t)(c * C::kScaleChunk) * op.sw_kstride,
-                  lds_sw0 + (uint32_t)((c & 1) * sizeof(L.swc[0])));
+            if constexpr (!kSwPerBlock)
+                copy4(src.sw, sw_voff(), (uint32_t)(c * C::kScaleChunk) * op.sw_kstride,
+                      lds_sw0 + (uint32_t)((c & 1) * sizeof(L.swc[0])));
         }
+        if constexpr (kSwPerBlock)
+            copy4(src.sw, sw_voff(), (uint32_t)kb * op.sw_kstride,
+                  lds_sw0 + (uint32_t)st * sizeof(L.swc[0]));
     };
     // all of block kb
     auto issue = [&](const TileOperands &src, int kb, int st) {
-        issue_scales(src, kb);
+        issue_scales(src, kb, st);
         issue_a(src, kb, st, -1);
         issue_w(src, kb, st);
     };
@@ -667,10 +683,15 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     // outputs of fragment j).
     static_assert(!(kPow2 && C::kRowScaledW), "row-scaled W runs with FP32 scales");
     float swr[C::kTN][4];
-    auto load_scales = [&](int kb, float (&sc)[C::kTM], float (&swj)[C::kTN]) {
+    auto load_scales = [&](int s, int kb, float (&sc)[C::kTM], float (&swj)[C::kTN]) {
         const int cb = (kb / C::kScaleChunk) & 1, piece = (kb >> 2) & (C::kScalePieces - 1);
         // weight scale of the tile's 128-column block nb for block kb
-        auto wsc = [&](int nb) { return L.swc[cb][nb * C::kScaleChunk + (kb & (C::kScaleChunk - 1))]; };
+        auto wsc = [&](int nb) {
+            if constexpr (kSwPerBlock)
+                return L.swc[s][nb];
+            else
+                return L.swc[cb][nb * C::kScaleChunk + (kb & (C::kScaleChunk - 1))];
+        };
         const float *sa_lane = &L.chunks.v[cb][piece][wm * C::WM + lr][kb & 3];
         if constexpr (C::kRowScaledW) {
             const float *sw_lane = &L.wchunks.v[cb][piece][wn * C::WN + 4 * lk][kb & 3];
@@ -716,7 +737,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j) wfr[j] = wfrag(s, j);
         }
-        if constexpr (!kSplit) load_scales(kb, sc, swj);
+        if constexpr (!kSplit) load_scales(s, kb, sc, swj);
         float sc_next[C::kTM], swj_next[C::kTN];
         // combined scale of M tile i and N fragment j: sa(i) * sw(j)
         auto scale = [&](int i, int j) {
@@ -768,7 +789,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
                 af_next = afrag_at(s ^ 1, 0);
             else
                 af_next = af;
-            if (kSplit && i == C::kTM - 1) load_scales(kb + 1, sc_next, swj_next);
+            if (kSplit && i == C::kTM - 1) load_scales(s ^ 1, kb + 1, sc_next, swj_next);
 #pragma unroll
             for (int j = 0; j < C::kTN; ++j) {
                 if constexpr (kPow2) {
@@ -801,7 +822,8 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         // never drains at a barrier:
         //   G1(j): the A rows of every wave's first kTM / 2 M tiles of block j;
         //   G2(j): the other A rows of block j + 1, the W tile of block j + 2
-        //          and the scale chunks that start at block j + 2.
+        //          and the scale chunks that start at block j + 2 (reading W
+        //          transposed: and block j + 2's weight scales).
         // Block kb (stage st) runs as: rows 0 .. kTM/2 - 2; wait for G2(kb - 1)
         // (only the kG1 newer copies may stay outstanding), barrier, issue
         // G2(kb); rows kTM/2 - 1 .. kTM - 2; wait for G1(kb + 1) (kG2 newer
@@ -820,7 +842,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         constexpr int kG1 = kAHalf;
         // G2 without a scale chunk; a chunk's copies come after the A and W
         // copies of G2, which only makes the wait for G1 stricter
-        constexpr int kG2 = C::kALoads - kAHalf + C::kBLoads;
+        constexpr int kG2 = C::kALoads - kAHalf + C::kBLoads + (kSwPerBlock ? 1 : 0);
         static_assert((C::WM / 2) % (8 * C::kWaves) == 0 && C::kTM % 2 == 0, "split block");
         // Blocks past the end are copied from empty buffers (every lane out of
         // bounds: nothing is read, zeros land in regions no block uses) so
@@ -839,13 +861,13 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         };
         issue(op, kb0, 0);
         issue_w(src_for(kb0 + 1), kb0 + 1, 1);
-        issue_scales(src_for(kb0 + 1), kb0 + 1);
+        issue_scales(src_for(kb0 + 1), kb0 + 1, 1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         issue_a(src_for(kb0 + 1), kb0 + 1, 1, 0);  // G1(kb0 + 1)
 #pragma unroll
         for (int j = 0; j < C::kTN; ++j) wfr[j] = wfrag(0, j);
-        load_scales(kb0, sc, swj);
+        load_scales(0, kb0, sc, swj);
         af_carry = afrag_at(0, 0);
         for (int kb = kb0; kb < kb1; ++kb) {
             const int st = (kb - kb0) & 1;
@@ -857,7 +879,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
                     issue_a(src_for(kb + 1), kb + 1, st ^ 1, 1);
                     const TileOperands next2 = src_for(kb + 2);
                     issue_w(next2, kb + 2, st);
-                    issue_scales(next2, kb + 2);
+                    issue_scales(next2, kb + 2, st);
                 },
                 [&] {
                     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kG2) : "memory");
@@ -877,7 +899,9 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         for (int kb = kb0; kb < kb1; ++kb) {
             const int i = kb - kb0;
             if (kb + D - 1 < kb1)
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"((D - 1) * C::kCopiesPerBlock) : "memory");
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"((D - 1) * (C::kCopiesPerBlock +
+                                                                (kSwPerBlock ? 1 : 0)))
+                             : "memory");
             else
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
