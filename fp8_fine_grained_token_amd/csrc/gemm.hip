@@ -1373,7 +1373,9 @@ struct __align__(4096) FusedLds {
     uint8_t a16[FusedCfg::kStagesA][FusedCfg::BM * 256];
     uint8_t a8[2][FusedCfg::BM * 128];  // swizzled like Stage::a
     float sa[2][FusedCfg::BM];
-    float sw[FusedCfg::kStagesW][64];
+    // weight scales in chunks of 8 K blocks, as in TileLds: buffer b holds
+    // at word 8 nb + j the scale of column block nb for K block 8 c + j
+    float swc[2][64];
 };
 
 template <int OUT>
@@ -1402,8 +1404,8 @@ __global__ __launch_bounds__(FusedCfg::kThreads) void fused_quant_gemm_kernel(Ge
     const v4i rw = make_rsrc(p.w + n0 * K, (uint32_t)(cw * K));
     const int64_t nb0 = n0 >> 7, nbs = ((n0 + cw - 1) >> 7) - nb0 + 1;
     const v4i rsw = make_rsrc(p.sw + nb0 * G, (uint32_t)(nbs * G * 4));
-    v4i rx0 = rx, rw0 = rw, rsw0 = rsw;  // empty views for blocks past the end
-    rx0[2] = rw0[2] = rsw0[2] = 0;
+    v4i rx0 = rx, rw0 = rw;  // empty views for blocks past the end
+    rx0[2] = rw0[2] = 0;
 
     // W copy t of wave v fills W-stage rows 8 (v + 8 t) .. + 8 (as in
     // tile_mainloop: lane L -> physical chunk L % 8 of row L / 8, holding
@@ -1417,12 +1419,16 @@ __global__ __launch_bounds__(FusedCfg::kThreads) void fused_quant_gemm_kernel(Ge
     const uint32_t a_rowstep = (uint32_t)(32 * 2 * K);
     const uint32_t lds_w0 = lds_addr(&L.w[0][1024 * wave]);
     const uint32_t lds_a0 = lds_addr(&L.a16[0][1024 * wave]);
-    const uint32_t lds_sw0 = lds_addr(&L.sw[0][0]);
-    const uint32_t sw_voff = (uint32_t)(lane * G * 4);
+    const uint32_t lds_sw0 = lds_addr(&L.swc[0][0]);
+    const uint32_t sw_voff = (uint32_t)((lane >> 3) * G * 4 + (lane & 7) * 4);
 
-    // bf16 A of block k (this wave's 8 rows); the W tile and weight scales
-    // of block k.  Blocks past the split read from empty views, so every
-    // iteration issues the same copies.
+    // bf16 A of block k (this wave's 8 rows); the W tile of block k, and the
+    // weight-scale chunk starting at block k if one does (at the split's
+    // first block and every 8 blocks).  A and W of blocks past the split
+    // read from empty views.  The loop's waits leave only the newest bf16
+    // copies outstanding, so the chunk copies need no count of their own;
+    // the prologue's wait counts the chunk that starts at the split's first
+    // block.
     auto issue_a = [&](int k) {
         const bool in = k < kb1;
         const v4i &a_r = in ? rx : rx0;
@@ -1436,15 +1442,17 @@ __global__ __launch_bounds__(FusedCfg::kThreads) void fused_quant_gemm_kernel(Ge
     auto issue_w = [&](int k) {
         const bool in = k < kb1;
         const v4i &w_r = in ? rw : rw0;
-        const v4i &s_r = in ? rsw : rsw0;
         const int kc = in ? k : kb0;
         const uint32_t w_st = (uint32_t)((k % C::kStagesW) * sizeof(L.w[0]));
 #pragma unroll
         for (int t = 0; t < C::kWLoads; ++t)
             copy16_nt(w_r, w_voff + t * w_rowstep, (uint32_t)kc * 128u,
                       lds_w0 + w_st + 1024u * C::kWaves * t);
-        copy4(s_r, sw_voff, (uint32_t)kc * 4u,
-              lds_sw0 + (uint32_t)((k % C::kStagesW) * sizeof(L.sw[0])));
+        // (none past the split: such a copy would land in a buffer that the
+        // split's last chunk may still occupy)
+        if (in && (k == kb0 || (k & 7) == 0))
+            copy4(rsw, sw_voff, (uint32_t)(k & ~7) * 4u,
+                  lds_sw0 + (uint32_t)(((k >> 3) & 1) * sizeof(L.swc[0])));
     };
 
     // Quantize block kb from its bf16 stage (this wave's 8 rows) into E4M3
@@ -1509,7 +1517,7 @@ __global__ __launch_bounds__(FusedCfg::kThreads) void fused_quant_gemm_kernel(Ge
         for (int j = 0; j < C::kTN; ++j)
             wfr[j] = make_v8i(*reinterpret_cast<const uint4 *>(lw + j * 2048 + frag0),
                               *reinterpret_cast<const uint4 *>(lw + j * 2048 + frag1));
-        const float swv = L.sw[kb % C::kStagesW][col_off >> 7];
+        const float swv = L.swc[(kb >> 3) & 1][(col_off >> 7) * 8 + (kb & 7)];
 #pragma unroll
         for (int i = 0; i < C::kTM; ++i) {
             const v8i af = make_v8i(*reinterpret_cast<const uint4 *>(la + i * 2048 + frag0),
