@@ -924,10 +924,10 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
 // for rows that are not a power of two long), which spreads the 16 rows a
 // wave writes at once over the banks.
 //
-// Final outputs and split-K partials are each written once; kStream selects
-// nontemporal stores for them (the reduction reads the partials back with
+// Final outputs and split-K partials are each written once, with
+// nontemporal stores (the reduction reads the partials back with
 // nontemporal loads).
-template <class C, int OUT, bool kStream, size_t kBufBytes>
+template <class C, int OUT, size_t kBufBytes>
 __device__ __forceinline__ void tile_store_buf(const v4f (&acc)[C::kTM][C::kTN], uint8_t *buf,
                                                void *c, int64_t ldc, int64_t row0,
                                                int64_t row_end, int64_t n0, int64_t N) {
@@ -994,10 +994,7 @@ __device__ __forceinline__ void tile_store_buf(const v4f (&acc)[C::kTM][C::kTN],
                 u32x4 *dst = reinterpret_cast<u32x4 *>(static_cast<uint8_t *>(c) +
                                                        (grow * ldc + gcol) * kOB);
                 const u32x4 w = {v.x, v.y, v.z, v.w};
-                if (kStream)
-                    __builtin_nontemporal_store(w, dst);
-                else
-                    *dst = w;
+                __builtin_nontemporal_store(w, dst);
             }
         }
     }
@@ -1005,11 +1002,11 @@ __device__ __forceinline__ void tile_store_buf(const v4f (&acc)[C::kTM][C::kTN],
 
 // The tile's LDS operand stages are free once the main loop is done and
 // serve as the store buffer.
-template <class C, int OUT, bool kStream = true>
+template <class C, int OUT>
 __device__ __forceinline__ void tile_store(const v4f (&acc)[C::kTM][C::kTN], TileLds<C> &L,
                                            void *c, int64_t ldc, int64_t row0, int64_t row_end,
                                            int64_t n0, int64_t N) {
-    tile_store_buf<C, OUT, kStream, sizeof(L.stages)>(
+    tile_store_buf<C, OUT, sizeof(L.stages)>(
         acc, reinterpret_cast<uint8_t *>(&L.stages[0]), c, ldc, row0, row_end, n0, N);
 }
 
@@ -1081,8 +1078,8 @@ __global__ __launch_bounds__(C::kThreads) void dense_gemm_kernel(GemmParams p) {
     // Partial sums are written and read back once, both with the
     // nontemporal policy (see splitk_reduce_kernel).
     if (OUT == kOutPartial)
-        tile_store<C, kOutF32, true>(acc, lds, p.partial + (int64_t)ks * p.M * p.N, p.N, row0,
-                                     p.M, n0, p.N);
+        tile_store<C, kOutF32>(acc, lds, p.partial + (int64_t)ks * p.M * p.N, p.N, row0, p.M,
+                               n0, p.N);
     else
         tile_store<C, OUT>(acc, lds, p.c, p.N, row0, p.M, n0, p.N);
 }
@@ -1558,11 +1555,11 @@ __global__ __launch_bounds__(FusedCfg::kThreads) void fused_quant_gemm_kernel(Ge
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (p.ksplit > 1)
-        tile_store_buf<C, kOutF32, true, sizeof(L.w)>(acc, &L.w[0][0],
-                                                       p.partial + (int64_t)ks * p.M * p.N, p.N,
-                                                       row0, p.M, n0, p.N);
+        tile_store_buf<C, kOutF32, sizeof(L.w)>(acc, &L.w[0][0],
+                                                 p.partial + (int64_t)ks * p.M * p.N, p.N, row0,
+                                                 p.M, n0, p.N);
     else
-        tile_store_buf<C, OUT, true, sizeof(L.w)>(acc, &L.w[0][0], p.c, p.N, row0, p.M, n0, p.N);
+        tile_store_buf<C, OUT, sizeof(L.w)>(acc, &L.w[0][0], p.c, p.N, row0, p.M, n0, p.N);
 }
 
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
