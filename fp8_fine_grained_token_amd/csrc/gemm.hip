@@ -314,7 +314,8 @@ struct TileOperands {
     // tile's 128-column block L / kScaleChunk for K block kScaleChunk c + L %
     // kScaleChunk, at byte offset (L / kScaleChunk) sw_lstride + (L %
     // kScaleChunk) sw_kstride (voffset) + kScaleChunk c sw_kstride (soffset)
-    // of the sw view
+    // of the sw view; with W read transposed, lane L of the per-block copy
+    // reads block L for K block kb at L sw_lstride + kb sw_kstride
     uint32_t sw_lstride, sw_kstride;
     uint32_t ldw;           // transposed W only: bytes per row of W [K][N]
 };
@@ -365,11 +366,11 @@ __device__ __forceinline__ TileOperands tile_operands_transw(const uint8_t *a, c
     t.sa = make_rsrc(sa + row0 * G, (uint32_t)(ra * G * 4));
     t.w = make_rsrc(w + n0, (uint32_t)(K * ldw - n0));
     const int64_t nb0 = n0 >> 7, nbs = ((n0 + cw - 1) >> 7) - nb0 + 1;
-    // A chunk copy's lane reads sw[kb][nb0 + nb] at offset 4 nb + kb NB 4
-    // (the chunk's first K block in soffset): the buffer range check covers
-    // voffset + soffset, so the range runs to the end of the scales (lanes
-    // past the tile's blocks read other blocks' scales into LDS words nobody
-    // uses; past the end they read zero).
+    // Lane L of the per-block copy reads sw[kb][nb0 + L] at offset 4 L +
+    // kb NB 4 (soffset): the buffer range check covers voffset + soffset,
+    // so the range runs to the end of the scales (lanes past the tile's
+    // blocks read other blocks' scales into LDS words nobody uses; past the
+    // end they read zero).
     t.sw = make_rsrc(sw + nb0, (uint32_t)(((int64_t)(G - 1) * NB + nbs) * 4));
     t.swr = make_rsrc(sw, 0);
     t.sw_lstride = 4u;
