@@ -1,5 +1,6 @@
-"""GPU parity with weight scales that differ by up to 2^10 from one 128x128
-block to the next.
+"""GPU parity with scales that differ by up to 2^10 from one group to the
+next: 128x128 weight blocks, 1x128 activation groups and the 128x1 groups of
+the Wgrad operands.
 
 Each block (nb, kb) of the bf16 weights is multiplied by 2^e(nb, kb) with
 e = (3 nb + 5 kb) mod 11 - 5.  A power of two leaves the E4M3 bytes of the
@@ -154,3 +155,74 @@ def test_grouped_block_varying_weight_scales():
                                  dev(gi.offsets.astype(np.int32)), out_dtype="f32")
     check_gemm(c, R, "f32", "grouped varying W scales",
                grouped_error_bound(qa, sa, qw, sw, gi.offsets, np.arange(T)))
+
+
+# ---- activation scales and Wgrad row scales ---------------------------------
+
+def group_exponent(r, kb):
+    return (7 * r + 3 * kb) % 11 - 5
+
+
+def scale_groups(a_bits, along_rows=False):
+    """bf16 [R][C] with each 1x128 group (row r, column block kb) multiplied
+    by 2^group_exponent(r, kb); with along_rows, each 128x1 group (row block
+    r // 128, column c) by 2^group_exponent(c, r // 128) instead."""
+    x = (a_bits.astype(np.uint32) << 16).view(np.float32).copy()
+    R, C = x.shape
+    r = np.arange(R)[:, None]
+    c = np.arange(C)[None, :]
+    e = group_exponent(c, r // 128) if along_rows else group_exponent(r, c // 128)
+    x *= np.exp2(e).astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_group_exponents_reach_the_scales():
+    a, _ = I.activations(np.random.default_rng(9), 37, 1280, 0.01, 20.0)
+    q0, s0 = oracle.quant_act_1x128(a)
+    q1, s1 = oracle.quant_act_1x128(scale_groups(a))
+    e = group_exponent(np.arange(37)[:, None], np.arange(10)[None, :])
+    assert np.array_equal(q0, q1)
+    assert np.array_equal(s1, s0 * np.exp2(e).astype(np.float32))
+    t0, u0 = oracle.quant_act_128x1_t(a)
+    t1, u1 = oracle.quant_act_128x1_t(scale_groups(a, along_rows=True))
+    assert np.array_equal(t0, t1)
+    e_t = group_exponent(np.arange(1280)[:, None], np.arange(1)[None, :])
+    assert np.array_equal(u1, u0 * np.exp2(e_t).astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (4096, 7168, 1280),  # both tile widths; a partial activation-scale chunk
+    (300, 384, 2304),    # small tiles with split-K inside chunks; G = 18
+])
+def test_gemm_group_varying_activation_scales(M, N, K):
+    # activation scales 2^10 apart from group to group and row to row, with
+    # the weight-block pattern as well: a wrong row, K block, piece or chunk
+    # of the activation scales lands far outside the bound
+    g = I.gemm_inputs(M, N, K, seed=M + N + K + 1, outlier_frac=0.01, outlier_mult=20.0)
+    qa, sa = oracle.quant_act_1x128(scale_groups(g.a_bf16))
+    qw, sw = oracle.quant_weight_128x128(scale_blocks(g.w_bf16))
+    t = torch()
+    nbytes = B.fp8_gemm_workspace_bytes(M, N, K, "f32")
+    ws = t.empty(nbytes, dtype=t.uint8, device="cuda") if nbytes else None
+    c = B.fp8_block_gemm(dev(qa), dev(sa), dev(qw), dev(sw), out_dtype="f32", workspace=ws)
+    rows = rows_for(M, 256)
+    R = oracle.block_gemm(qa, sa, qw, sw, rows)
+    splits = max(1, nbytes // (M * N * 4))
+    check_gemm(c[t.from_numpy(rows).cuda()], R, "f32", f"varying A scales {M}x{N}x{K}",
+               gemm_error_bound(qa, sa, qw, sw, rows, splits=splits))
+
+
+@pytest.mark.parametrize("T,N,K", [(384, 300, 640), (1152, 1100, 2304)])
+def test_wgrad_group_varying_row_scales(T, N, K):
+    # dW = dY^T X from 128x1 groups whose scales are 2^10 apart (row chunks
+    # of both operands, T / 128 = 3 or 9 K blocks: partial chunks of 4)
+    rng = np.random.default_rng(T + N + K)
+    dy, _ = I.activations(rng, T, N, 0.0, 1.0)
+    x, _ = I.activations(rng, T, K, 0.01, 50.0)
+    qdy, sdy = oracle.quant_act_128x1_t(scale_groups(dy, along_rows=True))   # [N][T]
+    qx, sx = oracle.quant_act_128x1_t(scale_groups(x, along_rows=True))      # [K][T]
+    rows = np.arange(N) if N <= 300 else tile_rows(N, 128, per_tile=2)
+    R = oracle.rowscaled_gemm(qdy, sdy, qx, sx, rows)
+    c = B.fp8_block_gemm_wgrad(dev(qdy), dev(sdy), dev(qx), dev(sx), out_dtype="f32")
+    check_gemm(c[torch().from_numpy(rows).cuda()], R, "f32", f"wgrad varying scales {N}x{K}",
+               gemm_error_bound(qdy, sdy, qx, sx, rows, row_scaled_w=True))
