@@ -501,6 +501,27 @@ def test_gemm_scale_chunks_not_a_multiple(M, N, K):
                gemm_error_bound(qa, sa, qw, sw, rows))
 
 
+@pytest.mark.parametrize("M,N,K", [
+    (256, 256, 32768),   # 256 K blocks: 32 scale chunks; 128 x 64 tiles with split-K
+    (4096, 7168, 16384), # both 256-row tile widths over 128 K blocks
+])
+def test_gemm_long_k(M, N, K):
+    # Long inner dimensions: many scale chunks and double-buffer turns, and
+    # the FP32 promotion over up to 256 blocks, on rows of every M tile
+    g = I.gemm_inputs(M, N, K, seed=K + 5, outlier_frac=0.001, outlier_mult=100.0)
+    qa, sa, qw, sw = quantize(g)
+    t = torch()
+    nbytes = B.fp8_gemm_workspace_bytes(M, N, K, "f32")
+    ws = t.empty(nbytes, dtype=t.uint8, device="cuda") if nbytes else None
+    c = run_gemm(qa, sa, qw, sw, "f32", workspace=ws)
+    rows = np.arange(M, step=17) if M <= 256 else tile_rows(M, 256, per_tile=1)
+    log(f"  {M}x{N}x{K} (workspace {nbytes} B): oracle on {rows.size} rows")
+    R = oracle.block_gemm(qa, sa, qw, sw, rows)
+    splits = max(1, nbytes // (M * N * 4))
+    check_gemm(c[t.from_numpy(rows).cuda()], R, "f32", f"long K {M}x{N}x{K}",
+               gemm_error_bound(qa, sa, qw, sw, rows, splits=splits))
+
+
 def test_quant_then_gemm_chain_matches_oracle_chain():
     # The GPU quantizer's output fed to the GPU GEMM equals the oracle chain.
     g = I.gemm_inputs(96, 256, 768, seed=12, outlier_frac=0.01, outlier_mult=50.0)
