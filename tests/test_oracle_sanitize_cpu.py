@@ -5,8 +5,8 @@ oracle/oracle.c on small ragged shapes (partial 128-groups and blocks, an
 empty expert, special bf16 values) with exact-size heap buffers.  Built with
 gcc -fsanitize=address,undefined and no recovery, any out-of-bounds access,
 use after free or undefined operation in the oracle ends the run with an
-error report.  (The oracle's OpenMP pragmas are left out of this build, so
-it runs the same loops on one thread.)
+error report.  (The sanitizer build leaves out the oracle's OpenMP
+pragmas, so it runs the same loops on one thread.)
 """
 import os
 import shutil
