@@ -280,6 +280,40 @@ def test_workspace_query():
     assert lib.fp8_gemm_workspace_bytes(0, 2048, 7168, B.FP8_OUT_F32) == 0
 
 
+@pytest.mark.parametrize("M,N,K,splits", [
+    # 128 x 64 output tiles; the split count doubles while tiles x splits
+    # stay within 256 CUs and every split keeps at least 4 K blocks, then K
+    # blocks are dealt evenly (ceil) and empty splits dropped
+    (256, 2048, 7168, 4),     # 64 tiles, 56 K blocks -> 4 x 14
+    (256, 256, 32768, 32),    # 8 tiles, 256 K blocks -> 32 x 8
+    (300, 384, 1280, 2),      # 18 tiles (ragged M), 10 K blocks: 4 would leave 2 each
+    (128, 128, 896, 1),       # 7 K blocks cannot give two splits of 4
+    (128, 128, 1152, 2),      # 9 K blocks -> 5 + 4
+    (128, 128, 2048, 4),      # 16 K blocks -> 4 x 4
+    (128, 128, 4224, 7),      # 33 K blocks: 8 splits of ceil(33/8) = 5 need only 7
+    (100, 128, 4224, 7),
+    (1024, 1024, 1024, 2),    # 128 tiles: doubling reaches exactly 256
+    (1032, 1024, 1024, 1),    # 144 tiles
+    (4096, 3840, 7168, 1),    # 240 256x256 tiles: too few for the big plan, too many to split
+    (4096, 4096, 7168, 1),    # 256 256x256 tiles: the big plan
+])
+def test_workspace_split_counts(M, N, K, splits):
+    ws = B.lib().fp8_gemm_workspace_bytes(M, N, K, B.FP8_OUT_BF16)
+    assert ws == (splits * M * N * 4 if splits > 1 else 0)
+
+
+def test_workspace_fits_noalloc_scratch():
+    # every split plan's FP32 partials fit the no-allocation entry point's
+    # fixed array, whose size the header states as 8 MiB
+    lib = B.lib()
+    worst = 0
+    for M in (1, 64, 127, 128, 129, 256, 300, 512, 1000, 1024, 2048, 4000):
+        for N in (128, 256, 384, 1024, 2048, 4096, 7168):
+            for K in (128, 512, 1024, 4224, 7168, 65536):
+                worst = max(worst, lib.fp8_gemm_workspace_bytes(M, N, K, B.FP8_OUT_F32))
+    assert 0 < worst <= 8 << 20
+
+
 def test_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     x = torch.zeros((4, 128), dtype=torch.bfloat16)
