@@ -313,10 +313,20 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=None):
         del pa, psa, pw, psw
 
     if want("fused_quant_gemm_4096x7168x7168"):
-        # bf16 activations quantized inside the GEMM (no E4M3 round trip)
+        # bf16 activations quantized inside the GEMM (no E4M3 round trip);
+        # without a workspace the entry point runs the fused kernel
         P.add_flops("fused_quant_gemm_4096x7168x7168",
                     *P.timed(lambda: F.fp8_block_gemm_fused_quant(X, qw, sw, out_dtype="bf16",
                                                                   c=C)), fl)
+    if want("fused_quant_entry_staged_4096x7168x7168"):
+        # the same call with the workspace it asks for: at this width it
+        # takes the staged plan (the quantizer, then the block GEMM)
+        few = torch.empty(F.fp8_fused_quant_workspace_bytes(M, N, K, "bf16"), dtype=torch.uint8,
+                          device="cuda")
+        P.add_flops("fused_quant_entry_staged_4096x7168x7168",
+                    *P.timed(lambda: F.fp8_block_gemm_fused_quant(X, qw, sw, out_dtype="bf16",
+                                                                  c=C, workspace=few)), fl)
+        del few
     if want("fused_quant_crossover_m4096_k7168"):
         # The fused GEMM against the two-call path (quantizer, then GEMM),
         # each timed from a flushed cache, over the output width N: every
@@ -330,10 +340,15 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=None):
             cn = torch.empty((M, n), dtype=torch.bfloat16, device="cuda")
             # each path in its best configuration: with the split-K
             # workspace it asks for (small N)
-            nf = F.fp8_fused_quant_workspace_bytes(M, n, K, "bf16")
+            nf = F.fp8_fused_quant_kernel_workspace_bytes(M, n, K, "bf16")
             fws = torch.empty(nf, dtype=torch.uint8, device="cuda") if nf else None
             ms_f, _ = P.timed(lambda: F.fp8_block_gemm_fused_quant(X, wq, ws, out_dtype="bf16",
                                                                    c=cn, workspace=fws))
+            # the entry point with its own workspace size: the faster plan
+            ne = F.fp8_fused_quant_workspace_bytes(M, n, K, "bf16")
+            ews = torch.empty(ne, dtype=torch.uint8, device="cuda") if ne else None
+            ms_e, _ = P.timed(lambda: F.fp8_block_gemm_fused_quant(X, wq, ws, out_dtype="bf16",
+                                                                   c=cn, workspace=ews))
             nb = F.fp8_gemm_workspace_bytes(M, n, K, "bf16")
             gws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
 
@@ -343,14 +358,20 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=None):
             ms_t, _ = P.timed(two_call)
             rows.append({"N": n, "fused_us": round(ms_f * 1e3, 2),
                          "two_call_us": round(ms_t * 1e3, 2),
+                         "entry_us": round(ms_e * 1e3, 2),
+                         "entry_plan": "fused" if ne == nf else "staged",
                          "fused_split_k_workspace_bytes": nf,
+                         "entry_workspace_bytes": ne,
                          "two_call_split_k_workspace_bytes": nb,
                          "fused_faster": ms_f < ms_t})
-            del wq, ws, cn, gws, fws
+            del wq, ws, cn, gws, fws, ews
         P.out["fused_quant_crossover_m4096_k7168"] = {
             "rows": rows, "note": "M=4096, K=7168, bf16 out; each launch (or pair) after a "
-                                  "512 MB cache flush; median of 50; both paths get the "
-                                  "split-K workspaces they ask for"}
+                                  "512 MB cache flush; median of 50; fused = the fused "
+                                  "kernel with its split-K workspace, entry = "
+                                  "fp8_block_gemm_fused_quant with its own workspace "
+                                  "size (its faster plan), two_call = quantizer then "
+                                  "block GEMM with its split-K workspace"}
 
     # backward of the same layer: dY [4096][7168] (same distribution as X
     # without outliers); Dgrad = forward GEMM with the transposed weights,

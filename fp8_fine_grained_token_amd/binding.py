@@ -59,6 +59,8 @@ _SIGNATURES = {
     "fp8_block_gemm_fused_quant": ([_P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, _P,
                                     _P, ctypes.c_size_t, _P], ctypes.c_int),
     "fp8_fused_quant_workspace_bytes": ([_I64, _I64, _I64, ctypes.c_int], ctypes.c_size_t),
+    "fp8_fused_quant_kernel_workspace_bytes": ([_I64, _I64, _I64, ctypes.c_int],
+                                               ctypes.c_size_t),
     "fp8_block_gemm_noalloc": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P],
                                ctypes.c_int),
     "fp8_quant_act_1x128_pow2": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
@@ -223,6 +225,11 @@ def fp8_fused_quant_workspace_bytes(M: int, N: int, K: int, out_dtype="bf16") ->
     return int(lib().fp8_fused_quant_workspace_bytes(M, N, K, code))
 
 
+def fp8_fused_quant_kernel_workspace_bytes(M: int, N: int, K: int, out_dtype="bf16") -> int:
+    code, _ = _out_code(out_dtype)
+    return int(lib().fp8_fused_quant_kernel_workspace_bytes(M, N, K, code))
+
+
 def _workspace_args(workspace):
     if workspace is None:
         return ctypes.c_void_p(0), 0
@@ -292,9 +299,12 @@ def fp8_block_gemm_fused_quant(x, w, sw, out_dtype="bf16", c=None, q_out=None, s
     """C[M][N] = fp8_block_gemm(fp8_quant_act_1x128(x), w, sw) with the 1x128
     quantization of the bf16 activations x [M][K] done inside the GEMM.
     With return_quantized (or q_out / sa_out given) the E4M3 bytes [M][K]
-    and scales [M][K/128] are written too and (c, q, sa) is returned.  A
-    workspace of fp8_fused_quant_workspace_bytes(M, N, K) bytes enables the
-    split-K path for small M x N."""
+    and scales [M][K/128] are written too and (c, q, sa) is returned.  With a
+    workspace of fp8_fused_quant_workspace_bytes(M, N, K) bytes the library
+    takes the faster plan for the shape (for wide outputs or few tokens: the
+    quantizer, then the block GEMM); with one of
+    fp8_fused_quant_kernel_workspace_bytes(M, N, K) bytes the fused kernel
+    splits K."""
     torch = _torch()
     _rank(x, "x", 2)
     _rank(w, "w", 2)

@@ -165,18 +165,27 @@ fp8_status fp8_block_grouped_gemm(const void *a_e4m3, const float *a_scales,
  *                 fp32: optional outputs (both NULL, or both given), which
  *                 receive exactly what fp8_quant_act_1x128 writes, e.g. to
  *                 keep the FP8 activations for the backward pass.
- *   workspace / workspace_bytes: optional, as for fp8_block_gemm, with the
- *                 size from fp8_fused_quant_workspace_bytes(); with it, K is
- *                 split over workgroups when the output tiles alone would
- *                 not fill the GPU.
+ *   workspace / workspace_bytes: optional (256-byte aligned); it selects
+ *                 the plan:
+ *     - workspace_bytes >= fp8_fused_quant_workspace_bytes(): the faster plan
+ *       for the shape.  The fused kernel (quantization inside the GEMM, K
+ *       split over workgroups when the output tiles alone would not fill
+ *       the GPU) for C one 256-column tile wide (N <= 256) over at least
+ *       2048 tokens; elsewhere, where every further 256-column tile would
+ *       quantize its rows again, the staged plan: fp8_quant_act_1x128 into
+ *       q_e4m3_out / a_scales_out (or into the workspace when they are NULL
+ *       or q_e4m3_out is not 16-byte aligned), then fp8_block_gemm with its
+ *       split-K partials in the workspace.
+ *     - less (or NULL and 0): the fused kernel, with K split when
+ *       workspace_bytes >= fp8_fused_quant_kernel_workspace_bytes() > 0.
  * The quantized values, the products and the accumulation are those of the
  * two-call path, so C is the same up to the FP32 summation order (bitwise
  * the same where both calls run the same K splits, e.g. both without a
- * workspace).  Every 256-column tile of C quantizes its activation rows
- * again, so this call is the faster one only for small and medium N (see
- * the measured crossover in the documentation).  Errors: as fp8_block_gemm,
+ * workspace, and always under the staged plan).  Errors: as fp8_block_gemm,
  * plus FP8_ERR_NULL when only one of q_e4m3_out / a_scales_out is given, and
  * FP8_ERR_ALIGN for x_bf16 not 16-byte or q_e4m3_out not 8-byte aligned.
+ * The staged plan enqueues two kernels; FP8_ERR_HIP from the second leaves
+ * the first enqueued.
  */
 fp8_status fp8_block_gemm_fused_quant(const void *x_bf16, const void *w_e4m3,
                                       const float *w_scales, void *c, int out_dtype,
@@ -342,9 +351,20 @@ fp8_status fp8_block_gemm_dgrad(const void *dy_e4m3, const float *dy_scales,
  * shape (0 when the shape does not use it). */
 size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int out_dtype);
 
-/* The same for fp8_block_gemm_fused_quant (whose tiles, and so its splits,
- * differ from fp8_block_gemm's). */
+/* Workspace bytes with which fp8_block_gemm_fused_quant takes the faster
+ * plan for this shape: the fused kernel's split-K partials (0 if it does not
+ * split), or for the staged plan the E4M3 activations, their scales and
+ * fp8_block_gemm's partials, each part rounded up to 256 bytes. */
 size_t fp8_fused_quant_workspace_bytes(int64_t M, int64_t N, int64_t K, int out_dtype);
+
+/* Workspace bytes that let the fused kernel itself split K for this shape
+ * whenever fp8_block_gemm_fused_quant runs it (its 64 x 256 tiles, and so
+ * its splits, differ from fp8_block_gemm's; 0 when it does not split).  On
+ * shapes that prefer the staged plan the call runs the fused kernel only
+ * with fewer than fp8_fused_quant_workspace_bytes() bytes, which may or may
+ * not leave room for these partials. */
+size_t fp8_fused_quant_kernel_workspace_bytes(int64_t M, int64_t N, int64_t K,
+                                              int out_dtype);
 
 /* Static, human-readable name of a status code. */
 const char *fp8_status_string(fp8_status s);

@@ -85,7 +85,7 @@ def run_cases():
     # ... and with its split-K workspace (4 splits of 1024 x 256 x 2304)
     x = act(12, 1024, 2304)
     qw, sw = F.fp8_quant_weight_128x128(wts(13, 256, 2304))
-    nf = F.fp8_fused_quant_workspace_bytes(1024, 256, 2304, "f32")
+    nf = F.fp8_fused_quant_kernel_workspace_bytes(1024, 256, 2304, "f32")
     assert nf > 0
     fws = torch.empty(nf, dtype=torch.uint8, device="cuda")
     c, q, s = F.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype="f32", return_quantized=True,

@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
         + ["fp8_quant_act_128x1_t", "fp8_transpose_weight_128x128", "fp8_block_gemm_wgrad"]
         + ["fp8_gemm_workspace_bytes", "fp8_status_string", "fp8_block_gemm_noalloc",
            "fp8_block_gemm_fused_quant", "fp8_fused_quant_workspace_bytes",
-           "fp8_block_gemm_dgrad"])
+           "fp8_fused_quant_kernel_workspace_bytes", "fp8_block_gemm_dgrad"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -184,11 +184,12 @@ def test_fused_quant_gemm_argument_errors():
     assert fq(M=0, x=NUL, c=NUL) == B.FP8_OK
 
 
-def test_fused_quant_workspace_bytes():
-    # the fused GEMM's 64 x 256 tiles split K while tiles x splits fit in 256
-    # CUs and every split keeps 4 K blocks; its partials are FP32 [S][M][N]
+def test_fused_quant_kernel_workspace_bytes():
+    # the fused kernel's 64 x 256 tiles split K while tiles x splits fit in
+    # 256 CUs and every split keeps 4 K blocks; its partials are FP32
+    # [S][M][N]
     lib = B.lib()
-    ws = lib.fp8_fused_quant_workspace_bytes
+    ws = lib.fp8_fused_quant_kernel_workspace_bytes
     assert ws(4096, 256, 7168, B.FP8_OUT_BF16) == 4 * 4096 * 256 * 4   # 64 tiles -> 4 splits
     assert ws(4096, 512, 7168, B.FP8_OUT_F32) == 2 * 4096 * 512 * 4    # 128 tiles -> 2 splits
     assert ws(4096, 1024, 7168, B.FP8_OUT_BF16) == 0                   # 256 tiles fill the CUs
@@ -196,6 +197,39 @@ def test_fused_quant_workspace_bytes():
     assert ws(64, 256, 1024, B.FP8_OUT_BF16) == 2 * 64 * 256 * 4
     assert ws(0, 256, 1024, B.FP8_OUT_BF16) == 0
     assert ws(64, 200, 1024, B.FP8_OUT_BF16) == 0
+    assert ws(64, 256, 1024, 7) == 0
+
+
+def r256(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("M,N,K,expect", [
+    # the fused kernel is the faster plan: C one 256-column tile wide over at
+    # least 2048 tokens; its own split-K partials
+    (4096, 256, 7168, 4 * 4096 * 256 * 4),  # 64 tiles: 4 splits of 14
+    (2048, 128, 7168, 8 * 2048 * 128 * 4),  # 32 tiles: 8 splits of 7 K blocks
+    (16384, 256, 7168, 0),                  # 256 tiles of 64 rows fill the CUs
+    # elsewhere the staged plan: E4M3 activations, their scales, then the
+    # block GEMM's split-K partials, each part rounded up to 256 bytes
+    (4096, 512, 7168, 4096 * 7168 + 4096 * 56 * 4),
+    (4096, 7168, 7168, 4096 * 7168 + 4096 * 56 * 4),
+    (2047, 256, 7168, 2047 * 7168 + r256(2047 * 56 * 4) + 4 * 2047 * 256 * 4),
+    (64, 256, 1024, 64 * 1024 + 64 * 8 * 4 + 2 * 64 * 256 * 4),
+    (64, 256, 512, 64 * 512 + 64 * 4 * 4),
+    (1, 128, 128, 256 + 256),
+])
+def test_fused_quant_workspace_bytes(M, N, K, expect):
+    lib = B.lib()
+    assert lib.fp8_fused_quant_workspace_bytes(M, N, K, B.FP8_OUT_BF16) == expect
+    assert lib.fp8_fused_quant_workspace_bytes(M, N, K, B.FP8_OUT_F32) == expect
+
+
+def test_fused_quant_workspace_bytes_invalid():
+    ws = B.lib().fp8_fused_quant_workspace_bytes
+    assert ws(0, 256, 1024, B.FP8_OUT_BF16) == 0
+    assert ws(64, 200, 1024, B.FP8_OUT_BF16) == 0
+    assert ws(64, 256, 1000, B.FP8_OUT_BF16) == 0
     assert ws(64, 256, 1024, 7) == 0
 
 

@@ -11,6 +11,11 @@ FP8 cast with the transfer of activations), so:
   - with FP32 output C equals the two-call path (GPU quantizer, then the
     plain GEMM) bit for bit: the same bytes, scales, block products and
     promotion order per output.
+With the entry point's own workspace size, shapes wider than one 256-column
+tile or with fewer than 2048 tokens take the staged plan (the quantizer, then
+the block GEMM): there C and the optional outputs must equal the two calls'
+bit for bit.  The tests of the fused kernel's split-K path pass the kernel's
+own workspace size, which keeps the fused kernel on the shapes they use.
 """
 import numpy as np
 import pytest
@@ -41,8 +46,13 @@ def assert_bytes_and_scales(qg, sg, qo, so, what):
     assert nbad == 0 and sbad == 0
 
 
-def fused_workspace(M, N, K):
-    nb = B.fp8_fused_quant_workspace_bytes(M, N, K, "f32")
+def fused_kernel_workspace(M, N, K):
+    # the fused kernel's split-K partials; on shapes whose faster plan is the
+    # staged one the call keeps the fused kernel only below the entry
+    # point's own workspace size
+    nb = B.fp8_fused_quant_kernel_workspace_bytes(M, N, K, "f32")
+    entry = B.fp8_fused_quant_workspace_bytes(M, N, K, "f32")
+    assert nb < entry or (N <= 256 and M >= 2048 and nb == entry), (nb, entry)
     return torch().empty(nb, dtype=torch().uint8, device="cuda") if nb else None
 
 
@@ -51,7 +61,7 @@ def run_case(a_bits, w_bits, out, rows=None, what="", split=False):
     qa, sa = oracle.quant_act_1x128(a_bits)
     x = dev_bf16(a_bits)
     M, K = a_bits.shape
-    ws = fused_workspace(M, w_bits.shape[0], K) if split else None
+    ws = fused_kernel_workspace(M, w_bits.shape[0], K) if split else None
     if split:
         assert ws is not None, "shape has no split-K plan"
     c, q, s = B.fp8_block_gemm_fused_quant(x, dev(qw), dev(sw), out_dtype=out,
@@ -136,13 +146,12 @@ def test_fused_split_k_equals_two_call_split_k_fp32(M, N, K, splits):
     qw, sw = B.fp8_quant_weight_128x128(dev_bf16(g.w_bf16))
     qa, sa = B.fp8_quant_act_1x128(x)
     nb = B.fp8_gemm_workspace_bytes(M, N, K, "f32")
-    nf = B.fp8_fused_quant_workspace_bytes(M, N, K, "f32")
-    assert nb == nf == splits * M * N * 4
+    fws = fused_kernel_workspace(M, N, K)
+    assert nb == fws.numel() == splits * M * N * 4
     c2 = B.fp8_block_gemm(qa, sa, qw, sw, out_dtype="f32",
                           workspace=t.empty(nb, dtype=t.uint8, device="cuda"))
-    c1, q1, s1 = B.fp8_block_gemm_fused_quant(
-        x, qw, sw, out_dtype="f32", return_quantized=True,
-        workspace=t.empty(nf, dtype=t.uint8, device="cuda"))
+    c1, q1, s1 = B.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype="f32",
+                                              return_quantized=True, workspace=fws)
     t.cuda.synchronize()
     assert t.equal(q1, qa) and t.equal(s1.view(t.int32), sa.view(t.int32))
     log(f"  fused split-K ({splits}) vs two-call split-K FP32: max |diff| = "
@@ -182,3 +191,68 @@ def test_fused_without_quantized_outputs_and_repeatable():
     c0 = B.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype="f32")
     c1, _, _ = B.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype="f32", return_quantized=True)
     assert t.equal(c0, c1)
+
+
+def two_call(x, qw, sw, out):
+    t = torch()
+    M, K = x.shape
+    N = qw.shape[0]
+    qa, sa = B.fp8_quant_act_1x128(x)
+    nb = B.fp8_gemm_workspace_bytes(M, N, K, out)
+    ws = t.empty(nb, dtype=t.uint8, device="cuda") if nb else None
+    return B.fp8_block_gemm(qa, sa, qw, sw, out_dtype=out, workspace=ws), qa, sa
+
+
+@pytest.mark.parametrize("M,N,K,out", [
+    (300, 512, 2304, "f32"),     # block GEMM split 4 ways through the workspace
+    (64, 256, 1024, "bf16"),     # fewer than 2048 tokens, one column tile
+    (2047, 256, 2304, "f32"),    # one token below the fused plan's range
+    (1, 128, 128, "f32"),
+    (4096, 7168, 7168, "bf16"),  # the dense layer: 28 column tiles
+])
+def test_fused_entry_staged_plan_equals_two_calls(M, N, K, out):
+    # with fp8_fused_quant_workspace_bytes() (filled with garbage first) the
+    # call quantizes into q_out / sa_out, or into the workspace without them,
+    # and runs the block GEMM: C, bytes and scales equal the two calls'
+    t = torch()
+    g = I.gemm_inputs(M, N, K, seed=M + 3 * N + K, outlier_frac=0.01, outlier_mult=50.0)
+    x = dev_bf16(g.a_bf16)
+    qw, sw = B.fp8_quant_weight_128x128(dev_bf16(g.w_bf16))
+    c2, qa, sa = two_call(x, qw, sw, out)
+    nf = B.fp8_fused_quant_workspace_bytes(M, N, K, out)
+    assert nf >= M * K + M * (K // 128) * 4
+    ws = t.full((nf,), 0xA5, dtype=t.uint8, device="cuda")
+    c1, q1, s1 = B.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype=out, return_quantized=True,
+                                              workspace=ws)
+    ws.fill_(0x5A)
+    c0 = B.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype=out, workspace=ws)
+    t.cuda.synchronize()
+    assert t.equal(q1, qa) and t.equal(s1.view(t.int32), sa.view(t.int32))
+    log(f"  staged {M}x{N}x{K} {out}: max |diff| vs two calls = "
+        f"{(c1.float() - c2.float()).abs().max().item():.3e}")
+    assert t.equal(c1, c2) and t.equal(c0, c2)
+
+
+def test_fused_entry_keeps_fused_kernel_for_unaligned_q_out():
+    # E4M3 outputs 8- but not 16-byte aligned: the block GEMM could not read
+    # them, so even with the whole workspace the call runs the fused kernel
+    # (split as with the kernel's own workspace size)
+    t = torch()
+    M, N, K = 300, 512, 2304
+    g = I.gemm_inputs(M, N, K, seed=77, outlier_frac=0.01, outlier_mult=50.0)
+    x = dev_bf16(g.a_bf16)
+    qw, sw = B.fp8_quant_weight_128x128(dev_bf16(g.w_bf16))
+    qa, sa = B.fp8_quant_act_1x128(x)
+    raw = t.empty(M * K + 16, dtype=t.uint8, device="cuda")
+    q8 = raw[8:8 + M * K].view(M, K)
+    assert q8.data_ptr() % 16 == 8
+    s8 = t.empty((M, K // 128), dtype=t.float32, device="cuda")
+    nf = B.fp8_fused_quant_workspace_bytes(M, N, K, "f32")
+    c1, _, _ = B.fp8_block_gemm_fused_quant(
+        x, qw, sw, out_dtype="f32", q_out=q8, sa_out=s8,
+        workspace=t.empty(nf, dtype=t.uint8, device="cuda"))
+    ck = B.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype="f32",
+                                      workspace=fused_kernel_workspace(M, N, K))
+    t.cuda.synchronize()
+    assert t.equal(q8, qa) and t.equal(s8.view(t.int32), sa.view(t.int32))
+    assert t.equal(c1, ck)

@@ -4,7 +4,8 @@ The flag is read once per process, so the calls run in a child Python
 process started with FP8BLK_LOG=1; its stderr must name the expected plan
 for each entry point (two tile widths for 4096 x 7168, split-K for a small
 M with a workspace, the unsplit small-tile plan without one, the grouped,
-fused, Dgrad and Wgrad kernels).
+fused, Dgrad and Wgrad kernels, and the fused entry point's staged plan
+with its workspace).
 """
 import os
 import subprocess
@@ -37,6 +38,9 @@ F.fp8_block_gemm(qa2, sa2, qw2, sw2, workspace=ws)
 F.fp8_block_gemm(qa2, sa2, qw2, sw2)
 x = torch.randn(64, 2048, device="cuda").to(torch.bfloat16)
 F.fp8_block_gemm_fused_quant(x, qw2, sw2)
+wsf = torch.empty(F.fp8_fused_quant_workspace_bytes(64, 1024, 2048), dtype=torch.uint8,
+                  device="cuda")
+F.fp8_block_gemm_fused_quant(x, qw2, sw2, workspace=wsf)
 qg, sg = q8(300, 256); wg, swg = w8(2 * 256, 256)
 off = torch.tensor([0, 100, 300], dtype=torch.int32, device="cuda")
 F.fp8_block_grouped_gemm(qg, sg, wg.view(2, 256, 256), swg.view(2, 2, 2), off)
@@ -68,6 +72,8 @@ def test_plan_log_lines():
         "block_gemm M=64 N=1024 K=2048 tiles=128x64 split-K + reduction",
         "block_gemm M=64 N=1024 K=2048 tiles=128x64 ksplit=1",
         "block_gemm_fused_quant M=64 N=1024 K=2048 tiles=64x256",
+        "block_gemm_fused_quant M=64 N=1024 K=2048 plan=staged",
+        "block_gemm M=64 N=1024 K=2048 tiles=128x64 split-K + reduction",
         "block_grouped_gemm M=300 N=256 K=256 tiles=128x256",
         "block_gemm_dgrad (W read transposed) M=64 N=2048 K=1024",
         "block_gemm_wgrad M=512 N=384 K=256",

@@ -127,7 +127,7 @@ def test_fused_block_varying_weight_scales(M, N, K, split):
     t = torch()
     ws = None
     if split:
-        nbytes = B.fp8_fused_quant_workspace_bytes(M, N, K, "f32")
+        nbytes = B.fp8_fused_quant_kernel_workspace_bytes(M, N, K, "f32")
         assert nbytes > 0, "shape has no split-K plan"
         ws = t.empty(nbytes, dtype=t.uint8, device="cuda")
     c = B.fp8_block_gemm_fused_quant(dev_bf16(a), dev(qw), dev(sw), out_dtype="f32",
