@@ -6,9 +6,10 @@ split-K path takes its partials from the caller's workspace and reduces
 them with a kernel (the no-allocation GEMM from the library's static
 scratch array instead).  Each test captures 1x128 activation quantization
 followed by a GEMM (plain, split-K, grouped, no-allocation, Dgrad on the
-forward weights), or the GEMM with the quantization fused in, into one
-graph (torch.cuda.CUDAGraph over the library's launches on the capture
-stream) and replays it several times.  Between
+forward weights), or the GEMM with the quantization fused in (also as the
+quantizer and block GEMM that its entry point runs for a small M when given
+its workspace), into one graph (torch.cuda.CUDAGraph over the library's
+launches on the capture stream) and replays it several times.  Between
 replays the program's own eager work changes the bf16 input in place and
 synchronizes, and every replay must equal, bit for bit, the eager chain on
 the same input: the same kernels run on the same bytes, in a fixed
@@ -196,6 +197,38 @@ def test_graph_fused_quant_gemm():
         return q2, s2, c2
 
     replay_and_check(capture, eager, x, fresh, "fused quantization + GEMM 96x512x1280 f32")
+
+
+def test_graph_fused_entry_staged_plan():
+    # the same entry point with the workspace it asks for: at 96 tokens it
+    # takes the staged plan, i.e. the quantizer and the split-K block GEMM
+    # (partials in the same workspace); with and without quantized outputs
+    t = torch()
+    M, N, K = 96, 512, 1280
+    x = activations(9, M, K)
+    fresh = [activations(60 + r, M, K) for r in range(REPLAYS)]
+    qw, sw = B.fp8_quant_weight_128x128(dev_bf16(I.weights(np.random.default_rng(10), (N, K))))
+    nb = B.fp8_fused_quant_workspace_bytes(M, N, K, "f32")
+    assert nb > M * K + M * (K // 128) * 4 and B.fp8_gemm_workspace_bytes(M, N, K, "f32") > 0
+    ws = t.empty(nb, dtype=t.uint8, device="cuda")
+    q = t.empty((M, K), dtype=t.uint8, device="cuda")
+    s = t.empty((M, K // 128), dtype=t.float32, device="cuda")
+    c = t.empty((M, N), dtype=t.float32, device="cuda")
+    c0 = t.empty((M, N), dtype=t.float32, device="cuda")
+
+    def capture():
+        B.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype="f32", c=c, q_out=q, sa_out=s,
+                                     workspace=ws)
+        B.fp8_block_gemm_fused_quant(x, qw, sw, out_dtype="f32", c=c0, workspace=ws)
+        return q, s, c, c0
+
+    def eager():
+        qa, sa = B.fp8_quant_act_1x128(x)
+        gws = t.empty(B.fp8_gemm_workspace_bytes(M, N, K, "f32"), dtype=t.uint8, device="cuda")
+        c2 = B.fp8_block_gemm(qa, sa, qw, sw, out_dtype="f32", workspace=gws)
+        return qa, sa, c2, c2
+
+    replay_and_check(capture, eager, x, fresh, "fused entry, staged plan 96x512x1280 f32")
 
 
 def test_graph_dgrad_transposed_split_k():
