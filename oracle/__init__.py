@@ -74,6 +74,8 @@ def _load():
         lib.orc_rowscaled_gemm_rows.restype = None
         lib.orc_quant_act_128x1_t.argtypes = [P, I64, I64, P, P]
         lib.orc_quant_act_128x1_t.restype = None
+        lib.orc_quant_act_128x1_t_pow2.argtypes = [P, I64, I64, P, P]
+        lib.orc_quant_act_128x1_t_pow2.restype = None
         lib.orc_grouped_gemm_rows.argtypes = [P, P, P, P, P, I64, I64, I64, I64,
                                               P, I64, P, P]
         lib.orc_grouped_gemm_rows.restype = None
@@ -191,6 +193,17 @@ def quant_act_128x1_t(x_bf16: np.ndarray):
     q = np.empty((K, M), dtype=np.uint8)
     s = np.empty((K, (M + 127) // 128), dtype=np.float32)
     _load().orc_quant_act_128x1_t(_ptr(x), M, K, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quant_act_128x1_t_pow2(x_bf16: np.ndarray):
+    """As quant_act_128x1_t with power-of-two scales (oracle.c, pow2
+    reading)."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    q = np.empty((K, M), dtype=np.uint8)
+    s = np.empty((K, (M + 127) // 128), dtype=np.float32)
+    _load().orc_quant_act_128x1_t_pow2(_ptr(x), M, K, _ptr(q), _ptr(s))
     return q, s
 
 

@@ -249,10 +249,11 @@ void orc_quant_weight_128x128_pow2(const uint16_t *w, int64_t N, int64_t K,
 
 /* 128x1 tiles, written transposed [backward reading above]: group (mb, k)
  * holds x[m][k] for m in [128 mb, min(128 mb + 128, M)), quantized as one
- * group (amax / 448 scale, as orc_quant_group).  q_t is E4M3 [K][M] with
- * q_t[k][m] the code of x[m][k]; scales_t is fp32 [K][ceil(M/128)]. */
-void orc_quant_act_128x1_t(const uint16_t *x, int64_t M, int64_t K,
-                           uint8_t *q_t, float *scales_t) {
+ * group (as orc_quant_group: amax / 448 scale, or with pow2 the power-of-two
+ * scale).  q_t is E4M3 [K][M] with q_t[k][m] the code of x[m][k]; scales_t
+ * is fp32 [K][ceil(M/128)]. */
+static void orc_quant_128x1_t(const uint16_t *x, int64_t M, int64_t K, int pow2,
+                              uint8_t *q_t, float *scales_t) {
     int64_t GM = (M + ORC_GROUP - 1) / ORC_GROUP;
     int64_t k;
     uint8_t *q = (uint8_t *)malloc((size_t)(M * K > 0 ? M * K : 1));
@@ -264,7 +265,7 @@ void orc_quant_act_128x1_t(const uint16_t *x, int64_t M, int64_t K,
             int64_t m0 = mb * ORC_GROUP;
             int64_t h = (M - m0 < ORC_GROUP) ? M - m0 : ORC_GROUP;
             scales_t[k * GM + mb] =
-                orc_quant_group(x + m0 * K + k, K, h, 1, 0, q + m0 * K + k);
+                orc_quant_group(x + m0 * K + k, K, h, 1, pow2, q + m0 * K + k);
         }
     }
 #pragma omp parallel for schedule(static)
@@ -273,6 +274,16 @@ void orc_quant_act_128x1_t(const uint16_t *x, int64_t M, int64_t K,
         for (m = 0; m < M; ++m) q_t[k * M + m] = q[m * K + k];
     }
     free(q);
+}
+
+void orc_quant_act_128x1_t(const uint16_t *x, int64_t M, int64_t K,
+                           uint8_t *q_t, float *scales_t) {
+    orc_quant_128x1_t(x, M, K, 0, q_t, scales_t);
+}
+
+void orc_quant_act_128x1_t_pow2(const uint16_t *x, int64_t M, int64_t K,
+                                uint8_t *q_t, float *scales_t) {
+    orc_quant_128x1_t(x, M, K, 1, q_t, scales_t);
 }
 
 /* ---- GEMM reference ----------------------------------------------------- */

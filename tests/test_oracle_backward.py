@@ -38,6 +38,23 @@ def test_128x1_transposed_equals_1x128_of_the_transpose():
     assert np.array_equal(s_t.view(np.uint32), s_ref.view(np.uint32))
 
 
+def test_128x1_transposed_pow2_equals_1x128_pow2_of_the_transpose():
+    # the same with power-of-two scales, against the pinned pow2 1x128
+    # quantizer; zero, subnormal and large columns take the special scales
+    x, _ = I.activations(np.random.default_rng(34), 300, 200, 0.01, 50.0)
+    x[:, 3] = 0
+    x[:130, 4] = 0x0001
+    x[:, 5] = 0x7F7F
+    q_t, s_t = oracle.quant_act_128x1_t_pow2(x)
+    q_ref, s_ref = oracle.quant_act_1x128_pow2(np.ascontiguousarray(x.T))
+    assert q_t.shape == (200, 300) and s_t.shape == (200, 3)
+    assert np.array_equal(q_t, q_ref)
+    assert np.array_equal(s_t.view(np.uint32), s_ref.view(np.uint32))
+    # every nonzero scale is a power of two
+    nz = s_t[s_t > 0]
+    assert np.all(np.frexp(nz)[0] == 0.5)
+
+
 def test_rowscaled_gemm_reduces_to_the_block_gemm():
     # with every row of a 128-row block carrying that block's scales, the
     # per-row-scaled GEMM is the block-scaled GEMM, bit for bit
