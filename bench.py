@@ -378,7 +378,8 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=None):
     # Wgrad = dY^T X from 128x1 tiles
     bwd = [n for n in ("bwd_quant_128x1_t_4096x7168", "bwd_transpose_weight_7168x7168",
                        "bwd_dgrad_4096x7168x7168", "bwd_dgrad_transposed_reads_4096x7168x7168",
-                       "bwd_wgrad_7168x7168_over_4096") if want(n)]
+                       "bwd_wgrad_7168x7168_over_4096", "pow2_bwd_quant_128x1_t_4096x7168",
+                       "pow2_bwd_wgrad_7168x7168_over_4096") if want(n)]
     if bwd:
         dy = to_dev_bf16(torch, I.activations(np.random.default_rng(7), M, N, 0.0, 1.0)[0])
         if want("bwd_quant_128x1_t_4096x7168"):
@@ -411,6 +412,19 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=None):
             P.add_flops("bwd_wgrad_7168x7168_over_4096",
                         *P.timed(lambda: F.fp8_block_gemm_wgrad(qdy_t, sdy_t, qx_t, sx_t,
                                                                 out_dtype="f32", dw=dw)), fl)
+            del qdy_t, sdy_t, qx_t, sx_t, dw
+        if want("pow2_bwd_quant_128x1_t_4096x7168"):
+            P.add_bytes("pow2_bwd_quant_128x1_t_4096x7168",
+                        *P.timed(lambda: F.fp8_quant_act_128x1_t_pow2(dy)), quant_bytes(M, N))
+        if want("pow2_bwd_wgrad_7168x7168_over_4096"):
+            # power-of-two scales: the block-scaled MFMA takes each row's
+            # scale, so the tiles are 256 rows tall
+            qdy_t, sdy_t = F.fp8_quant_act_128x1_t_pow2(dy)
+            qx_t, sx_t = F.fp8_quant_act_128x1_t_pow2(X)
+            dw = torch.empty((N, K), dtype=torch.float32, device="cuda")
+            P.add_flops("pow2_bwd_wgrad_7168x7168_over_4096",
+                        *P.timed(lambda: F.fp8_block_gemm_wgrad_pow2(qdy_t, sdy_t, qx_t, sx_t,
+                                                                     out_dtype="f32", dw=dw)), fl)
             del qdy_t, sdy_t, qx_t, sx_t, dw
         del dy, qdy, sdy, qwt, swt
 

@@ -51,9 +51,12 @@ _SIGNATURES = {
     "fp8_gemm_workspace_bytes": ([_I64, _I64, _I64, ctypes.c_int], ctypes.c_size_t),
     "fp8_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "fp8_quant_act_128x1_t": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "fp8_quant_act_128x1_t_pow2": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "fp8_transpose_weight_128x128": ([_P, _P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "fp8_block_gemm_wgrad": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P],
                              ctypes.c_int),
+    "fp8_block_gemm_wgrad_pow2": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P],
+                                  ctypes.c_int),
     "fp8_block_gemm_dgrad": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P,
                               ctypes.c_size_t, _P], ctypes.c_int),
     "fp8_block_gemm_fused_quant": ([_P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, _P,
@@ -409,6 +412,15 @@ def fp8_block_grouped_gemm_pow2(a, sa, w, sw, group_offsets, out_dtype="bf16", c
 def fp8_quant_act_128x1_t(x, q_t=None, scales_t=None, stream=None):
     """x: bf16 [M][K] -> (q_t uint8 [K][M], scales_t fp32 [K][ceil(M/128)]):
     128x1 tiles (128 rows of one column), written transposed."""
+    return _quant_128x1_t("fp8_quant_act_128x1_t", x, q_t, scales_t, stream)
+
+
+def fp8_quant_act_128x1_t_pow2(x, q_t=None, scales_t=None, stream=None):
+    """As fp8_quant_act_128x1_t with power-of-two scales."""
+    return _quant_128x1_t("fp8_quant_act_128x1_t_pow2", x, q_t, scales_t, stream)
+
+
+def _quant_128x1_t(fn, x, q_t, scales_t, stream):
     torch = _torch()
     _rank(x, "x", 2)
     M, K = x.shape
@@ -418,10 +430,10 @@ def fp8_quant_act_128x1_t(x, q_t=None, scales_t=None, stream=None):
         scales_t = torch.empty((K, (M + 127) // 128), dtype=torch.float32, device=x.device)
     _shape(q_t, "q_t", (K, M))
     _shape(scales_t, "scales_t", (K, (M + 127) // 128))
-    _check(lib().fp8_quant_act_128x1_t(_dev(x, "x", torch.bfloat16), M, K,
-                                       _dev(q_t, "q_t", torch.uint8),
-                                       _dev(scales_t, "scales_t", torch.float32),
-                                       _stream_handle(stream)), "fp8_quant_act_128x1_t")
+    _check(getattr(lib(), fn)(_dev(x, "x", torch.bfloat16), M, K,
+                              _dev(q_t, "q_t", torch.uint8),
+                              _dev(scales_t, "scales_t", torch.float32),
+                              _stream_handle(stream)), fn)
     return q_t, scales_t
 
 
@@ -452,6 +464,18 @@ def fp8_block_gemm_wgrad(dy_t, dy_t_scales, x_t, x_t_scales, out_dtype="f32", dw
                          stream=None):
     """dW [N][K] = dY^T X from 128x1-grouped operands written transposed:
     dy_t [N][T], x_t [K][T] (uint8 E4M3), scales [N][T/128] and [K][T/128]."""
+    return _wgrad("fp8_block_gemm_wgrad", dy_t, dy_t_scales, x_t, x_t_scales, out_dtype, dw,
+                  stream)
+
+
+def fp8_block_gemm_wgrad_pow2(dy_t, dy_t_scales, x_t, x_t_scales, out_dtype="f32", dw=None,
+                              stream=None):
+    """As fp8_block_gemm_wgrad, for power-of-two scales."""
+    return _wgrad("fp8_block_gemm_wgrad_pow2", dy_t, dy_t_scales, x_t, x_t_scales, out_dtype,
+                  dw, stream)
+
+
+def _wgrad(fn, dy_t, dy_t_scales, x_t, x_t_scales, out_dtype, dw, stream):
     torch = _torch()
     _rank(dy_t, "dy_t", 2)
     _rank(x_t, "x_t", 2)
@@ -465,10 +489,10 @@ def fp8_block_gemm_wgrad(dy_t, dy_t_scales, x_t, x_t_scales, out_dtype="f32", dw
         _shape(dy_t_scales, "dy_t_scales", (N, T // 128))
         _shape(x_t_scales, "x_t_scales", (K, T // 128))
     _shape(dw, "dw", (N, K))
-    _check(lib().fp8_block_gemm_wgrad(_dev(dy_t, "dy_t", torch.uint8),
-                                      _dev(dy_t_scales, "dy_t_scales", torch.float32),
-                                      _dev(x_t, "x_t", torch.uint8),
-                                      _dev(x_t_scales, "x_t_scales", torch.float32),
-                                      _dev(dw, "dw", tdt), code, N, K, T,
-                                      _stream_handle(stream)), "fp8_block_gemm_wgrad")
+    _check(getattr(lib(), fn)(_dev(dy_t, "dy_t", torch.uint8),
+                              _dev(dy_t_scales, "dy_t_scales", torch.float32),
+                              _dev(x_t, "x_t", torch.uint8),
+                              _dev(x_t_scales, "x_t_scales", torch.float32),
+                              _dev(dw, "dw", tdt), code, N, K, T,
+                              _stream_handle(stream)), fn)
     return dw

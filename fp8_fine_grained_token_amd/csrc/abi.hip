@@ -126,6 +126,30 @@ fp8_status grouped_gemm(const void *a_e4m3, const float *a_scales, const void *w
                                                 as_stream(hip_stream)));
 }
 
+fp8_status quant_128x1_t(const void *x_bf16, int64_t M, int64_t K, void *q_t, float *scales_t,
+                         bool pow2, void *hip_stream) {
+    fp8_status st = check_quant(x_bf16, M, K, q_t, scales_t);
+    if (st != FP8_OK || M == 0 || K == 0) return st;
+    if (!aligned(x_bf16, 2) || !aligned(scales_t, 4)) return FP8_ERR_ALIGN;
+    clear_last_error();
+    return from_hip(fp8blk::launch_quant_act_128x1_t(x_bf16, M, K, q_t, scales_t, pow2,
+                                                     as_stream(hip_stream)));
+}
+
+fp8_status wgrad(const void *dy_t, const float *dy_t_scales, const void *x_t,
+                 const float *x_t_scales, void *dw, int out_dtype, int64_t N, int64_t K,
+                 int64_t T, bool pow2, void *hip_stream) {
+    // rows N, columns K, inner dimension T (tokens)
+    fp8_status st = check_gemm_common(dy_t, dy_t_scales, x_t, x_t_scales, dw, out_dtype, N, K, T,
+                                      nullptr, 0);
+    if (st != FP8_OK || N == 0 || K == 0) return st;
+    if (T == 0) return FP8_ERR_SHAPE;
+    clear_last_error();
+    return from_hip(fp8blk::launch_block_gemm_wgrad(dy_t, dy_t_scales, x_t, x_t_scales, dw,
+                                                    out_dtype == FP8_OUT_BF16, N, K, T, pow2,
+                                                    as_stream(hip_stream)));
+}
+
 // Plan of fp8_block_gemm_fused_quant.  The fused kernel quantizes a tile's
 // activation rows again for every 256-column tile of C, and copies bf16 rows
 // (twice the bytes of E4M3 ones) into 64-row tiles, so it beats the
@@ -307,12 +331,12 @@ fp8_status fp8_block_grouped_gemm_pow2(const void *a_e4m3, const float *a_scales
 
 fp8_status fp8_quant_act_128x1_t(const void *x_bf16, int64_t M, int64_t K, void *q_t,
                                  float *scales_t, void *hip_stream) {
-    fp8_status st = check_quant(x_bf16, M, K, q_t, scales_t);
-    if (st != FP8_OK || M == 0 || K == 0) return st;
-    if (!aligned(x_bf16, 2) || !aligned(scales_t, 4)) return FP8_ERR_ALIGN;
-    clear_last_error();
-    return from_hip(
-        fp8blk::launch_quant_act_128x1_t(x_bf16, M, K, q_t, scales_t, as_stream(hip_stream)));
+    return quant_128x1_t(x_bf16, M, K, q_t, scales_t, false, hip_stream);
+}
+
+fp8_status fp8_quant_act_128x1_t_pow2(const void *x_bf16, int64_t M, int64_t K, void *q_t,
+                                      float *scales_t, void *hip_stream) {
+    return quant_128x1_t(x_bf16, M, K, q_t, scales_t, true, hip_stream);
 }
 
 fp8_status fp8_transpose_weight_128x128(const void *q_e4m3, const float *scales, int64_t N,
@@ -332,15 +356,14 @@ fp8_status fp8_transpose_weight_128x128(const void *q_e4m3, const float *scales,
 fp8_status fp8_block_gemm_wgrad(const void *dy_t, const float *dy_t_scales, const void *x_t,
                                 const float *x_t_scales, void *dw, int out_dtype, int64_t N,
                                 int64_t K, int64_t T, void *hip_stream) {
-    // rows N, columns K, inner dimension T (tokens)
-    fp8_status st = check_gemm_common(dy_t, dy_t_scales, x_t, x_t_scales, dw, out_dtype, N, K, T,
-                                      nullptr, 0);
-    if (st != FP8_OK || N == 0 || K == 0) return st;
-    if (T == 0) return FP8_ERR_SHAPE;
-    clear_last_error();
-    return from_hip(fp8blk::launch_block_gemm_wgrad(dy_t, dy_t_scales, x_t, x_t_scales, dw,
-                                                    out_dtype == FP8_OUT_BF16, N, K, T,
-                                                    as_stream(hip_stream)));
+    return wgrad(dy_t, dy_t_scales, x_t, x_t_scales, dw, out_dtype, N, K, T, false, hip_stream);
+}
+
+fp8_status fp8_block_gemm_wgrad_pow2(const void *dy_t, const float *dy_t_scales,
+                                     const void *x_t, const float *x_t_scales, void *dw,
+                                     int out_dtype, int64_t N, int64_t K, int64_t T,
+                                     void *hip_stream) {
+    return wgrad(dy_t, dy_t_scales, x_t, x_t_scales, dw, out_dtype, N, K, T, true, hip_stream);
 }
 
 size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int out_dtype) {

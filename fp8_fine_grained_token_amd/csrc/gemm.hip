@@ -138,7 +138,6 @@ struct TileCfg {
     static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "loader");
     static_assert((SCALE_PIECES * BM) % 64 == 0 && (SCALE_PIECES * BN) % 64 == 0, "scale loader");
     static_assert(SCALE_PIECES == 1 || SCALE_PIECES == 2, "scale chunk pieces");
-    static_assert(!ROW_SCALED_W || STAGES >= 3, "row-scaled W runs the S >= 3 pipeline");
     static_assert(((BM + BN) * 128) % 4096 == 0, "stage size");
     static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile");
     // A wave's columns sit in one 128-column weight-scale block when WN
@@ -682,7 +681,12 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
     // row-scaled W, sc[i] = sa(i) and swr[j][e] = the scale of W row 16 j +
     // 4 (lane / 16) + e of the wave's columns (the rows of this lane's four
     // outputs of fragment j).
-    static_assert(!(kPow2 && C::kRowScaledW), "row-scaled W runs with FP32 scales");
+    // FP32 row scales are held per output (swr) and reloaded for each block,
+    // which the two-stage pipeline's early reads of the next block's scales
+    // would overwrite; power-of-two row scales go to the MFMA as one code per
+    // lane and fragment, like the block-scaled path's.
+    static_assert(!C::kRowScaledW || kPow2 || C::kStages >= 3,
+                  "FP32 row scales run the S >= 3 pipeline");
     float swr[C::kTN][4];
     auto load_scales = [&](int s, int kb, float (&sc)[C::kTM], float (&swj)[C::kTN]) {
         const int cb = (kb / C::kScaleChunk) & 1, piece = (kb >> 2) & (C::kScalePieces - 1);
@@ -694,7 +698,14 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
                 return L.swc[cb][nb * C::kScaleChunk + (kb & (C::kScaleChunk - 1))];
         };
         const float *sa_lane = &L.chunks.v[cb][piece][wm * C::WM + lr][kb & 3];
-        if constexpr (C::kRowScaledW) {
+        if constexpr (C::kRowScaledW && kPow2) {
+            // lane L holds row lr of W fragment j: its own row's code
+            const float *sw_lane = &L.wchunks.v[cb][piece][wn * C::WN + lr][kb & 3];
+#pragma unroll
+            for (int i = 0; i < C::kTM; ++i) sc[i] = e8m0_code(sa_lane[64 * i]);
+#pragma unroll
+            for (int j = 0; j < C::kTN; ++j) swj[j] = e8m0_code(sw_lane[64 * j]);
+        } else if constexpr (C::kRowScaledW) {
             const float *sw_lane = &L.wchunks.v[cb][piece][wn * C::WN + 4 * lk][kb & 3];
 #pragma unroll
             for (int i = 0; i < C::kTM; ++i) sc[i] = sa_lane[64 * i];
@@ -850,7 +861,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
         // that the wait counts stay fixed and the loop body has no
         // data-dependent branches.
         TileOperands none = op;
-        none.a[2] = none.w[2] = none.sa[2] = none.sw[2] = 0;
+        none.a[2] = none.w[2] = none.sa[2] = none.sw[2] = none.swr[2] = 0;
         auto src_for = [&](int kb) {
             const bool in = kb < kb1;
             TileOperands t;
@@ -858,6 +869,7 @@ __device__ __forceinline__ void tile_mainloop(const TileOperands &op, int64_t K,
             t.w = in ? op.w : none.w;
             t.sa = in ? op.sa : none.sa;
             t.sw = in ? op.sw : none.sw;
+            t.swr = in ? op.swr : none.swr;
             return t;
         };
         issue(op, kb0, 0);
@@ -1033,9 +1045,16 @@ using MidTile = TileCfg<128, 256, 2, 4, 3>;
 using WgradTile = TileCfg<128, 256, 2, 4, 3, 1, true>;
 // 128 x 192 on 8 waves (wave tile 64 x 48): covers part of the Wgrad columns
 // when 128 x 256 tiles alone would leave a nearly empty last round (see
-// plan_wgrad_two_kind).  Row-scaled W has a scale per column, so a wave's
+// plan_row_scaled_two_kind).  Row-scaled W has a scale per column, so a wave's
 // 48 columns may straddle 128-column boundaries freely.
 using WgradNarrowTile = TileCfg<128, 192, 2, 4, 3, 1, true>;
+// Wgrad with power-of-two scales: the block-scaled MFMA applies each row's
+// code itself and accumulates across K blocks, so no per-output scales sit
+// in registers and the forward GEMM's 256 x 256 (and 256 x 192) tiles with
+// two stages fit; scale chunks of 4 K blocks for both operands (128 KiB of
+// stages + 2 x 8 KiB of chunks).
+using WgradPow2Tile = TileCfg<256, 256, 2, 4, 2, 1, true>;
+using WgradPow2NarrowTile = TileCfg<256, 192, 2, 4, 2, 1, true>;
 
 // Logical tile index of this workgroup after the XCD remap (gridDim.x is a
 // multiple of 8; each XCD gets a contiguous range of logical tiles).
@@ -1159,14 +1178,15 @@ __global__ __launch_bounds__(BigTile::kThreads) void dense_gemm_two_kind_kernel(
 }
 
 // Wgrad with 128 x 256 tiles on columns [0, n_split) and 128 x 192 tiles on
-// the rest (plan_wgrad_two_kind).
-template <int OUT>
-__global__ __launch_bounds__(WgradTile::kThreads) void wgrad_two_kind_kernel(GemmParams p) {
+// the rest (plan_row_scaled_two_kind); with power-of-two scales, 256 x 256 and
+// 256 x 192 tiles.
+template <class CW, class CN, int OUT, bool kPow2>
+__global__ __launch_bounds__(CW::kThreads) void wgrad_two_kind_kernel(GemmParams p) {
     __shared__ union WgradLds {
-        TileLds<WgradTile> wide;
-        TileLds<WgradNarrowTile> narrow;
+        TileLds<CW> wide;
+        TileLds<CN> narrow;
     } lds;
-    two_kind_tile<WgradTile, WgradNarrowTile, OUT, false>(p, lds.wide, lds.narrow);
+    two_kind_tile<CW, CN, OUT, kPow2>(p, lds.wide, lds.narrow);
 }
 
 // Split-K reduction: C = sum over splits in fixed order 0..S-1, then the
@@ -1612,15 +1632,18 @@ bool plan_two_kind(int64_t M, int64_t N, int &tn1, int &tn2) {
 // used when it finishes at least 3% before the wide tiles alone: for
 // dW 7168 x 7168, a = 16 and b = 16 model at 6.46 wide-tile times against 7.
 constexpr double kWgradNarrowCost = 0.82;
+// The same model for the power-of-two Wgrad's 256 x 256 and 256 x 192 tiles,
+// whose narrow tile costs ~0.85 of a wide one (as in plan_two_kind): for dW
+// 7168 x 7168, a = 4 and b = 32 model at 3.55 wide-tile times against 4.
+constexpr double kWgradPow2NarrowCost = 0.85;
 
 // Finishing time of one XCD, in wide-tile times.  After the wide tiles, the
 // 32 - rem CUs holding q of them are free at q, the rem CUs holding q + 1 at
 // q + 1.  Each narrow tile goes to the CU free first, so the narrow tiles end
 // level by level: all CUs of the first group at q + r, q + 2r, ..., those
 // of the second at q + 1 + r, ..., merged in time order.
-double xcd_finish(int64_t wide, int64_t narrow) {
+double xcd_finish(int64_t wide, int64_t narrow, double r) {
     constexpr int kCUsPerXcd = kCUs / kNumXcd;
-    const double r = kWgradNarrowCost;
     const int64_t q = wide / kCUsPerXcd, rem = wide % kCUsPerXcd;
     double end = (double)(q + (rem ? 1 : 0));
     int64_t left = narrow, k_lo = 1, k_hi = 1;
@@ -1640,8 +1663,12 @@ double xcd_finish(int64_t wide, int64_t narrow) {
     return end;
 }
 
-bool plan_wgrad_two_kind(int64_t M, int64_t N, int &tn1, int &tn2) {
-    // the same shapes come back every training step
+// CW: the wide tile, CN: the narrow one (same rows), r: the narrow tile's
+// cost in wide-tile times.
+template <class CW, class CN>
+bool plan_row_scaled_two_kind(int64_t M, int64_t N, double r, int &tn1, int &tn2) {
+    static_assert(CW::BM == CN::BM, "two-kind tiles");
+    // the same shapes come back every training step (one cache per tile pair)
     thread_local int64_t last_m = -1, last_n = -1;
     thread_local int last_a = 0, last_b = 0;
     if (M == last_m && N == last_n) {
@@ -1649,19 +1676,20 @@ bool plan_wgrad_two_kind(int64_t M, int64_t N, int &tn1, int &tn2) {
         tn2 = last_b;
         return last_b > 0;
     }
-    const int64_t tm = (M + WgradTile::BM - 1) / WgradTile::BM;
-    const int64_t tn_wide = (N + WgradTile::BN - 1) / WgradTile::BN;
-    const double base = xcd_finish((tm * tn_wide + kNumXcd - 1) / kNumXcd, 0);
+    const int64_t tm = (M + CW::BM - 1) / CW::BM;
+    const int64_t tn_wide = (N + CW::BN - 1) / CW::BN;
+    const double base = xcd_finish((tm * tn_wide + kNumXcd - 1) / kNumXcd, 0, r);
     double best = 0.97 * base;
     int best_a = (int)tn_wide, best_b = 0;
     // a grid of at most one round of wide tiles finishes in one tile time
     // either way
-    const int64_t a_end = tm * tn_wide > kCUs ? (N + WgradTile::BN - 1) / WgradTile::BN : 0;
+    const int64_t a_end = tm * tn_wide > kCUs ? (N + CW::BN - 1) / CW::BN : 0;
     for (int64_t a = 0; a < a_end; ++a) {
-        const int64_t rest = N - WgradTile::BN * a;
+        const int64_t rest = N - CW::BN * a;
         if (rest <= 0) break;
-        const int64_t b = (rest + WgradNarrowTile::BN - 1) / WgradNarrowTile::BN;
-        const double t = xcd_finish((tm * a + kNumXcd - 1) / kNumXcd, (tm * b + kNumXcd - 1) / kNumXcd);
+        const int64_t b = (rest + CN::BN - 1) / CN::BN;
+        const double t = xcd_finish((tm * a + kNumXcd - 1) / kNumXcd,
+                                    (tm * b + kNumXcd - 1) / kNumXcd, r);
         if (t < best) {
             best = t;
             best_a = (int)a;
@@ -1819,9 +1847,43 @@ hipError_t launch_block_gemm(const void *a, const float *sa, const void *w, cons
                     : block_gemm<kOutF32, false>(p, pl, c, stream);
 }
 
+namespace {
+
+// Wgrad on the tile pair CW (wide) / CN (narrow): the two-kind plan when
+// it beats wide tiles alone, else wide tiles.
+template <class CW, class CN, bool kPow2>
+hipError_t launch_wgrad(GemmParams &p, bool bf16_out, double narrow_cost, const char *entry,
+                        const char *kinds, const char *wide, hipStream_t stream) {
+    int tn1, tn2;
+    if (plan_row_scaled_two_kind<CW, CN>(p.M, p.N, narrow_cost, tn1, tn2)) {
+        p.tiles_m = (int)((p.M + CW::BM - 1) / CW::BM);
+        p.tn1 = tn1;
+        p.tn2 = tn2;
+        p.n_split = (int64_t)tn1 * CW::BN;
+        const int per1 = (p.tiles_m * tn1 + kNumXcd - 1) / kNumXcd;
+        const int per2 = (p.tiles_m * tn2 + kNumXcd - 1) / kNumXcd;
+        const dim3 grid((unsigned)(kNumXcd * (per1 + per2)));
+        log_plan(entry, p.M, p.N, p.K, kinds, tn1, tn2, 1, (int)grid.x);
+        if (bf16_out)
+            hipLaunchKernelGGL((wgrad_two_kind_kernel<CW, CN, kOutBF16, kPow2>), grid,
+                               dim3(CW::kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((wgrad_two_kind_kernel<CW, CN, kOutF32, kPow2>), grid,
+                               dim3(CW::kThreads), 0, stream, p);
+        return hipGetLastError();
+    }
+    log_plan(entry, p.M, p.N, p.K, wide, 0, 0, 1,
+             round_up((int)(((p.M + CW::BM - 1) / CW::BM) * ((p.N + CW::BN - 1) / CW::BN)),
+                      kNumXcd));
+    return bf16_out ? launch_dense<CW, kOutBF16, kPow2>(p, stream)
+                    : launch_dense<CW, kOutF32, kPow2>(p, stream);
+}
+
+}  // namespace
+
 hipError_t launch_block_gemm_wgrad(const void *a, const float *sa, const void *b,
                                    const float *sb, void *c, bool bf16_out, int64_t M, int64_t N,
-                                   int64_t K, hipStream_t stream) {
+                                   int64_t K, bool pow2, hipStream_t stream) {
     GemmParams p{};
     p.a = static_cast<const uint8_t *>(a);
     p.sa = sa;
@@ -1836,30 +1898,12 @@ hipError_t launch_block_gemm_wgrad(const void *a, const float *sa, const void *b
     p.group_m = 8;
     p.ksplit = 1;
     p.kb_per_split = p.G;
-    int tn1, tn2;
-    if (plan_wgrad_two_kind(M, N, tn1, tn2)) {
-        p.tiles_m = (int)((M + WgradTile::BM - 1) / WgradTile::BM);
-        p.tn1 = tn1;
-        p.tn2 = tn2;
-        p.n_split = (int64_t)tn1 * WgradTile::BN;
-        const int per1 = (p.tiles_m * tn1 + kNumXcd - 1) / kNumXcd;
-        const int per2 = (p.tiles_m * tn2 + kNumXcd - 1) / kNumXcd;
-        const dim3 grid((unsigned)(kNumXcd * (per1 + per2)));
-        log_plan("block_gemm_wgrad", M, N, K, "128x256+128x192", tn1, tn2, 1, (int)grid.x);
-        if (bf16_out)
-            hipLaunchKernelGGL((wgrad_two_kind_kernel<kOutBF16>), grid, dim3(WgradTile::kThreads),
-                               0, stream, p);
-        else
-            hipLaunchKernelGGL((wgrad_two_kind_kernel<kOutF32>), grid, dim3(WgradTile::kThreads),
-                               0, stream, p);
-        return hipGetLastError();
-    }
-    log_plan("block_gemm_wgrad", M, N, K, "128x256", 0, 0, 1,
-             round_up((int)(((M + WgradTile::BM - 1) / WgradTile::BM) *
-                            ((N + WgradTile::BN - 1) / WgradTile::BN)),
-                      kNumXcd));
-    return bf16_out ? launch_dense<WgradTile, kOutBF16, false>(p, stream)
-                    : launch_dense<WgradTile, kOutF32, false>(p, stream);
+    if (pow2)
+        return launch_wgrad<WgradPow2Tile, WgradPow2NarrowTile, true>(
+            p, bf16_out, kWgradPow2NarrowCost, "block_gemm_wgrad_pow2", "256x256+256x192",
+            "256x256", stream);
+    return launch_wgrad<WgradTile, WgradNarrowTile, false>(
+        p, bf16_out, kWgradNarrowCost, "block_gemm_wgrad", "128x256+128x192", "128x256", stream);
 }
 
 hipError_t launch_grouped_gemm(const void *a, const float *sa, const void *w, const float *sw,

@@ -18,7 +18,7 @@ hipError_t launch_quant_weight_128x128(const void *w, int64_t N, int64_t K, void
 // 128x1 tiles (128 rows of one column) of x [M][K], written transposed:
 // q_t [K][M], scales_t [K][ceil(M/128)].
 hipError_t launch_quant_act_128x1_t(const void *x, int64_t M, int64_t K, void *q_t,
-                                    float *scales_t, hipStream_t stream);
+                                    float *scales_t, bool pow2, hipStream_t stream);
 
 // E4M3 weights [N][K] with 128x128 block scales [ceil(N/128)][ceil(K/128)],
 // transposed: q_t [K][N], scales_t [ceil(K/128)][ceil(N/128)].
@@ -31,9 +31,10 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // C[M][N] = sum_kb sa[m][kb] sb[n][kb] sum_{k in kb} a[m][k] b[n][k]: one
 // scale per row and K block on both operands (the Wgrad GEMM).
+// pow2: every scale is a power of two, applied by the block-scaled MFMA.
 hipError_t launch_block_gemm_wgrad(const void *a, const float *sa, const void *b,
                                    const float *sb, void *c, bool bf16_out, int64_t M, int64_t N,
-                                   int64_t K, hipStream_t stream);
+                                   int64_t K, bool pow2, hipStream_t stream);
 
 // pow2: every scale is a power of two, applied by the block-scaled MFMA.
 hipError_t launch_block_gemm(const void *a, const float *sa, const void *w, const float *sw,

@@ -229,7 +229,7 @@ constexpr int kTBlocksPerCU = 2;       // resident workgroups per CU (VGPR-bound
 constexpr int kTCUs = 256;
 __device__ __forceinline__ int tswz(int r) { return 16 * ((r >> 5) & 3); }
 
-template <bool kVec, bool kVecOut>
+template <bool kVec, bool kVecOut, bool kPow2>
 __global__ __launch_bounds__(kTThreads) void quant_act_128x1_t_kernel(
     const uint16_t *__restrict__ x, uint8_t *__restrict__ q_t, float *__restrict__ scales_t,
     int64_t M, int64_t K, int64_t GM, int64_t KT) {
@@ -284,16 +284,17 @@ __global__ __launch_bounds__(kTThreads) void quant_act_128x1_t_kernel(
         amax = fmaxf(amax, __shfl_xor(amax, 1));
         amax = fmaxf(amax, __shfl_xor(amax, 2));
         // As in the 1x128 kernel: when every column of the wave has amax >=
-        // 2^-60, one branch-free path (constant-division scale, reciprocal +
-        // FMA quotients) serves the wave; otherwise the per-group selection.
+        // 2^-60 (with power-of-two scales: amax > 0), one branch-free path
+        // (constant-division or power-of-two scale, reciprocal + FMA
+        // quotients) serves the wave; otherwise the per-group selection.
         float y[32], s;
-        if (__all(amax >= 0x1p-60f)) {
-            s = scale_fast(amax);
+        if (__all(kPow2 ? amax > 0.0f : amax >= 0x1p-60f)) {
+            s = kPow2 ? scale_pow2(amax) : scale_fast(amax);
             const float r = 1.0f / s;
 #pragma unroll
             for (int i = 0; i < 32; ++i) y[i] = quot_fast(f[i], s, r);
         } else {
-            const QuotientCtx qc(amax);
+            const QuotientCtx qc(amax, kPow2);
             s = qc.s;
 #pragma unroll
             for (int i = 0; i < 32; ++i) y[i] = qc(f[i]);
@@ -483,8 +484,11 @@ hipError_t launch_quant_act_1x128(const void *x, int64_t M, int64_t K, void *q, 
                 : quant_act<false>(x, M, K, q, scales, stream);
 }
 
-hipError_t launch_quant_act_128x1_t(const void *x, int64_t M, int64_t K, void *q_t,
-                                    float *scales_t, hipStream_t stream) {
+namespace {
+
+template <bool kPow2>
+hipError_t quant_act_128x1_t(const void *x, int64_t M, int64_t K, void *q_t, float *scales_t,
+                             hipStream_t stream) {
     const int64_t GM = (M + kTRows - 1) / kTRows;
     const int64_t KT = (K + kTCols - 1) / kTCols;
     const int64_t ntiles = GM * KT;
@@ -494,18 +498,26 @@ hipError_t launch_quant_act_128x1_t(const void *x, int64_t M, int64_t K, void *q
     const uint16_t *xx = static_cast<const uint16_t *>(x);
     uint8_t *qq = static_cast<uint8_t *>(q_t);
     if (vec && vec_out)
-        hipLaunchKernelGGL((quant_act_128x1_t_kernel<true, true>), grid, dim3(kTThreads), 0,
-                           stream, xx, qq, scales_t, M, K, GM, KT);
+        hipLaunchKernelGGL((quant_act_128x1_t_kernel<true, true, kPow2>), grid, dim3(kTThreads),
+                           0, stream, xx, qq, scales_t, M, K, GM, KT);
     else if (vec)
-        hipLaunchKernelGGL((quant_act_128x1_t_kernel<true, false>), grid, dim3(kTThreads), 0,
-                           stream, xx, qq, scales_t, M, K, GM, KT);
+        hipLaunchKernelGGL((quant_act_128x1_t_kernel<true, false, kPow2>), grid,
+                           dim3(kTThreads), 0, stream, xx, qq, scales_t, M, K, GM, KT);
     else if (vec_out)
-        hipLaunchKernelGGL((quant_act_128x1_t_kernel<false, true>), grid, dim3(kTThreads), 0,
-                           stream, xx, qq, scales_t, M, K, GM, KT);
+        hipLaunchKernelGGL((quant_act_128x1_t_kernel<false, true, kPow2>), grid,
+                           dim3(kTThreads), 0, stream, xx, qq, scales_t, M, K, GM, KT);
     else
-        hipLaunchKernelGGL((quant_act_128x1_t_kernel<false, false>), grid, dim3(kTThreads), 0,
-                           stream, xx, qq, scales_t, M, K, GM, KT);
+        hipLaunchKernelGGL((quant_act_128x1_t_kernel<false, false, kPow2>), grid,
+                           dim3(kTThreads), 0, stream, xx, qq, scales_t, M, K, GM, KT);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_act_128x1_t(const void *x, int64_t M, int64_t K, void *q_t,
+                                    float *scales_t, bool pow2, hipStream_t stream) {
+    return pow2 ? quant_act_128x1_t<true>(x, M, K, q_t, scales_t, stream)
+                : quant_act_128x1_t<false>(x, M, K, q_t, scales_t, stream);
 }
 
 hipError_t launch_transpose_weight(const void *q, const float *s, int64_t N, int64_t K,

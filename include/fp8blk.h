@@ -298,6 +298,32 @@ fp8_status fp8_block_gemm_wgrad(const void *dy_t, const float *dy_t_scales,
                                 int64_t T, void *hip_stream);
 
 /*
+ * The backward pair with power-of-two scales (the rule of the _pow2
+ * quantizers above, on the matrix core's block-scaled MFMA; page
+ * "kailasan.com recruit 147436", passage on matrix units taking the
+ * per-group scaling factors themselves).
+ *   fp8_quant_act_128x1_t_pow2: fp8_quant_act_128x1_t with each 128x1
+ *     group's scale the smallest power of two s with 448 s >= amax (at least
+ *     2^-126; an all-zero group stores 2^-126 and zero bytes).
+ *   fp8_block_gemm_wgrad_pow2: fp8_block_gemm_wgrad on such operands.  Each
+ *     operand row's E8M0 code goes to the MFMA with that row, and the MFMA
+ *     accumulates the scaled K blocks in FP32 itself, so no per-output
+ *     scales are held and the tiles are 256 rows tall (the FP32-scale Wgrad
+ *     uses 128).  Only the scales' exponent fields are read: a scale that is
+ *     not a power of two gives a result computed with its exponent alone
+ *     (not checked).
+ * Arguments, layouts, requirements and errors are those of the plain entry
+ * points.
+ */
+fp8_status fp8_quant_act_128x1_t_pow2(const void *x_bf16, int64_t M, int64_t K,
+                                      void *q_t, float *scales_t,
+                                      void *hip_stream);
+fp8_status fp8_block_gemm_wgrad_pow2(const void *dy_t, const float *dy_t_scales,
+                                     const void *x_t, const float *x_t_scales,
+                                     void *dw, int out_dtype, int64_t N,
+                                     int64_t K, int64_t T, void *hip_stream);
+
+/*
  * fp8_block_gemm for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  * Arguments, layouts, results and errors are those of fp8_block_gemm with no

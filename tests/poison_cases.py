@@ -105,6 +105,15 @@ def run_cases():
         qy, sy = F.fp8_quant_act_128x1_t(act(10, t, n))
         qx, sx = F.fp8_quant_act_128x1_t(act(11, t, k))
         keep(name, F.fp8_block_gemm_wgrad(qy, sy, qx, sx, out_dtype="f32"))
+    # pow2 Wgrad (two-stage 256-row tiles): both widths with ragged last
+    # tiles (dW 4100 x 6016 over 640 tokens: 5 K blocks, a partial scale
+    # chunk), and one width
+    for name, (n, k, t) in [("wgrad_pow2_two_kind", (4100, 6016, 640)),
+                            ("wgrad_pow2_small", (520, 896, 256))]:
+        qy, sy = F.fp8_quant_act_128x1_t_pow2(act(12, t, n))
+        qx, sx = F.fp8_quant_act_128x1_t_pow2(act(13, t, k))
+        keep(name + "_q", qy)
+        keep(name, F.fp8_block_gemm_wgrad_pow2(qy, sy, qx, sx, out_dtype="f32"))
     return out
 
 

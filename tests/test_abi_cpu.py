@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
         + ["fp8_quant_act_128x1_t", "fp8_transpose_weight_128x128", "fp8_block_gemm_wgrad"]
         + ["fp8_gemm_workspace_bytes", "fp8_status_string", "fp8_block_gemm_noalloc",
            "fp8_block_gemm_fused_quant", "fp8_fused_quant_workspace_bytes",
-           "fp8_fused_quant_kernel_workspace_bytes", "fp8_block_gemm_dgrad"])
+           "fp8_fused_quant_kernel_workspace_bytes", "fp8_block_gemm_dgrad",
+           "fp8_quant_act_128x1_t_pow2", "fp8_block_gemm_wgrad_pow2"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -255,9 +256,10 @@ def test_noalloc_gemm_argument_errors():
     assert 0 < worst <= 8 << 20
 
 
-def test_backward_argument_errors():
+@pytest.mark.parametrize("suffix", SUFFIXES)
+def test_backward_argument_errors(suffix):
     lib = B.lib()
-    q = lib.fp8_quant_act_128x1_t
+    q = getattr(lib, "fp8_quant_act_128x1_t" + suffix)
     assert q(NUL, 4, 128, A16, A16, NUL) == B.FP8_ERR_NULL
     assert q(A16, -1, 128, A16, A16, NUL) == B.FP8_ERR_SHAPE
     assert q(NUL, 0, 128, NUL, NUL, NUL) == B.FP8_OK
@@ -267,7 +269,7 @@ def test_backward_argument_errors():
     assert t(A16, A16, -1, 128, A16, A16, NUL) == B.FP8_ERR_SHAPE
     assert t(NUL, NUL, 0, 128, NUL, NUL, NUL) == B.FP8_OK
     assert t(A16, ctypes.c_void_p(0x10002), 128, 128, A16, A16, NUL) == B.FP8_ERR_ALIGN
-    w = lib.fp8_block_gemm_wgrad
+    w = getattr(lib, "fp8_block_gemm_wgrad" + suffix)
 
     def wg(a=A16, sa=A16, b=A16, sb=A16, c=A16, dt=B.FP8_OUT_F32, N=256, K=256, T=512):
         return w(a, sa, b, sb, c, dt, N, K, T, NUL)

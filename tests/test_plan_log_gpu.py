@@ -4,8 +4,8 @@ The flag is read once per process, so the calls run in a child Python
 process started with FP8BLK_LOG=1; its stderr must name the expected plan
 for each entry point (two tile widths for 4096 x 7168, split-K for a small
 M with a workspace, the unsplit small-tile plan without one, the grouped,
-fused, Dgrad and Wgrad kernels, and the fused entry point's staged plan
-with its workspace).
+fused, Dgrad and Wgrad kernels, the fused entry point's staged plan with its
+workspace, and the pow2 Wgrad's 256-row tiles).
 """
 import os
 import subprocess
@@ -51,6 +51,9 @@ dyt = torch.randn(256, 512, device="cuda").to(torch.bfloat16)
 qx, sx = F.fp8_quant_act_128x1_t(xt)
 qy, sy = F.fp8_quant_act_128x1_t(dyt)
 F.fp8_block_gemm_wgrad(qy, sy, qx, sx)
+qy2, sy2 = F.fp8_quant_act_128x1_t_pow2(dyt)
+qx2, sx2 = F.fp8_quant_act_128x1_t_pow2(xt)
+F.fp8_block_gemm_wgrad_pow2(qy2, sy2, qx2, sx2)
 torch.cuda.synchronize()
 print("child done", flush=True)
 """ % ROOT
@@ -77,6 +80,7 @@ def test_plan_log_lines():
         "block_grouped_gemm M=300 N=256 K=256 tiles=128x256",
         "block_gemm_dgrad (W read transposed) M=64 N=2048 K=1024",
         "block_gemm_wgrad M=512 N=384 K=256",
+        "block_gemm_wgrad_pow2 M=512 N=384 K=256 tiles=256x256",
     ]
     assert len(lines) == len(expect), lines
     for ln, e in zip(lines, expect):
