@@ -379,7 +379,8 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=None):
     bwd = [n for n in ("bwd_quant_128x1_t_4096x7168", "bwd_transpose_weight_7168x7168",
                        "bwd_dgrad_4096x7168x7168", "bwd_dgrad_transposed_reads_4096x7168x7168",
                        "bwd_wgrad_7168x7168_over_4096", "pow2_bwd_quant_128x1_t_4096x7168",
-                       "pow2_bwd_wgrad_7168x7168_over_4096") if want(n)]
+                       "pow2_bwd_wgrad_7168x7168_over_4096",
+                       "pow2_bwd_dgrad_transposed_reads_4096x7168x7168") if want(n)]
     if bwd:
         dy = to_dev_bf16(torch, I.activations(np.random.default_rng(7), M, N, 0.0, 1.0)[0])
         if want("bwd_quant_128x1_t_4096x7168"):
@@ -426,6 +427,16 @@ def measure_parts(torch, F, I, X, Wb, qa, sa, qw, sw, C, only=None):
                         *P.timed(lambda: F.fp8_block_gemm_wgrad_pow2(qdy_t, sdy_t, qx_t, sx_t,
                                                                      out_dtype="f32", dw=dw)), fl)
             del qdy_t, sdy_t, qx_t, sx_t, dw
+        if want("pow2_bwd_dgrad_transposed_reads_4096x7168x7168"):
+            # Dgrad on pow2-quantized dY and forward weights
+            pdy, psdy = F.fp8_quant_act_1x128_pow2(dy)
+            pw, psw = F.fp8_quant_weight_128x128_pow2(Wb)
+            dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+            P.add_flops("pow2_bwd_dgrad_transposed_reads_4096x7168x7168",
+                        *P.timed(lambda: F.fp8_block_gemm_dgrad_pow2(pdy, psdy, pw, psw,
+                                                                     out_dtype="bf16", dx=dx)),
+                        fl)
+            del pdy, psdy, pw, psw, dx
         del dy, qdy, sdy, qwt, swt
 
     # decode GEMM, 256 x 2048 x 7168 (split-K with workspace)

@@ -14,5 +14,5 @@ from .binding import (  # noqa: F401
     fp8_transpose_weight_128x128, fp8_block_gemm_wgrad, fp8_block_gemm_fused_quant,
     fp8_block_gemm_noalloc, fp8_block_gemm_dgrad, fp8_fused_quant_workspace_bytes,
     fp8_fused_quant_kernel_workspace_bytes, fp8_quant_act_128x1_t_pow2,
-    fp8_block_gemm_wgrad_pow2,
+    fp8_block_gemm_wgrad_pow2, fp8_block_gemm_dgrad_pow2,
 )

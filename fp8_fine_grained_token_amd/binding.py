@@ -59,6 +59,8 @@ _SIGNATURES = {
                                   ctypes.c_int),
     "fp8_block_gemm_dgrad": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P,
                               ctypes.c_size_t, _P], ctypes.c_int),
+    "fp8_block_gemm_dgrad_pow2": ([_P, _P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P,
+                                   ctypes.c_size_t, _P], ctypes.c_int),
     "fp8_block_gemm_fused_quant": ([_P, _P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, _P,
                                     _P, ctypes.c_size_t, _P], ctypes.c_int),
     "fp8_fused_quant_workspace_bytes": ([_I64, _I64, _I64, ctypes.c_int], ctypes.c_size_t),
@@ -275,6 +277,17 @@ def fp8_block_gemm_dgrad(dy, sdy, w, sw, out_dtype="bf16", dx=None, workspace=No
     """dX [M][K] = dY [M][N] W [N][K]: dy E4M3 [M][N] with scales [M][N/128]
     (1x128 along N), w the forward weights E4M3 [N][K] with 128x128 block
     scales [N/128][K/128], read transposed inside the GEMM."""
+    return _dgrad("fp8_block_gemm_dgrad", dy, sdy, w, sw, out_dtype, dx, workspace, stream)
+
+
+def fp8_block_gemm_dgrad_pow2(dy, sdy, w, sw, out_dtype="bf16", dx=None, workspace=None,
+                              stream=None):
+    """As fp8_block_gemm_dgrad, for power-of-two scales."""
+    return _dgrad("fp8_block_gemm_dgrad_pow2", dy, sdy, w, sw, out_dtype, dx, workspace,
+                  stream)
+
+
+def _dgrad(fn, dy, sdy, w, sw, out_dtype, dx, workspace, stream):
     torch = _torch()
     _rank(dy, "dy", 2)
     _rank(w, "w", 2)
@@ -289,7 +302,6 @@ def fp8_block_gemm_dgrad(dy, sdy, w, sw, out_dtype="bf16", dx=None, workspace=No
         _shape(sw, "sw", (N // 128, K // 128))
     _shape(dx, "dx", (M, K))
     wp, wb = _workspace_args(workspace)
-    fn = "fp8_block_gemm_dgrad"
     _check(getattr(lib(), fn)(_dev(dy, "dy", torch.uint8), _dev(sdy, "sdy", torch.float32),
                               _dev(w, "w", torch.uint8), _dev(sw, "sw", torch.float32),
                               _dev(dx, "dx", tdt), code, M, N, K, wp, wb, _stream_handle(stream)),

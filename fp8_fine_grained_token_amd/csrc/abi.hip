@@ -150,6 +150,22 @@ fp8_status wgrad(const void *dy_t, const float *dy_t_scales, const void *x_t,
                                                     as_stream(hip_stream)));
 }
 
+fp8_status dgrad(const void *dy_e4m3, const float *dy_scales, const void *w_e4m3,
+                 const float *w_scales, void *dx, int out_dtype, int64_t M, int64_t N, int64_t K,
+                 void *workspace, size_t workspace_bytes, bool pow2, void *hip_stream) {
+    // output M x K, inner dimension N
+    fp8_status st = check_gemm_common(dy_e4m3, dy_scales, w_e4m3, w_scales, dx, out_dtype, M, K,
+                                      N, workspace, workspace_bytes);
+    if (st != FP8_OK || M == 0 || K == 0) return st;
+    if (N == 0) return FP8_ERR_SHAPE;
+    // W is addressed through one buffer resource with 32-bit offsets
+    if (N * K >= ((int64_t)1 << 32)) return FP8_ERR_SHAPE;
+    clear_last_error();
+    return from_hip(fp8blk::launch_block_gemm_dgrad(dy_e4m3, dy_scales, w_e4m3, w_scales, dx,
+                                                    out_dtype == FP8_OUT_BF16, M, N, K, workspace,
+                                                    workspace_bytes, pow2, as_stream(hip_stream)));
+}
+
 // Plan of fp8_block_gemm_fused_quant.  The fused kernel quantizes a tile's
 // activation rows again for every 256-column tile of C, and copies bf16 rows
 // (twice the bytes of E4M3 ones) into 64-row tiles, so it beats the
@@ -235,17 +251,17 @@ fp8_status fp8_block_gemm_dgrad(const void *dy_e4m3, const float *dy_scales,
                                 const void *w_e4m3, const float *w_scales, void *dx,
                                 int out_dtype, int64_t M, int64_t N, int64_t K, void *workspace,
                                 size_t workspace_bytes, void *hip_stream) {
-    // output M x K, inner dimension N
-    fp8_status st = check_gemm_common(dy_e4m3, dy_scales, w_e4m3, w_scales, dx, out_dtype, M, K,
-                                      N, workspace, workspace_bytes);
-    if (st != FP8_OK || M == 0 || K == 0) return st;
-    if (N == 0) return FP8_ERR_SHAPE;
-    // W is addressed through one buffer resource with 32-bit offsets
-    if (N * K >= ((int64_t)1 << 32)) return FP8_ERR_SHAPE;
-    clear_last_error();
-    return from_hip(fp8blk::launch_block_gemm_dgrad(dy_e4m3, dy_scales, w_e4m3, w_scales, dx,
-                                                    out_dtype == FP8_OUT_BF16, M, N, K, workspace,
-                                                    workspace_bytes, as_stream(hip_stream)));
+    return dgrad(dy_e4m3, dy_scales, w_e4m3, w_scales, dx, out_dtype, M, N, K, workspace,
+                 workspace_bytes, false, hip_stream);
+}
+
+fp8_status fp8_block_gemm_dgrad_pow2(const void *dy_e4m3, const float *dy_scales,
+                                     const void *w_e4m3, const float *w_scales, void *dx,
+                                     int out_dtype, int64_t M, int64_t N, int64_t K,
+                                     void *workspace, size_t workspace_bytes,
+                                     void *hip_stream) {
+    return dgrad(dy_e4m3, dy_scales, w_e4m3, w_scales, dx, out_dtype, M, N, K, workspace,
+                 workspace_bytes, true, hip_stream);
 }
 
 fp8_status fp8_block_gemm_fused_quant(const void *x_bf16, const void *w_e4m3,

@@ -2030,10 +2030,44 @@ hipError_t launch_block_gemm_fused_quant(const void *x, const void *w, const flo
 // activations (inner dimension N) and W read transposed from its forward
 // layout; the same plan as fp8_block_gemm for an M x Kx output over N
 // (256 x 256 tiles, or 128 x 64 tiles with split-K for small M).
+namespace {
+
+// Launches the planned Dgrad (W read transposed) for one output type and
+// scale mode: the forward GEMM's plans (see block_gemm).
+template <int OUT, bool kPow2>
+hipError_t dgrad_gemm(GemmParams p, const Plan &pl, void *dx, hipStream_t stream) {
+    if (pl.big && pl.tn2 > 0) {
+        // the forward GEMM's two tile widths
+        p.tiles_m = (int)((p.M + 255) / 256);
+        p.tn1 = pl.tn1;
+        p.tn2 = pl.tn2;
+        p.n_split = (int64_t)pl.tn1 * BigTile::BN;
+        const int per1 = (p.tiles_m * p.tn1 + kNumXcd - 1) / kNumXcd;
+        const int per2 = (p.tiles_m * p.tn2 + kNumXcd - 1) / kNumXcd;
+        const int grid = kNumXcd * (per1 + per2);
+        hipLaunchKernelGGL((dense_gemm_two_kind_kernel<OUT, kPow2, true>), dim3(grid),
+                           dim3(BigTile::kThreads), 0, stream, p);
+        return hipGetLastError();
+    }
+    if (pl.big) return launch_dense<BigTile, OUT, kPow2, true>(p, stream);
+    if (p.ksplit > 1) {
+        hipError_t e = launch_dense<SmallTile, kOutPartial, kPow2, true>(p, stream);
+        if (e != hipSuccess) return e;
+        const int64_t MN = p.M * p.N;
+        const int64_t blocks = (MN / 4 + 255) / 256;
+        hipLaunchKernelGGL(splitk_reduce_kernel<OUT>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           p.partial, dx, MN, p.ksplit);
+        return hipGetLastError();
+    }
+    return launch_dense<SmallTile, OUT, kPow2, true>(p, stream);
+}
+
+}  // namespace
+
 hipError_t launch_block_gemm_dgrad(const void *dy, const float *sdy, const void *w,
                                    const float *sw, void *dx, bool bf16_out, int64_t M,
                                    int64_t N, int64_t Kx, void *workspace, size_t workspace_bytes,
-                                   hipStream_t stream) {
+                                   bool pow2, hipStream_t stream) {
     GemmParams p{};
     p.a = static_cast<const uint8_t *>(dy);
     p.sa = sdy;
@@ -2053,42 +2087,14 @@ hipError_t launch_block_gemm_dgrad(const void *dy, const float *sdy, const void 
     p.ksplit = pl.ksplit;
     p.kb_per_split = pl.kb_per_split;
     p.partial = static_cast<float *>(workspace);
-    log_dense_plan("block_gemm_dgrad (W read transposed)", p, pl);
-    if (pl.big && pl.tn2 > 0) {
-        // the forward GEMM's two tile widths (see block_gemm)
-        p.tiles_m = (int)((p.M + 255) / 256);
-        p.tn1 = pl.tn1;
-        p.tn2 = pl.tn2;
-        p.n_split = (int64_t)pl.tn1 * BigTile::BN;
-        const int per1 = (p.tiles_m * p.tn1 + kNumXcd - 1) / kNumXcd;
-        const int per2 = (p.tiles_m * p.tn2 + kNumXcd - 1) / kNumXcd;
-        const int grid = kNumXcd * (per1 + per2);
-        if (bf16_out)
-            hipLaunchKernelGGL((dense_gemm_two_kind_kernel<kOutBF16, false, true>), dim3(grid),
-                               dim3(BigTile::kThreads), 0, stream, p);
-        else
-            hipLaunchKernelGGL((dense_gemm_two_kind_kernel<kOutF32, false, true>), dim3(grid),
-                               dim3(BigTile::kThreads), 0, stream, p);
-        return hipGetLastError();
-    }
-    if (pl.big)
-        return bf16_out ? launch_dense<BigTile, kOutBF16, false, true>(p, stream)
-                        : launch_dense<BigTile, kOutF32, false, true>(p, stream);
-    if (p.ksplit > 1) {
-        hipError_t e = launch_dense<SmallTile, kOutPartial, false, true>(p, stream);
-        if (e != hipSuccess) return e;
-        const int64_t MN = p.M * p.N;
-        const int64_t blocks = (MN / 4 + 255) / 256;
-        if (bf16_out)
-            hipLaunchKernelGGL(splitk_reduce_kernel<kOutBF16>, dim3((unsigned)blocks), dim3(256),
-                               0, stream, p.partial, dx, MN, p.ksplit);
-        else
-            hipLaunchKernelGGL(splitk_reduce_kernel<kOutF32>, dim3((unsigned)blocks), dim3(256),
-                               0, stream, p.partial, dx, MN, p.ksplit);
-        return hipGetLastError();
-    }
-    return bf16_out ? launch_dense<SmallTile, kOutBF16, false, true>(p, stream)
-                    : launch_dense<SmallTile, kOutF32, false, true>(p, stream);
+    log_dense_plan(pow2 ? "block_gemm_dgrad_pow2 (W read transposed)"
+                        : "block_gemm_dgrad (W read transposed)",
+                   p, pl);
+    if (pow2)
+        return bf16_out ? dgrad_gemm<kOutBF16, true>(p, pl, dx, stream)
+                        : dgrad_gemm<kOutF32, true>(p, pl, dx, stream);
+    return bf16_out ? dgrad_gemm<kOutBF16, false>(p, pl, dx, stream)
+                    : dgrad_gemm<kOutF32, false>(p, pl, dx, stream);
 }
 
 }  // namespace fp8blk

@@ -62,10 +62,11 @@ hipError_t launch_block_gemm_fused_quant(const void *x, const void *w, const flo
 
 // Dgrad dX [M][Kx] = dY [M][N] W [N][Kx], W E4M3 with 128x128 block scales
 // [N/128][Kx/128] in its forward layout, read transposed in LDS.
+// pow2: every scale is a power of two, applied by the block-scaled MFMA.
 hipError_t launch_block_gemm_dgrad(const void *dy, const float *sdy, const void *w,
                                    const float *sw, void *dx, bool bf16_out, int64_t M,
                                    int64_t N, int64_t Kx, void *workspace, size_t workspace_bytes,
-                                   hipStream_t stream);
+                                   bool pow2, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const void *a, const float *sa, const void *w, const float *sw,
                                const int32_t *offsets, int64_t E, int64_t T, void *c,

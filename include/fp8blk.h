@@ -373,6 +373,21 @@ fp8_status fp8_block_gemm_dgrad(const void *dy_e4m3, const float *dy_scales,
                                 int out_dtype, int64_t M, int64_t N, int64_t K,
                                 void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/*
+ * fp8_block_gemm_dgrad with every scale a power of two (dY from
+ * fp8_quant_act_1x128_pow2, W from fp8_quant_weight_128x128_pow2): the
+ * block-scaled MFMA applies the scales' E8M0 codes and accumulates each K
+ * block itself, as in fp8_block_gemm_pow2.  Only the scales' exponent fields
+ * are read.  Arguments, layouts, workspace and errors are those of
+ * fp8_block_gemm_dgrad; results equal fp8_block_gemm_pow2(dy, W^T) bit for
+ * bit where both run the same K splits.
+ */
+fp8_status fp8_block_gemm_dgrad_pow2(const void *dy_e4m3, const float *dy_scales,
+                                     const void *w_e4m3, const float *w_scales, void *dx,
+                                     int out_dtype, int64_t M, int64_t N, int64_t K,
+                                     void *workspace, size_t workspace_bytes,
+                                     void *hip_stream);
+
 /* Workspace bytes that let fp8_block_gemm use its split-K path for this
  * shape (0 when the shape does not use it). */
 size_t fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int out_dtype);

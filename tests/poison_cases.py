@@ -99,6 +99,10 @@ def run_cases():
         qw, sw = F.fp8_quant_weight_128x128(wts(9, n, kx))
         keep(name, F.fp8_block_gemm_dgrad(qd, sd, qw, sw, out_dtype="f32",
                                           workspace=ws_for(m, kx, n) if split else None))
+    # pow2 Dgrad reading W transposed, two widths
+    qd, sd = F.fp8_quant_act_1x128_pow2(act(14, 4096, 384))
+    qw, sw = F.fp8_quant_weight_128x128_pow2(wts(15, 384, 7168))
+    keep("dgrad_pow2_two_kind", F.fp8_block_gemm_dgrad_pow2(qd, sd, qw, sw, out_dtype="f32"))
     # Wgrad: the two-width plan of dW 7168 x 7168 (over 256 tokens) and a
     # single-width one
     for name, (n, k, t) in [("wgrad_two_kind", (7168, 7168, 256)), ("wgrad_small", (512, 384, 384))]:

@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
         + ["fp8_gemm_workspace_bytes", "fp8_status_string", "fp8_block_gemm_noalloc",
            "fp8_block_gemm_fused_quant", "fp8_fused_quant_workspace_bytes",
            "fp8_fused_quant_kernel_workspace_bytes", "fp8_block_gemm_dgrad",
-           "fp8_quant_act_128x1_t_pow2", "fp8_block_gemm_wgrad_pow2"])
+           "fp8_quant_act_128x1_t_pow2", "fp8_block_gemm_wgrad_pow2",
+           "fp8_block_gemm_dgrad_pow2"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -139,12 +140,14 @@ def test_grouped_argument_errors(suffix):
     assert grouped_(lib, T=0, E=0, a=NUL, sa=NUL, off=NUL, c=NUL) == B.FP8_OK
 
 
-def test_dgrad_argument_errors():
+@pytest.mark.parametrize("suffix", SUFFIXES)
+def test_dgrad_argument_errors(suffix):
     lib = B.lib()
 
     def dg(dy=A16, sdy=A16, w=A16, sw=A16, dx=A16, dt=B.FP8_OUT_BF16, M=128, N=256, K=512,
            ws=NUL, wsb=0):
-        return lib.fp8_block_gemm_dgrad(dy, sdy, w, sw, dx, dt, M, N, K, ws, wsb, NUL)
+        return getattr(lib, "fp8_block_gemm_dgrad" + suffix)(dy, sdy, w, sw, dx, dt, M, N, K,
+                                                            ws, wsb, NUL)
     assert dg(N=200) == B.FP8_ERR_SHAPE          # inner dimension
     assert dg(K=500) == B.FP8_ERR_SHAPE          # output columns
     assert dg(M=-1) == B.FP8_ERR_SHAPE

@@ -8,6 +8,9 @@ path: every scale is a power of two, so applying it is exact, and the matrix
 core adds each scaled K block into its FP32 accumulator with one rounding.
 The GEMM's tiles (256 x 256 and 256 x 192, two LDS stages) are checked on
 ragged shapes and on both plans (one tile width, two widths).
+fp8_block_gemm_dgrad_pow2 (the forward weights read transposed) is checked
+against the oracle within the same bound, and FP32 bitwise against
+fp8_block_gemm_pow2 on the transposed copy of W, on every plan.
 """
 import numpy as np
 import pytest
@@ -127,3 +130,41 @@ def test_pow2_wgrad_workload_chain_sampled_rows_and_deterministic():
     R = oracle.rowscaled_gemm(qdy_o, sdy_o, qx_o, sx_o, rows)
     check_gemm(c0[torch().from_numpy(rows).cuda()], R, "f32", "pow2 wgrad workload rows",
                gemm_error_bound(qdy_o, sdy_o, qx_o, sx_o, rows, row_scaled_w=True))
+
+
+# ---- Dgrad on the forward weights, read transposed, power-of-two scales ---------
+
+@pytest.mark.parametrize("M,N,K", [
+    (64, 256, 384),      # small tiles, one output tile row
+    (300, 384, 640),     # small tiles, ragged M
+    (256, 7168, 2048),   # small tiles with split-K through a workspace
+    (4000, 1280, 7040),  # 256 x 256 tiles, ragged M, a half-used last tile
+    (4096, 512, 6144),   # 256 x 192 tiles only
+    (4096, 384, 7168),   # both tile widths
+])
+def test_pow2_dgrad_transposed_reads(M, N, K):
+    # against the oracle (every row up to 300, else rows of every tile)
+    # within the per-output bound, and FP32 bitwise equal to the pow2 GEMM
+    # on the transposed copy of W
+    rng = np.random.default_rng(M + 5 * N + 3 * K)
+    dy, _ = I.activations(rng, M, N, 0.01, 20.0)
+    w = I.weights(rng, (N, K))
+    qw, sw = oracle.quant_weight_128x128_pow2(w)
+    qdy, sdy = oracle.quant_act_1x128_pow2(dy)
+    qwt, swt = oracle.transpose_weight(qw, sw)
+    t = torch()
+    nbytes = B.fp8_gemm_workspace_bytes(M, K, N, "f32")
+    ws = t.empty(nbytes, dtype=t.uint8, device="cuda") if nbytes else None
+    d = [dev(qdy), dev(sdy), dev(qw), dev(sw)]
+    c32 = B.fp8_block_gemm_dgrad_pow2(*d, out_dtype="f32", workspace=ws)
+    c16 = B.fp8_block_gemm_dgrad_pow2(*d, out_dtype="bf16", workspace=ws)
+    ref = B.fp8_block_gemm_pow2(dev(qdy), dev(sdy), dev(qwt), dev(swt), out_dtype="f32",
+                                workspace=ws)
+    rows = np.arange(M) if M <= 300 else tile_rows(M, 256, per_tile=2)
+    log(f"  pow2 dgrad {M}x{N}x{K} (split-K workspace {nbytes} B): oracle on {rows.size} rows")
+    R = oracle.block_gemm(qdy, sdy, qwt, swt, rows)
+    b = gemm_error_bound(qdy, sdy, qwt, swt, rows, splits=max(1, nbytes // (M * K * 4)))
+    ri = t.from_numpy(rows).cuda()
+    check_gemm(c32[ri], R, "f32", f"pow2 dgrad {M}x{N}x{K} f32", b)
+    check_gemm(c16[ri], R, "bf16", f"pow2 dgrad {M}x{N}x{K} bf16", b)
+    assert t.equal(c32, ref), "transposed-read pow2 Dgrad differs from the pow2 GEMM on W^T"

@@ -9,7 +9,8 @@ GEMM case of tests/poison_cases.py (each tile kind and pipeline: dense two
 widths, one 256 x 256 round, small tiles with and without split-K, the
 no-allocation GEMM, grouped with partial scale chunks, power-of-two scales,
 the fused quantization with and without split-K, Dgrad reading W
-transposed, Wgrad in both plans, also with power-of-two scales)
+transposed (also with power-of-two scales), Wgrad in both plans (also with
+power-of-two scales))
 must give bitwise the same bytes with either library.  The poison build runs
 in a child process (the library is chosen when the process first loads it).
 """
