@@ -15,9 +15,12 @@ sustains on this work); the W warm-up steps; the K timed steps.
 Printed as one JSON line, with:
   * roofline: the dominant kernel (the GEMM), its algorithmic flops over its
     average duration measured with HIP events on its stream inside the timed
-    region, against the dense FP8 MFMA peak; the shader clock sampled over
-    the last part of a fixed untimed pre-roll of steps and the timed region;
-    the same kernel's flushed per-part fraction beside it;
+    region, against the dense FP8 MFMA peak; the shader clock of each XCD
+    over the timed steps, from its shader-clock and 100 MHz real-time
+    counters read on the GPU just before and just after them (the SMU's
+    reported GFX clock, sampled through amdsmi, beside it), and the fraction
+    against the peak at that clock; the same kernel's flushed per-part
+    fraction;
     traffic = HBM bytes per launch from committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE counters, scaled by the copy-kernel calibration, or null if
     the kernel source changed since;
@@ -55,6 +58,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+MAX_SCLK_MHZ = 2400.0      # the clock that peak is quoted at
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_dense_gemm.json")
 GEMM_SOURCE = os.path.join(ROOT, "fp8_fine_grained_token_amd", "csrc", "gemm.hip")
@@ -169,6 +173,61 @@ class ClockSampler:
         s = self.samples
         return {"mhz_mean": round(sum(s) / len(s), 1), "mhz_min": min(s), "mhz_max": max(s),
                 "samples": len(s), "max_sclk_mhz": self.max_mhz, "source": "amdsmi GFX clock"}
+
+
+class GpuClockProbe:
+    """Mean shader clock of each XCD between two probe launches on the
+    current stream, from its shader-clock counter (s_memtime) against the
+    100 MHz real-time counter (s_memrealtime), both read on the GPU by
+    _build/libfp8probe.so (the benchmark's probe, not the library)."""
+
+    WORKGROUPS = 64  # several per XCD, so every XCD is seen in both launches
+
+    def __init__(self, torch):
+        import ctypes
+        from fp8_fine_grained_token_amd import build as hip_build
+        self.torch = torch
+        self.error = None
+        self.bufs = [torch.zeros(3 * self.WORKGROUPS, dtype=torch.int64, device="cuda")
+                     for _ in range(2)]
+        try:
+            self.lib = ctypes.CDLL(hip_build.PROBE_LIB_PATH)
+            self.lib.fp8probe_clock.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+            self.lib.fp8probe_clock.restype = ctypes.c_int
+        except OSError as e:
+            self.lib, self.error = None, f"OSError: {e}"
+
+    def mark(self, i):
+        if self.lib is None:
+            return
+        stream = self.torch.cuda.current_stream().cuda_stream
+        rc = self.lib.fp8probe_clock(self.bufs[i].data_ptr(), self.WORKGROUPS, stream)
+        if rc != 0:
+            self.error = f"probe launch status {rc}"
+
+    def result(self):
+        """Call after a synchronization that follows mark(1)."""
+        if self.lib is None or self.error:
+            return {"mhz_mean": None, "error": self.error}
+        per = []
+        for i in range(2):
+            v = self.bufs[i].cpu().numpy().reshape(-1, 3)
+            d = {}
+            for xcd, t, r in v:
+                d.setdefault(int(xcd), (int(t), int(r)))
+            per.append(d)
+        mhz = {}
+        for xcd in sorted(set(per[0]) & set(per[1])):
+            dt = per[1][xcd][0] - per[0][xcd][0]
+            dr = per[1][xcd][1] - per[0][xcd][1]
+            if dr > 0 and dt > 0:
+                mhz[xcd] = round(dt / dr * 100.0, 1)
+        if not mhz:
+            return {"mhz_mean": None, "error": "no XCD seen in both probe launches"}
+        vals = list(mhz.values())
+        return {"mhz_mean": round(sum(vals) / len(vals), 1), "per_xcd_mhz": vals,
+                "source": "s_memtime over s_memrealtime (100 MHz) on each XCD, read by probe "
+                          "launches just before and just after the timed steps"}
 
 
 _GROUPED = []
@@ -679,15 +738,21 @@ def main():
             sampling = True
     if not sampling:
         clk.start()
+    probe = GpuClockProbe(torch)
     for _ in range(args.warmup):
         step(False)
+    probe.mark(0)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    probe.mark(1)
+    torch.cuda.synchronize()
     clock = clk.stop()
+    sclk = probe.result()
+    sclk["amdsmi_gfx_clock"] = clock
 
     ms_per_step = (t1 - t0) / args.steps * 1e3
     flops = 2 * M * N * K
@@ -698,7 +763,11 @@ def main():
     roof = {"bound": "mfma", "kernel": "dense_gemm_two_kind_kernel",
             "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic_from_counters(),
-            "gemm_us": round(gemm_ms * 1e3, 2), "sclk_timed_region": clock}
+            "gemm_us": round(gemm_ms * 1e3, 2), "sclk_timed_region": sclk}
+    if sclk.get("mhz_mean"):
+        # the same fraction against the FP8 peak at the clock the GPU ran at
+        roof["frac_at_running_clock"] = round(
+            achieved / (PEAK_FP8_TFLOPS * sclk["mhz_mean"] / MAX_SCLK_MHZ), 4)
     dense_part = result_tail.get("parts", {}).get("dense_gemm_4096x7168x7168")
     if dense_part:
         roof["frac_flushed_part"] = round(dense_part["frac_mfma"], 4)

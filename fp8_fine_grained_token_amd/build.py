@@ -9,6 +9,9 @@ It also builds _build/libfp8blk_poison.so, the same sources with
 FP8BLK_POISON_LDS defined (every LDS-DMA copy first poisons its destination):
 a race-check build that tests load through FP8BLK_LIB; the product path loads
 libfp8blk.so.
+
+And _build/libfp8probe.so from csrc/probe/clock.hip: the benchmark's
+shader-clock probe, kept out of the library.
 """
 from __future__ import annotations
 
@@ -22,6 +25,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(BUILD_DIR, "libfp8blk.so")
 POISON_LIB_PATH = os.path.join(BUILD_DIR, "libfp8blk_poison.so")
+PROBE_LIB_PATH = os.path.join(BUILD_DIR, "libfp8probe.so")
+PROBE_SRC = os.path.join(CSRC, "probe", "clock.hip")
 ARCH = "gfx950"
 
 
@@ -34,24 +39,27 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def _command(out: str, defines) -> list:
+def _command(out: str, defines, srcs=None) -> list:
     return [
         hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
         "-ffp-contract=off", "-fno-gpu-rdc", "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-Wall", "-Wno-unused-function",
         "-I" + os.path.join(os.path.dirname(HERE), "include"),
-    ] + ["-D" + d for d in defines] + ["-o", out] + sources()
+    ] + ["-D" + d for d in defines] + ["-o", out] + (srcs or sources())
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libfp8blk.so and the race-check
-    libfp8blk_poison.so (always rebuilds; the two compile in parallel)."""
+    """Compile every HIP source and link libfp8blk.so, the race-check
+    libfp8blk_poison.so and the clock probe libfp8probe.so (always rebuilds;
+    they compile in parallel)."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     jobs = []
-    for path, defines in ((LIB_PATH, []), (POISON_LIB_PATH, ["FP8BLK_POISON_LDS"])):
+    for path, defines, srcs in ((LIB_PATH, [], None),
+                                (POISON_LIB_PATH, ["FP8BLK_POISON_LDS"], None),
+                                (PROBE_LIB_PATH, [], [PROBE_SRC])):
         tmp = path + ".tmp%d" % os.getpid()
-        cmd = _command(tmp, defines)
+        cmd = _command(tmp, defines, srcs)
         if verbose:
             print(" ".join(cmd), flush=True)
         jobs.append((subprocess.Popen(cmd), tmp, path, cmd))
