@@ -383,6 +383,37 @@ def test_grouped_more_than_64_experts(case):
                grouped_error_bound(qa, sa, qw, sw, gi.offsets, np.arange(routed)))
 
 
+@pytest.mark.parametrize("pow2", [False, True])
+def test_grouped_expert_tails(pow2):
+    # Experts whose last 128-row M tile holds 1, 63, 64, 65, 127 or 128 rows
+    # (one to three M tiles each), two N tiles and 10 K blocks (a scale
+    # chunk boundary and a partial chunk); every routed row against the
+    # oracle, FP32 out.
+    counts = [64, 65, 127, 128, 192, 193, 1, 0, 63, 320]
+    E, T, N, K = len(counts), sum(counts) + 5, 512, 1280
+    gi = I.grouped_inputs(E, T, N, K, seed=640 + int(pow2), counts=counts)
+    if pow2:
+        qa, sa = oracle.quant_act_1x128_pow2(gi.a_bf16)
+        qw, sw = oracle.quant_weight_128x128_pow2(gi.w_bf16.reshape(E * N, K))
+        gemm = B.fp8_block_grouped_gemm_pow2
+    else:
+        qa, sa = oracle.quant_act_1x128(gi.a_bf16)
+        qw, sw = oracle.quant_weight_128x128(gi.w_bf16.reshape(E * N, K))
+        gemm = B.fp8_block_grouped_gemm
+    qw, sw = qw.reshape(E, N, K), sw.reshape(E, N // 128, K // 128)
+    R, found = oracle.grouped_gemm(qa, sa, qw, sw, gi.offsets)
+    t = torch()
+    c = t.full((T, N), 7.0, dtype=t.float32, device="cuda")
+    gemm(dev(qa), dev(sa), dev(qw), dev(sw), dev(gi.offsets.astype(np.int32)),
+         out_dtype="f32", c=c)
+    ch = host(c)
+    routed = int(gi.offsets[-1])
+    assert found[:routed].all()
+    assert np.all(ch[routed:] == 7.0), "unrouted rows were written"
+    check_gemm(c[:routed], R[:routed], "f32", f"grouped expert tails pow2={pow2}",
+               grouped_error_bound(qa, sa, qw, sw, gi.offsets, np.arange(routed)))
+
+
 def test_grouped_garbage_offsets_are_memory_safe():
     # Offsets beyond T and decreasing ranges are clamped/empty: no fault, and
     # rows outside [clamped off[0], clamped off[E]) stay untouched.
