@@ -176,12 +176,15 @@ class ClockSampler:
 
 
 class GpuClockProbe:
-    """Mean shader clock of each XCD between two probe launches on the
-    current stream, from its shader-clock counter (s_memtime) against the
+    """Mean shader clock of each compute unit between two probe launches on
+    the current stream, from its shader-clock counter (s_memtime) against the
     100 MHz real-time counter (s_memrealtime), both read on the GPU by
-    _build/libfp8probe.so (the benchmark's probe, not the library)."""
+    _build/libfp8probe.so (the benchmark's probe, not the library).  The
+    units' shader-clock counters are not aligned with each other, so the two
+    launches are matched unit by unit; the result gives each XCD's median
+    over its units and the mean over all units."""
 
-    WORKGROUPS = 64  # several per XCD, so every XCD is seen in both launches
+    WORKGROUPS = 4096  # 16 per compute unit, so every unit is seen in both launches
 
     def __init__(self, torch):
         import ctypes
@@ -209,25 +212,34 @@ class GpuClockProbe:
         """Call after a synchronization that follows mark(1)."""
         if self.lib is None or self.error:
             return {"mhz_mean": None, "error": self.error}
+        import numpy as np
         per = []
         for i in range(2):
             v = self.bufs[i].cpu().numpy().reshape(-1, 3)
             d = {}
-            for xcd, t, r in v:
-                d.setdefault(int(xcd), (int(t), int(r)))
+            for unit, t, r in v:   # each unit's earliest workgroup in the launch
+                u = int(unit)
+                if u not in d or int(r) < d[u][1]:
+                    d[u] = (int(t), int(r))
             per.append(d)
         mhz = {}
-        for xcd in sorted(set(per[0]) & set(per[1])):
-            dt = per[1][xcd][0] - per[0][xcd][0]
-            dr = per[1][xcd][1] - per[0][xcd][1]
+        for u in sorted(set(per[0]) & set(per[1])):
+            dt = per[1][u][0] - per[0][u][0]
+            dr = per[1][u][1] - per[0][u][1]
             if dr > 0 and dt > 0:
-                mhz[xcd] = round(dt / dr * 100.0, 1)
+                mhz[u] = dt / dr * 100.0
         if not mhz:
-            return {"mhz_mean": None, "error": "no XCD seen in both probe launches"}
-        vals = list(mhz.values())
-        return {"mhz_mean": round(sum(vals) / len(vals), 1), "per_xcd_mhz": vals,
-                "source": "s_memtime over s_memrealtime (100 MHz) on each XCD, read by probe "
-                          "launches just before and just after the timed steps"}
+            return {"mhz_mean": None, "error": "no compute unit seen in both probe launches"}
+        vals = np.array(list(mhz.values()))
+        xcds = sorted({u >> 8 for u in mhz})
+        per_xcd = [round(float(np.median([m for u, m in mhz.items() if u >> 8 == x])), 1)
+                   for x in xcds]
+        return {"mhz_mean": round(float(vals.mean()), 1),
+                "mhz_p10": round(float(np.percentile(vals, 10)), 1),
+                "mhz_p90": round(float(np.percentile(vals, 90)), 1),
+                "per_xcd_median_mhz": per_xcd, "compute_units_matched": int(vals.size),
+                "source": "s_memtime over s_memrealtime (100 MHz) per compute unit, read by "
+                          "probe launches just before and just after the timed steps"}
 
 
 _GROUPED = []
