@@ -15,8 +15,8 @@ sustains on this work); the W warm-up steps; the K timed steps.
 Printed as one JSON line, with:
   * roofline: the dominant kernel (the GEMM), its algorithmic flops over its
     average duration measured with HIP events on its stream inside the timed
-    region, against the dense FP8 MFMA peak; the shader clock of each XCD
-    over the timed steps, from its shader-clock and 100 MHz real-time
+    region, against the dense FP8 MFMA peak; the shader clock over the
+    timed steps, from each compute unit's shader-clock and 100 MHz real-time
     counters read on the GPU just before and just after them (the SMU's
     reported GFX clock, sampled through amdsmi, beside it), and the fraction
     against the peak at that clock; the same kernel's flushed per-part
